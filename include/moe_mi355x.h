@@ -1,0 +1,240 @@
+/*
+ * moe_mi355x.h - C ABI of the DeepSeekMoE layer forward on AMD MI355X (gfx950).
+ *
+ * The layer (sources: the "DeepSeek-V3 Technical Report" reading guide on
+ * xyznot.com, Turkish edition "Okuma rehberi" and French edition "Guide de
+ * lecture", Method section 2 "DeepSeekMoE with auxiliary-loss-free
+ * balancing", cited below as [RG-MoE]; its "Key ideas" section, FP8 bullet,
+ * cited as [RG-FP8]):
+ *
+ *   s_{i,t}  = Sigmoid(u_t . e_i)                       affinity sentence
+ *   g'_{i,t} = s_{i,t} if s_{i,t}+b_i is in the Top-K   gate equation
+ *              of {s_{j,t}+b_j}, else 0; g = g' normalised
+ *   h'_t     = u_t + sum_j FFN^(s)_j(u_t)                combine equation
+ *              + sum_i g_{i,t} FFN^(r)_i(u_t)
+ *   b_i     <- b_i - gamma if expert i is overloaded,    bias rule
+ *              b_i + gamma if underloaded (gamma = 0.001)
+ *
+ * One forward is: moe_route -> moe_permute -> [fp8_quantize_tiles] ->
+ * moe_expert_gemm -> moe_combine, then moe_bias_update at the end of a step.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as device pointers must point to device memory (HBM) of
+ *    the current HIP device; the caller owns every buffer.  The library
+ *    allocates and frees nothing, keeps no pointer after a call returns and
+ *    holds no mutable global state.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues kernels on it and returns without synchronising; calls on
+ *    distinct streams may run concurrently from different threads.
+ *  - Tensors are row-major and contiguous, element offsets are 64-bit.
+ *    bf16 is stored as raw 16-bit patterns, E4M3 as one byte per value (OCP
+ *    E4M3FN: exponent bias 7, largest finite 448, no infinities).
+ *  - Arguments are checked on the host before any launch.  A bad argument
+ *    returns MOE_EINVAL (or MOE_EUNSUPPORTED / MOE_EWORKSPACE) and launches
+ *    nothing; a launch failure returns MOE_EHIP.  With valid arguments the
+ *    device code cannot fail.  moe_last_error() gives a message for the last
+ *    failing call of the calling thread.  Device data (indices, counts) is
+ *    not validated: it must come from the producing entry point.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Limits of this implementation. */
+#define MOE_MAX_EXPERTS 1024   /* routed + shared experts */
+#define MOE_MAX_K 16           /* routed experts per token */
+#define MOE_TILE_ROWS 256      /* rows per entry of the GEMM tile map */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* NULL pointer, size out of range, bad enum */
+  MOE_EUNSUPPORTED = 2,  /* a valid combination this build does not run */
+  MOE_EWORKSPACE = 3,    /* workspace smaller than the size helper returns */
+  MOE_EHIP = 4           /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_E4M3 = 2
+} moe_dtype;
+
+/* Flags of moe_combine: drop a term of the combine equation (component checks). */
+#define MOE_COMBINE_NO_RESIDUAL 1u
+#define MOE_COMBINE_NO_SHARED 2u
+#define MOE_COMBINE_NO_ROUTED 4u
+
+int moe_abi_version(void);
+const char* moe_status_str(int status);
+/* Message of the last failing call made by this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * moe_route: sigmoid affinities, bias-steered top-K, normalised gates, loads.
+ * [RG-MoE] affinity sentence and gate equation.
+ *
+ *   u          device [T, d], dtype u_t (MOE_F32 or MOE_BF16): token states
+ *   centroids  device [Nr, d] fp32: expert centroids e_i
+ *   bias       device [Nr] fp32: routing bias b_i (read only here)
+ *   topk_idx   device [T, K] int32 out: selected experts of each token,
+ *              ordered by s+b descending; an exact tie goes to the lower index
+ *   topk_gate  device [T, K] fp32 out: g = s / (sum of the selected s) -
+ *              the gate keeps s, the bias only steers the selection
+ *   topk_score device [T, K] fp32 out, may be NULL: s of the selected experts
+ *   expert_load device [Nr] int32 out: number of tokens that selected each
+ *              expert (overwritten, not accumulated)
+ *   ws         device workspace of at least moe_route_workspace_bytes(T, d, Nr)
+ *   Affinities are computed in fp32 (products exact, fp32 accumulation in
+ *   blocks) and the sigmoid in fp32.
+ *   Errors: MOE_EINVAL for NULL required pointers, T < 0, d < 1,
+ *   Nr outside [1, MOE_MAX_EXPERTS], K outside [1, min(Nr, MOE_MAX_K)],
+ *   d not a multiple of 8; MOE_EWORKSPACE when ws_bytes is too small.
+ *   T == 0 is valid: expert_load is zeroed and nothing else is written.
+ * ---------------------------------------------------------------------- */
+size_t moe_route_workspace_bytes(int T, int d, int Nr);
+moe_status moe_route(const void* u, moe_dtype u_t, const float* centroids, const float* bias,
+                     int T, int d, int Nr, int K,
+                     int32_t* topk_idx, float* topk_gate, float* topk_score, int32_t* expert_load,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute: expert-contiguous, padded row layout (stable counting sort).
+ * Realises the per-expert token sets that the combine equation sums over;
+ * no token is dropped (blog "DeepSeek 알고 아는 척 좀 해보자 – 단편: 671B
+ * 파라미터의 괴물, DeepSeek-V3", section "DeepSeekMoE & load balancing").
+ *
+ * Segment i < Nr holds the rows (t, k) with topk_idx[t, k] == i in increasing
+ * t; segment Nr + j (j < Ns) holds every token 0..T-1 in order (shared expert
+ * j, gate 1).  Each segment is padded with rows of token -1 to a multiple of
+ * tile_m (a power of two in [1, MOE_TILE_ROWS]).
+ *
+ *   topk_idx   device [T, K] int32 in (from moe_route)
+ *   seg_offset device [Nr+Ns+1] int32 out: first row of each segment;
+ *              seg_offset[Nr+Ns] = padded rows in use
+ *   row_token  device [P_max] int32 out: token of every row, -1 = padding
+ *              (rows from seg_offset[Nr+Ns] to P_max are -1 as well)
+ *   inv_row    device [T, K] int32 out: row that holds (t, k)
+ *   tile_map   device [tiles_max, 4] int32 out: in segment order, each
+ *              segment cut into tiles of MOE_TILE_ROWS rows (the last one
+ *              shorter): {segment, first row, rows, 0}
+ *   n_tiles    device [1] int32 out: entries of tile_map in use
+ *   P_max = moe_permute_rows(...), tiles_max = moe_permute_tiles_max(...)
+ *   Errors: MOE_EINVAL for NULL pointers, bad sizes or tile_m;
+ *   MOE_EWORKSPACE when ws_bytes < moe_permute_workspace_bytes(...).
+ * ---------------------------------------------------------------------- */
+size_t moe_permute_rows(int T, int K, int Nr, int Ns, int tile_m);
+size_t moe_permute_tiles_max(int T, int K, int Nr, int Ns, int tile_m);
+size_t moe_permute_workspace_bytes(int T, int K, int Nr, int Ns);
+moe_status moe_permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, int tile_m,
+                       int32_t* seg_offset, int32_t* row_token, int32_t* inv_row,
+                       int32_t* tile_map, int32_t* n_tiles,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_expert_gemm: every expert's SwiGLU FFN on its rows of the layout.
+ * FFN^(s)_j and FFN^(r)_i of the [RG-MoE] combine equation; the pages do not
+ * print the FFN form, this library uses SwiGLU:
+ *   FFN(x) = W2 (SiLU(W_gate x) * (W_up x)),  SiLU(a) = a * sigmoid(a).
+ * y[row] = FFN_{segment(row)}(x[row_token[row]]) for every row of every
+ * tile (padding rows produce zeros or finite garbage that is never read).
+ *
+ *   x, x_t      device [T, d]: MOE_F32, MOE_BF16, or MOE_E4M3 codes
+ *   x_scale     device [T, d/128] fp32 for x_t == MOE_E4M3 (1x128 tiles,
+ *               from fp8_quantize_tiles), else NULL
+ *   w_t         MOE_F32, MOE_BF16 or MOE_E4M3 (128x128 blocks, [RG-FP8])
+ *   w13         device [Nr+Ns, 2I, d]: rows 0..I-1 W_gate, rows I..2I-1 W_up
+ *   w13_scale   device [Nr+Ns, 2I/128, d/128] fp32 for MOE_E4M3, else NULL
+ *   w2          device [Nr+Ns, d, I]: W_down
+ *   w2_scale    device [Nr+Ns, d/128, I/128] fp32 for MOE_E4M3, else NULL
+ *   seg_offset, row_token, tile_map, n_tiles: from moe_permute
+ *   tiles_max   capacity of tile_map (moe_permute_tiles_max)
+ *   ws          device workspace, moe_gemm_workspace_bytes(...) bytes: holds
+ *               the hidden state h of every row
+ *   y, y_t      device [P_max, d] out, MOE_F32 or MOE_BF16
+ * Supported (x_t, w_t, y_t): (F32, F32, F32); (BF16, BF16, BF16|F32);
+ * (BF16, E4M3, BF16) - fp8 weights, bf16 activations, h kept in bf16;
+ * (E4M3, E4M3, BF16) - fp8 activations and weights; h is re-quantised to
+ * E4M3 in 1x128 tiles before the down projection.
+ * fp8 block scales are applied per 128-wide K block in fp32; accumulation
+ * is fp32 throughout.
+ *   Errors: MOE_EINVAL for NULL pointers or bad sizes; MOE_EUNSUPPORTED for
+ *   other dtype combinations or fp8 with d or I not a multiple of 128, or d,
+ *   I not multiples of 64 on the MFMA paths; MOE_EWORKSPACE for a small ws.
+ * ---------------------------------------------------------------------- */
+size_t moe_gemm_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                moe_dtype x_t, moe_dtype w_t);
+moe_status moe_expert_gemm(const void* x, moe_dtype x_t, const float* x_scale,
+                           moe_dtype w_t, const void* w13, const float* w13_scale,
+                           const void* w2, const float* w2_scale,
+                           int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                           const int32_t* seg_offset, const int32_t* row_token,
+                           const int32_t* tile_map, const int32_t* n_tiles,
+                           void* ws, size_t ws_bytes,
+                           void* y, moe_dtype y_t, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine: h'_t = u_t + sum_j y[shared_j(t)] + sum_k g[t,k] y[inv_row[t,k]]
+ * ([RG-MoE] combine equation).  Accumulates in fp32 in a fixed order
+ * (residual, shared experts ascending, routed k ascending), so results are
+ * bitwise reproducible.
+ *
+ *   u, u_t       device [T, d], MOE_F32 or MOE_BF16
+ *   y, y_t       device [P_max, d] from moe_expert_gemm
+ *   inv_row      device [T, K] int32, topk_gate device [T, K] fp32
+ *   seg_offset   device [Nr+Ns+1] int32 (shared rows: seg_offset[Nr+j] + t)
+ *   flags        MOE_COMBINE_* bits to drop terms
+ *   out, out_t   device [T, d] out, MOE_F32 or MOE_BF16 (may not alias y)
+ *   Errors: MOE_EINVAL for NULL pointers, bad sizes, d not a multiple of 8.
+ * ---------------------------------------------------------------------- */
+moe_status moe_combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_t,
+                       const int32_t* inv_row, const float* topk_gate, const int32_t* seg_offset,
+                       int T, int d, int K, int Nr, int Ns, unsigned flags,
+                       void* out, moe_dtype out_t, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_bias_update: end-of-step bias rule ([RG-MoE] bias rule).  The pages do
+ * not define "overloaded"; this library compares the load with the mean
+ * load T*K/Nr exactly in integers: Nr*c_i > T*K -> b_i -= gamma,
+ * Nr*c_i < T*K -> b_i += gamma, equal -> unchanged; one fp32 add.
+ *
+ *   expert_load  device [Nr] int32 (from moe_route of this step)
+ *   total_assign T*K, the number of (token, expert) assignments of the step
+ *   gamma        bias step (0.001 on the pages)
+ *   bias         device [Nr] fp32, updated in place
+ *   Errors: MOE_EINVAL for NULL pointers, Nr out of range, total_assign < 0,
+ *   non-finite or negative gamma.
+ * ---------------------------------------------------------------------- */
+moe_status moe_bias_update(const int32_t* expert_load, int Nr, long long total_assign,
+                           float gamma, float* bias, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_quantize_tiles: tile-wise E4M3 quantisation ([RG-FP8]: 1x128 tiles for
+ * activations, 128x128 blocks for weights).  The pages give no scale rule;
+ * this library uses, per tile, sc = amax / 448 in IEEE fp32 (sc = 1 for an
+ * all-zero tile) and code = round-to-nearest-even(clamp(x / sc, -448, 448)),
+ * the division in IEEE fp32.  NaN is never produced for finite input.
+ *
+ *   x, x_t     device [rows, cols], MOE_F32 or MOE_BF16
+ *   tile_rows  1 or 128 (rows must be a multiple of it); tile_cols 128
+ *              (cols must be a multiple of it)
+ *   q          device [rows, cols] uint8 out (E4M3 codes)
+ *   scale      device [rows/tile_rows, cols/tile_cols] fp32 out
+ *   Errors: MOE_EINVAL for NULL pointers, bad sizes or tile shapes.
+ * ---------------------------------------------------------------------- */
+moe_status fp8_quantize_tiles(const void* x, moe_dtype x_t, long long rows, long long cols,
+                              int tile_rows, int tile_cols, uint8_t* q, float* scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

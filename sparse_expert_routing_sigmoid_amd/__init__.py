@@ -1,0 +1,274 @@
+"""Python binding of libmoe_mi355x (DeepSeekMoE layer forward on MI355X).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are torch tensors on the current HIP device; their data
+pointers and torch's current stream go through ctypes to the C ABI declared
+in include/moe_mi355x.h, with the same entry-point names.
+
+There is no CPU fallback: importing works without a GPU (so the library can
+be inspected), but every compute call raises if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+MOE_COMBINE_NO_RESIDUAL, MOE_COMBINE_NO_SHARED, MOE_COMBINE_NO_ROUTED = 1, 2, 4
+MOE_TILE_ROWS = 256
+MOE_MAX_K = 16
+MOE_MAX_EXPERTS = 1024
+
+# Every symbol the header declares, with its ctypes signature.
+_vp, _i, _ll, _sz, _f, _u = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_size_t, ctypes.c_float, ctypes.c_uint
+SIGNATURES = {
+    "moe_abi_version": (_i, []),
+    "moe_status_str": (ctypes.c_char_p, [_i]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_route_workspace_bytes": (_sz, [_i, _i, _i]),
+    "moe_route": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_permute_rows": (_sz, [_i, _i, _i, _i, _i]),
+    "moe_permute_tiles_max": (_sz, [_i, _i, _i, _i, _i]),
+    "moe_permute_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "moe_permute": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_gemm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "moe_expert_gemm": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                             _vp, _vp, _vp, _vp, _vp, _sz, _vp, _i, _vp]),
+    "moe_combine": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _u, _vp, _i, _vp]),
+    "moe_bias_update": (_i, [_vp, _i, _ll, _f, _vp, _vp]),
+    "fp8_quantize_tiles": (_i, [_vp, _i, _ll, _ll, _i, _i, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+def _status_name(s: int) -> str:
+    return {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}.get(s, str(s))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_mi355x.so (built by `python -m sparse_expert_routing_sigmoid_amd.build`)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_expert_routing_sigmoid_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        if t.numel() and not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        return t.data_ptr() if t.numel() else None
+    return t
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.uint8:
+        return MOE_E4M3
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------ sizes --
+def moe_route_workspace_bytes(T, d, Nr):
+    return lib().moe_route_workspace_bytes(T, d, Nr)
+
+
+def moe_permute_rows(T, K, Nr, Ns, tile_m):
+    return lib().moe_permute_rows(T, K, Nr, Ns, tile_m)
+
+
+def moe_permute_tiles_max(T, K, Nr, Ns, tile_m):
+    return lib().moe_permute_tiles_max(T, K, Nr, Ns, tile_m)
+
+
+def moe_permute_workspace_bytes(T, K, Nr, Ns):
+    return lib().moe_permute_workspace_bytes(T, K, Nr, Ns)
+
+
+def moe_gemm_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t):
+    return lib().moe_gemm_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t)
+
+
+# ------------------------------------------------------------ entry points --
+def moe_route(u, centroids, bias, K, topk_idx, topk_gate, topk_score, expert_load, ws, stream=None):
+    T, d = u.shape
+    Nr = centroids.shape[0]
+    _check(lib().moe_route(_ptr(u), dtype_code(u), _ptr(centroids), _ptr(bias), T, d, Nr, K,
+                           _ptr(topk_idx), _ptr(topk_gate), _ptr(topk_score), _ptr(expert_load),
+                           _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def moe_permute(topk_idx, Nr, Ns, tile_m, seg_offset, row_token, inv_row, tile_map, n_tiles, ws, stream=None):
+    T, K = topk_idx.shape
+    _check(lib().moe_permute(_ptr(topk_idx), T, K, Nr, Ns, tile_m, _ptr(seg_offset), _ptr(row_token),
+                             _ptr(inv_row), _ptr(tile_map), _ptr(n_tiles), _ptr(ws),
+                             ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def moe_expert_gemm(x, x_scale, w_t, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns, d, I, tile_m,
+                    seg_offset, row_token, tile_map, n_tiles, ws, y, x_t=None, stream=None):
+    x_t = dtype_code(x) if x_t is None else x_t
+    _check(lib().moe_expert_gemm(_ptr(x), x_t, _ptr(x_scale), w_t, _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                 _ptr(w2_scale), T, K, Nr, Ns, d, I, tile_m, _ptr(seg_offset), _ptr(row_token),
+                                 _ptr(tile_map), _ptr(n_tiles), _ptr(ws),
+                                 ws.numel() * ws.element_size() if ws is not None else 0,
+                                 _ptr(y), dtype_code(y), _stream(stream)))
+
+
+def moe_combine(u, y, inv_row, topk_gate, seg_offset, Nr, Ns, out, flags=0, stream=None):
+    T, d = u.shape
+    K = inv_row.shape[1]
+    _check(lib().moe_combine(_ptr(u), dtype_code(u), _ptr(y), dtype_code(y), _ptr(inv_row), _ptr(topk_gate),
+                             _ptr(seg_offset), T, d, K, Nr, Ns, flags, _ptr(out), dtype_code(out), _stream(stream)))
+
+
+def moe_bias_update(expert_load, total_assign, gamma, bias, stream=None):
+    _check(lib().moe_bias_update(_ptr(expert_load), bias.shape[0], int(total_assign), float(gamma), _ptr(bias),
+                                 _stream(stream)))
+
+
+def fp8_quantize_tiles(x, tile_rows, q, scale, tile_cols=128, stream=None):
+    """Quantise x viewed as [rows, cols] = [numel / last dim, last dim]."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    _check(lib().fp8_quantize_tiles(_ptr(x), dtype_code(x), rows, cols, tile_rows, tile_cols, _ptr(q), _ptr(scale),
+                                    _stream(stream)))
+
+
+# ------------------------------------------------------- layer plumbing --
+@dataclass
+class ExpertWeights:
+    """Expert weights as the library reads them: W13 [E, 2I, d], W2 [E, d, I]
+    (bf16/fp32 tensors, or E4M3 codes (uint8) with fp32 block scales)."""
+    w_t: int
+    w13: torch.Tensor
+    w2: torch.Tensor
+    w13_scale: torch.Tensor | None = None
+    w2_scale: torch.Tensor | None = None
+
+
+def quantize_weights(w13: torch.Tensor, w2: torch.Tensor, stream=None) -> ExpertWeights:
+    """E4M3 codes + 128x128 block scales of fp32/bf16 expert weights, made by
+    fp8_quantize_tiles (one 128x128 block per scale)."""
+    E, twoI, d = w13.shape
+    I = w2.shape[2]
+    q13 = torch.empty((E, twoI, d), dtype=torch.uint8, device=w13.device)
+    s13 = torch.empty((E, twoI // 128, d // 128), dtype=torch.float32, device=w13.device)
+    q2 = torch.empty((E, d, I), dtype=torch.uint8, device=w2.device)
+    s2 = torch.empty((E, d // 128, I // 128), dtype=torch.float32, device=w2.device)
+    fp8_quantize_tiles(w13, 128, q13, s13, stream=stream)
+    fp8_quantize_tiles(w2, 128, q2, s2, stream=stream)
+    return ExpertWeights(MOE_E4M3, q13, q2, s13, s2)
+
+
+class MoeLayer:
+    """Buffers and call order of one DeepSeekMoE layer forward.
+
+    Allocates every output and workspace once (torch, on `device`) and runs
+    moe_route -> moe_permute -> [fp8_quantize_tiles] -> moe_expert_gemm ->
+    moe_combine, then moe_bias_update when a step ends.  No host
+    synchronisation happens inside forward()."""
+
+    def __init__(self, T, d, Nr, Ns, I, K, act_dtype, weights: ExpertWeights, x_fp8=False,
+                 tile_m=32, out_dtype=None, device="cuda"):
+        self.T, self.d, self.Nr, self.Ns, self.I, self.K = T, d, Nr, Ns, I, K
+        self.tile_m, self.x_fp8, self.w = tile_m, x_fp8, weights
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        P = moe_permute_rows(T, K, Nr, Ns, tile_m)
+        tiles = moe_permute_tiles_max(T, K, Nr, Ns, tile_m)
+        self.P_max, self.tiles_max = P, tiles
+        self.topk_idx = torch.empty((T, K), **i32)
+        self.topk_gate = torch.empty((T, K), **f32)
+        self.topk_score = torch.empty((T, K), **f32)
+        self.expert_load = torch.empty((Nr,), **i32)
+        self.route_ws = torch.empty((max(moe_route_workspace_bytes(T, d, Nr), 1),), dtype=torch.uint8, device=dev)
+        self.seg_offset = torch.empty((Nr + Ns + 1,), **i32)
+        self.row_token = torch.empty((P,), **i32)
+        self.inv_row = torch.empty((T, K), **i32)
+        self.tile_map = torch.empty((tiles, 4), **i32)
+        self.n_tiles = torch.empty((1,), **i32)
+        self.perm_ws = torch.empty((max(moe_permute_workspace_bytes(T, K, Nr, Ns), 1),), dtype=torch.uint8,
+                                   device=dev)
+        self.x_t = MOE_E4M3 if x_fp8 else (MOE_BF16 if act_dtype == torch.bfloat16 else MOE_F32)
+        if x_fp8:
+            self.xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((T, d // 128), **f32)
+        self.gemm_ws = torch.empty((max(moe_gemm_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, self.x_t,
+                                                                  weights.w_t), 1),),
+                                   dtype=torch.uint8, device=dev)
+        out_dtype = act_dtype if out_dtype is None else out_dtype
+        self.y = torch.empty((P, d), dtype=out_dtype, device=dev)
+        self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
+
+    def route(self, u, centroids, bias, stream=None):
+        moe_route(u, centroids, bias, self.K, self.topk_idx, self.topk_gate, self.topk_score, self.expert_load,
+                  self.route_ws, stream)
+
+    def permute(self, stream=None):
+        moe_permute(self.topk_idx, self.Nr, self.Ns, self.tile_m, self.seg_offset, self.row_token, self.inv_row,
+                    self.tile_map, self.n_tiles, self.perm_ws, stream)
+
+    def experts(self, u, stream=None):
+        w = self.w
+        if self.x_fp8:
+            fp8_quantize_tiles(u, 1, self.xq, self.xs, stream=stream)
+            x, xs = self.xq, self.xs
+        else:
+            x, xs = u, None
+        moe_expert_gemm(x, xs, w.w_t, w.w13, w.w13_scale, w.w2, w.w2_scale, self.T, self.K, self.Nr, self.Ns,
+                        self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map, self.n_tiles,
+                        self.gemm_ws, self.y, x_t=self.x_t, stream=stream)
+
+    def combine(self, u, flags=0, out=None, stream=None):
+        out = self.out if out is None else out
+        moe_combine(u, self.y, self.inv_row, self.topk_gate, self.seg_offset, self.Nr, self.Ns, out, flags, stream)
+        return out
+
+    def forward(self, u, centroids, bias, stream=None):
+        self.route(u, centroids, bias, stream)
+        self.permute(stream)
+        self.experts(u, stream)
+        return self.combine(u, stream=stream)
+
+    def update_bias(self, bias, gamma=0.001, stream=None):
+        moe_bias_update(self.expert_load, self.T * self.K, gamma, bias, stream)

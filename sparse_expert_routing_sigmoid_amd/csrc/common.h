@@ -1,0 +1,111 @@
+// Internal helpers of the MI355X MoE library: error reporting, bf16 and
+// E4M3 conversions, wave-level reductions.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "moe_mi355x.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- errors --
+void set_error(const std::string& msg);
+void clear_error();
+
+#define MOE_REQUIRE(cond, code, msg)          \
+  do {                                        \
+    if (!(cond)) {                            \
+      ::moe::set_error(std::string(__func__) + ": " + (msg)); \
+      return (code);                          \
+    }                                         \
+  } while (0)
+
+// Checks the launch status after enqueueing kernels.
+moe_status launch_status(const char* where);
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// --------------------------------------------------------- conversions --
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (inputs are finite here).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// E4M3FN (OCP): bias 7, 3 mantissa bits, largest finite 448, subnormal step 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t sign = (code & 0x80u) << 24;
+  const uint32_t ef = (code >> 3) & 0xFu;
+  const uint32_t mf = code & 0x7u;
+  float mag;
+  if (ef == 0) {
+    mag = static_cast<float>(mf) * 0.001953125f;  // m * 2^-9, exact
+  } else {
+    mag = __uint_as_float(((ef + 120u) << 23) | (mf << 20));  // 2^(ef-7) * (1 + m/8)
+  }
+  return __uint_as_float(__float_as_uint(mag) | sign);
+}
+
+// Round-to-nearest-even of |x| <= 448 (already clamped) to an E4M3FN code,
+// done in integer arithmetic on the fp32 bit pattern.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {                 // |x| < 2^-6: subnormal range, step 2^-9
+    // q = RNE(|x| * 2^9); exact because the scale is a power of two.
+    const float s = __uint_as_float(a) * 512.0f;
+    const float r = __builtin_rintf(s);  // round half to even
+    code = static_cast<uint32_t>(r);     // 0..8; 8 is the smallest normal's code
+  } else {
+    // Normal: keep 3 mantissa bits with RNE on the 20 dropped bits.
+    const uint32_t lsb = (a >> 20) & 1u;
+    const uint32_t rounded = a + 0x7FFFFu + lsb;
+    const uint32_t e = (rounded >> 23) - 120u;  // biased exponent for bias 7
+    const uint32_t m = (rounded >> 20) & 7u;
+    code = (e << 3) | m;
+    if (code > 0x7Eu) code = 0x7Eu;      // cannot happen after clamping to 448
+  }
+  return code | sign;
+}
+
+// ---------------------------------------------------------- wave helpers --
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    unsigned long long o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Order-preserving map of a finite fp32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__host__ __device__ constexpr inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+}  // namespace moe

@@ -1,0 +1,253 @@
+// Bandwidth-bound steps of the layer: the gated combine, the bias rule and
+// tile-wise E4M3 quantisation.
+//
+// Sources: "DeepSeek-V3 Technical Report" reading guide (xyznot.com), Method
+// section 2 (combine equation, bias rule with gamma = 0.001) and "Key ideas",
+// FP8 bullet (E4M3, 1x128 activation tiles, 128x128 weight blocks).
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+// ------------------------------------------------------------- combine --
+// One block per token and 2048-column chunk; every thread owns 8 consecutive
+// columns (16 B of bf16), so all loads are 16 B and coalesced.  The sum runs
+// in fp32 in a fixed order: residual, shared experts, routed slots 0..K-1.
+template <typename T_>
+struct Vec8;
+template <>
+struct Vec8<uint16_t> {
+  __device__ static void load(const uint16_t* p, float (&v)[8]) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static void store(uint16_t* p, const float (&v)[8]) {
+    uint4 q;
+    q.x = pack_bf16x2(v[0], v[1]);
+    q.y = pack_bf16x2(v[2], v[3]);
+    q.z = pack_bf16x2(v[4], v[5]);
+    q.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = q;
+  }
+};
+template <>
+struct Vec8<float> {
+  __device__ static void load(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ static void store(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+constexpr int CB_THREADS = 256;
+constexpr int CB_COLS = CB_THREADS * 8;
+
+template <typename UT, typename YT, typename OT>
+__global__ __launch_bounds__(CB_THREADS) void k_combine(const UT* __restrict__ u, const YT* __restrict__ y,
+                                                        const int32_t* __restrict__ inv_row,
+                                                        const float* __restrict__ gate,
+                                                        const int32_t* __restrict__ seg_offset, int T, int d, int K,
+                                                        int Nr, int Ns, unsigned flags, OT* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int c = blockIdx.y * CB_COLS + threadIdx.x * 8;
+  if (c >= d) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float v[8];
+  if (!(flags & MOE_COMBINE_NO_RESIDUAL)) {
+    Vec8<UT>::load(u + (long long)t * d + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+  if (!(flags & MOE_COMBINE_NO_SHARED)) {
+    for (int j = 0; j < Ns; ++j) {
+      const long long row = (long long)seg_offset[Nr + j] + t;
+      Vec8<YT>::load(y + row * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  }
+  if (!(flags & MOE_COMBINE_NO_ROUTED)) {
+    for (int k = 0; k < K; ++k) {
+      const long long row = inv_row[(long long)t * K + k];
+      const float g = gate[(long long)t * K + k];
+      Vec8<YT>::load(y + row * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+  }
+  Vec8<OT>::store(out + (long long)t * d + c, acc);
+}
+
+template <typename UT, typename YT, typename OT>
+void launch_combine(const void* u, const void* y, const int32_t* inv_row, const float* gate, const int32_t* seg_offset,
+                    int T, int d, int K, int Nr, int Ns, unsigned flags, void* out, hipStream_t st) {
+  dim3 grid(T, (unsigned)ceil_div(d, CB_COLS));
+  hipLaunchKernelGGL((k_combine<UT, YT, OT>), grid, dim3(CB_THREADS), 0, st, static_cast<const UT*>(u),
+                     static_cast<const YT*>(y), inv_row, gate, seg_offset, T, d, K, Nr, Ns, flags,
+                     static_cast<OT*>(out));
+}
+
+// ---------------------------------------------------------------- bias --
+__global__ void k_bias_update(const int32_t* __restrict__ load, int Nr, long long total, float gamma,
+                              float* __restrict__ bias) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Nr) return;
+  const long long lhs = (long long)Nr * (long long)load[i];
+  const float b = bias[i];
+  if (lhs > total)
+    bias[i] = b - gamma;
+  else if (lhs < total)
+    bias[i] = b + gamma;
+}
+
+// ------------------------------------------------------------ quantise --
+template <typename XT>
+__device__ __forceinline__ float ld(const XT* p, long long i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, long long i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, long long i) { return bf16_to_f32(p[i]); }
+
+__device__ __forceinline__ uint32_t quant_one(float x, float sc) {
+  float q = x / sc;  // IEEE fp32 division
+  q = fminf(fmaxf(q, -448.0f), 448.0f);
+  return f32_to_e4m3(q);
+}
+
+// 1 x 128 tiles: one wave per tile, two values per lane.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_quant_1x128(const XT* __restrict__ x, long long rows, long long cols,
+                                                     uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const long long tiles_per_row = cols / 128;
+  const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= rows * tiles_per_row) return;
+  const int lane = threadIdx.x & 63;
+  const long long r = tile / tiles_per_row;
+  const long long c = (tile % tiles_per_row) * 128 + lane * 2;
+  const long long o = r * cols + c;
+  const float a = ld(x, o), b = ld(x, o + 1);
+  const float amax = wave_max_f32(fmaxf(fabsf(a), fabsf(b)));
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  const uint32_t qa = quant_one(a, sc), qb = quant_one(b, sc);
+  *reinterpret_cast<uint16_t*>(q + o) = static_cast<uint16_t>(qa | (qb << 8));
+  if (lane == 0) scale[tile] = sc;
+}
+
+// 128 x 128 blocks: one block of 256 threads per tile, 64 values per thread.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_quant_128x128(const XT* __restrict__ x, long long rows, long long cols,
+                                                       uint8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float red[4];
+  const long long tc = cols / 128;
+  const long long tr = blockIdx.x / tc, tcol = blockIdx.x % tc;
+  const int tid = threadIdx.x;
+  const int col = (tid & 31) * 4;        // 32 threads x 4 columns
+  const int row0 = tid >> 5;             // 8 row groups
+  float m = 0.f;
+  for (int rr = row0; rr < 128; rr += 8) {
+    const long long o = (tr * 128 + rr) * cols + tcol * 128 + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(ld(x, o + i)));
+  }
+  m = wave_max_f32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  for (int rr = row0; rr < 128; rr += 8) {
+    const long long o = (tr * 128 + rr) * cols + tcol * 128 + col;
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= quant_one(ld(x, o + i), sc) << (8 * i);
+    *reinterpret_cast<uint32_t*>(q + o) = w;
+  }
+  if (tid == 0) scale[blockIdx.x] = sc;
+}
+
+}  // namespace
+
+moe_status combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_t, const int32_t* inv_row,
+                   const float* topk_gate, const int32_t* seg_offset, int T, int d, int K, int Nr, int Ns,
+                   unsigned flags, void* out, moe_dtype out_t, void* stream) {
+  MOE_REQUIRE(T >= 0 && d >= 8 && d % 8 == 0, MOE_EINVAL, "need T >= 0 and d a positive multiple of 8");
+  MOE_REQUIRE(Nr >= 1 && Ns >= 0 && Nr + Ns <= MOE_MAX_EXPERTS, MOE_EINVAL, "expert counts out of range");
+  MOE_REQUIRE(K >= 1 && K <= MOE_MAX_K && K <= Nr, MOE_EINVAL, "K out of range");
+  MOE_REQUIRE((flags & ~7u) == 0, MOE_EINVAL, "unknown flag bits");
+  MOE_REQUIRE(u_t == MOE_F32 || u_t == MOE_BF16, MOE_EINVAL, "u_t must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(y_t == MOE_F32 || y_t == MOE_BF16, MOE_EINVAL, "y_t must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(out_t == MOE_F32 || out_t == MOE_BF16, MOE_EINVAL, "out_t must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(T == 0 || (u && y && inv_row && topk_gate && seg_offset && out), MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(out != y, MOE_EINVAL, "out aliases y");
+  if (T == 0) return MOE_OK;
+  hipStream_t st = as_stream(stream);
+  const int key = (u_t == MOE_BF16) * 4 + (y_t == MOE_BF16) * 2 + (out_t == MOE_BF16);
+  using B = uint16_t;
+  using F = float;
+  switch (key) {
+    case 0: launch_combine<F, F, F>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+    case 1: launch_combine<F, F, B>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+    case 2: launch_combine<F, B, F>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+    case 3: launch_combine<F, B, B>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+    case 4: launch_combine<B, F, F>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+    case 5: launch_combine<B, F, B>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+    case 6: launch_combine<B, B, F>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+    default: launch_combine<B, B, B>(u, y, inv_row, topk_gate, seg_offset, T, d, K, Nr, Ns, flags, out, st); break;
+  }
+  return launch_status("moe_combine");
+}
+
+moe_status bias_update(const int32_t* expert_load, int Nr, long long total_assign, float gamma, float* bias,
+                       void* stream) {
+  MOE_REQUIRE(expert_load && bias, MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(Nr >= 1 && Nr <= MOE_MAX_EXPERTS, MOE_EINVAL, "Nr out of range");
+  MOE_REQUIRE(total_assign >= 0, MOE_EINVAL, "total_assign < 0");
+  MOE_REQUIRE(std::isfinite(gamma) && gamma >= 0.f, MOE_EINVAL, "gamma must be finite and >= 0");
+  hipLaunchKernelGGL(k_bias_update, dim3((Nr + 255) / 256), dim3(256), 0, as_stream(stream), expert_load, Nr,
+                     total_assign, gamma, bias);
+  return launch_status("moe_bias_update");
+}
+
+moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long long cols, int tile_rows, int tile_cols,
+                          uint8_t* q, float* scale, void* stream) {
+  MOE_REQUIRE(x_t == MOE_F32 || x_t == MOE_BF16, MOE_EINVAL, "x_t must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(tile_cols == 128 && (tile_rows == 1 || tile_rows == 128), MOE_EINVAL,
+              "tiles must be 1x128 or 128x128");
+  MOE_REQUIRE(rows >= 0 && cols >= 0 && cols % 128 == 0 && rows % tile_rows == 0, MOE_EINVAL,
+              "rows/cols must be multiples of the tile");
+  MOE_REQUIRE(rows == 0 || cols == 0 || (x && q && scale), MOE_EINVAL, "NULL pointer");
+  const long long ntiles = (rows / tile_rows) * (cols / 128);
+  if (ntiles == 0) return MOE_OK;
+  MOE_REQUIRE(ntiles < (1LL << 31) * 4, MOE_EINVAL, "too many tiles");
+  hipStream_t st = as_stream(stream);
+  if (tile_rows == 1) {
+    dim3 grid((unsigned)ceil_div(ntiles, 4));
+    if (x_t == MOE_F32)
+      hipLaunchKernelGGL(k_quant_1x128<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), rows, cols, q,
+                         scale);
+    else
+      hipLaunchKernelGGL(k_quant_1x128<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x), rows, cols,
+                         q, scale);
+  } else {
+    dim3 grid((unsigned)ntiles);
+    if (x_t == MOE_F32)
+      hipLaunchKernelGGL(k_quant_128x128<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), rows, cols, q,
+                         scale);
+    else
+      hipLaunchKernelGGL(k_quant_128x128<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x), rows,
+                         cols, q, scale);
+  }
+  return launch_status("fp8_quantize_tiles");
+}
+
+}  // namespace moe

@@ -1,0 +1,94 @@
+// moe_expert_gemm: argument checks, workspace layout and dispatch of the
+// grouped SwiGLU expert GEMMs to the kernel family of each dtype combination.
+#include "common.h"
+
+namespace moe {
+
+size_t permute_rows(int T, int K, int Nr, int Ns, int tile_m);
+size_t permute_tiles_max(int T, int K, int Nr, int Ns, int tile_m);
+
+void launch_ffn_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
+                     const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int d, int I, uint16_t* h,
+                     void* y, bool y_f32, hipStream_t st);
+void launch_ffn_f32(const float* x, const float* w13, const float* w2, const int32_t* row_token,
+                    const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int d, int I, float* h, float* y,
+                    hipStream_t st);
+
+namespace {
+
+enum class Path { F32, BF16, W8A16, FP8, NONE };
+
+Path path_of(moe_dtype x_t, moe_dtype w_t) {
+  if (x_t == MOE_F32 && w_t == MOE_F32) return Path::F32;
+  if (x_t == MOE_BF16 && w_t == MOE_BF16) return Path::BF16;
+  if (x_t == MOE_BF16 && w_t == MOE_E4M3) return Path::W8A16;
+  if (x_t == MOE_E4M3 && w_t == MOE_E4M3) return Path::FP8;
+  return Path::NONE;
+}
+
+// Bytes of h per row for each path (fp8 keeps codes plus one fp32 scale per
+// 128 columns).
+size_t h_row_bytes(Path p, int I) {
+  switch (p) {
+    case Path::F32: return (size_t)I * 4;
+    case Path::BF16:
+    case Path::W8A16: return (size_t)I * 2;
+    case Path::FP8: return (size_t)I + (size_t)(I / 128) * 4;
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m, moe_dtype x_t, moe_dtype w_t) {
+  (void)d;
+  const Path p = path_of(x_t, w_t);
+  if (p == Path::NONE || T < 0 || I < 1) return 0;
+  const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
+  return P * h_row_bytes(p, I) + 256;
+}
+
+moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_dtype w_t, const void* w13,
+                       const float* w13_scale, const void* w2, const float* w2_scale, int T, int K, int Nr, int Ns,
+                       int d, int I, int tile_m, const int32_t* seg_offset, const int32_t* row_token,
+                       const int32_t* tile_map, const int32_t* n_tiles, void* ws, size_t ws_bytes, void* y,
+                       moe_dtype y_t, void* stream) {
+  MOE_REQUIRE(T >= 0 && d >= 1 && I >= 1, MOE_EINVAL, "need T >= 0, d >= 1, I >= 1");
+  MOE_REQUIRE(Nr >= 1 && Ns >= 0 && Nr + Ns <= MOE_MAX_EXPERTS, MOE_EINVAL, "expert counts out of range");
+  MOE_REQUIRE(K >= 1 && K <= MOE_MAX_K && K <= Nr, MOE_EINVAL, "K out of range");
+  MOE_REQUIRE(tile_m >= 1 && tile_m <= MOE_TILE_ROWS && (tile_m & (tile_m - 1)) == 0, MOE_EINVAL, "bad tile_m");
+  MOE_REQUIRE(x_t == MOE_F32 || x_t == MOE_BF16 || x_t == MOE_E4M3, MOE_EINVAL, "bad x_t");
+  MOE_REQUIRE(w_t == MOE_F32 || w_t == MOE_BF16 || w_t == MOE_E4M3, MOE_EINVAL, "bad w_t");
+  MOE_REQUIRE(y_t == MOE_F32 || y_t == MOE_BF16, MOE_EINVAL, "bad y_t");
+  MOE_REQUIRE(x && w13 && w2 && seg_offset && row_token && tile_map && n_tiles && y, MOE_EINVAL, "NULL pointer");
+  const Path p = path_of(x_t, w_t);
+  MOE_REQUIRE(p != Path::NONE, MOE_EUNSUPPORTED, "unsupported (x_t, w_t) combination");
+  MOE_REQUIRE(w_t != MOE_E4M3 || (w13_scale && w2_scale), MOE_EINVAL, "E4M3 weights need block scales");
+  MOE_REQUIRE(x_t != MOE_E4M3 || x_scale, MOE_EINVAL, "E4M3 activations need tile scales");
+  MOE_REQUIRE(ws && ws_bytes >= gemm_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t), MOE_EWORKSPACE,
+              "workspace smaller than moe_gemm_workspace_bytes");
+  const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
+  MOE_REQUIRE(P < (1ull << 31), MOE_EINVAL, "too many rows");
+  const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
+  hipStream_t st = as_stream(stream);
+  if (T == 0) return MOE_OK;
+  switch (p) {
+    case Path::F32:
+      MOE_REQUIRE(y_t == MOE_F32, MOE_EUNSUPPORTED, "fp32 path writes fp32 y");
+      launch_ffn_f32(static_cast<const float*>(x), static_cast<const float*>(w13), static_cast<const float*>(w2),
+                     row_token, tile_map, n_tiles, tiles_max, d, I, static_cast<float*>(ws), static_cast<float*>(y),
+                     st);
+      break;
+    case Path::BF16:
+      MOE_REQUIRE(d % 128 == 0 && I % 64 == 0, MOE_EUNSUPPORTED, "bf16 path needs d % 128 == 0 and I % 64 == 0");
+      launch_ffn_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
+                      static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, tiles_max, d, I,
+                      static_cast<uint16_t*>(ws), y, y_t == MOE_F32, st);
+      break;
+    default:
+      MOE_REQUIRE(false, MOE_EUNSUPPORTED, "fp8 paths not built yet");
+  }
+  return launch_status("moe_expert_gemm");
+}
+
+}  // namespace moe

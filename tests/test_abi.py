@@ -1,0 +1,136 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the public
+header declares, and rejects bad arguments on the host, before any launch,
+with the documented status codes.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_expert_routing_sigmoid_amd as M
+from oracle import moe as omoe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(M.SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    L = M.lib()
+    assert L.moe_abi_version() == 1
+    assert L.moe_status_str(0) == b"MOE_OK"
+    assert L.moe_status_str(3) == b"MOE_EWORKSPACE"
+
+
+@pytest.mark.parametrize("T,K,Nr,Ns,tile_m", [(64, 4, 16, 1, 32), (8192, 8, 256, 1, 32), (5, 3, 9, 2, 1),
+                                             (0, 2, 4, 1, 16), (128, 8, 256, 1, 16)])
+def test_row_bound_matches_oracle(T, K, Nr, Ns, tile_m):
+    assert M.moe_permute_rows(T, K, Nr, Ns, tile_m) == omoe.permuted_rows_max(T, K, Nr, Ns, tile_m)
+    tiles = M.moe_permute_tiles_max(T, K, Nr, Ns, tile_m)
+    assert tiles >= M.moe_permute_rows(T, K, Nr, Ns, tile_m) // M.MOE_TILE_ROWS + 1
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, M.lib().moe_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails on the host
+
+
+def test_route_rejects_bad_arguments():
+    L = M.lib()
+    ws = 1 << 30
+    good = dict(u=FAKE, ut=M.MOE_BF16, e=FAKE, b=FAKE, T=4, d=64, Nr=16, K=4, idx=FAKE, gate=FAKE, score=None,
+                load=FAKE, ws=FAKE, wsb=ws, st=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return _status(L.moe_route, a["u"], a["ut"], a["e"], a["b"], a["T"], a["d"], a["Nr"], a["K"], a["idx"],
+                       a["gate"], a["score"], a["load"], a["ws"], a["wsb"], a["st"])
+
+    assert call(u=None)[0] == M.MOE_EINVAL
+    assert call(load=None)[0] == M.MOE_EINVAL
+    assert call(K=0)[0] == M.MOE_EINVAL
+    assert call(K=17, Nr=32)[0] == M.MOE_EINVAL
+    assert call(K=5, Nr=4)[0] == M.MOE_EINVAL
+    assert call(Nr=1025)[0] == M.MOE_EINVAL
+    assert call(d=60)[0] == M.MOE_EINVAL
+    assert call(ut=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    st, msg = call(wsb=16)
+    assert st == M.MOE_EWORKSPACE and "workspace" in msg
+
+
+def test_permute_rejects_bad_arguments():
+    L = M.lib()
+    args = [FAKE, 8, 2, 4, 1, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return L.moe_permute(*a)
+
+    assert call(5, 3) == M.MOE_EINVAL        # tile_m not a power of two
+    assert call(5, 512) == M.MOE_EINVAL      # tile_m above MOE_TILE_ROWS
+    assert call(2, 5) == M.MOE_EINVAL        # K > Nr
+    assert call(0, None) == M.MOE_EINVAL     # NULL topk_idx
+    assert call(12, 4) == M.MOE_EWORKSPACE
+
+
+def test_gemm_rejects_bad_arguments():
+    L = M.lib()
+    base = [FAKE, M.MOE_BF16, None, M.MOE_BF16, FAKE, None, FAKE, None, 64, 4, 16, 1, 256, 128, 32,
+            FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE, M.MOE_BF16, None]
+
+    def call(**kw):
+        a = list(base)
+        pos = dict(x_t=1, x_scale=2, w_t=3, w13_scale=5, d=12, I=13, ws_bytes=20, y_t=22, x=0)
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return L.moe_expert_gemm(*a)
+
+    assert call(x=None) == M.MOE_EINVAL
+    assert call(x_t=M.MOE_F32) == M.MOE_EUNSUPPORTED                     # f32 x with bf16 weights
+    assert call(w_t=M.MOE_E4M3) == M.MOE_EINVAL                          # fp8 weights without scales
+    assert call(x_t=M.MOE_E4M3, w_t=M.MOE_E4M3, w13_scale=FAKE) == M.MOE_EINVAL  # no x_scale / w2_scale
+    assert call(ws_bytes=10) == M.MOE_EWORKSPACE
+    assert call(d=200) == M.MOE_EUNSUPPORTED                             # MFMA path needs d % 128 == 0
+    assert call(y_t=M.MOE_E4M3) == M.MOE_EINVAL
+
+
+def test_combine_bias_quant_reject_bad_arguments():
+    L = M.lib()
+    assert L.moe_combine(FAKE, M.MOE_BF16, FAKE, M.MOE_BF16, FAKE, FAKE, FAKE, 4, 100, 2, 8, 1, 0, FAKE,
+                         M.MOE_BF16, None) == M.MOE_EINVAL            # d % 8 != 0
+    assert L.moe_combine(FAKE, M.MOE_BF16, FAKE, M.MOE_BF16, FAKE, FAKE, FAKE, 4, 64, 2, 8, 1, 8, FAKE,
+                         M.MOE_BF16, None) == M.MOE_EINVAL            # unknown flag
+    assert L.moe_combine(FAKE, M.MOE_BF16, FAKE, M.MOE_BF16, FAKE, FAKE, FAKE, 4, 64, 2, 8, 1, 0, FAKE,
+                         M.MOE_BF16, None) == M.MOE_EINVAL            # out aliases y
+    assert L.moe_bias_update(None, 4, 8, 0.001, FAKE, None) == M.MOE_EINVAL
+    assert L.moe_bias_update(FAKE, 4, -1, 0.001, FAKE, None) == M.MOE_EINVAL
+    assert L.moe_bias_update(FAKE, 4, 8, float("nan"), FAKE, None) == M.MOE_EINVAL
+    assert L.fp8_quantize_tiles(FAKE, M.MOE_BF16, 4, 100, 1, 128, FAKE, FAKE, None) == M.MOE_EINVAL
+    assert L.fp8_quantize_tiles(FAKE, M.MOE_BF16, 100, 128, 128, 128, FAKE, FAKE, None) == M.MOE_EINVAL
+    assert L.fp8_quantize_tiles(FAKE, M.MOE_BF16, 4, 128, 2, 128, FAKE, FAKE, None) == M.MOE_EINVAL
+    assert L.fp8_quantize_tiles(FAKE, M.MOE_E4M3, 4, 128, 1, 128, FAKE, FAKE, None) == M.MOE_EINVAL
+
+
+def test_python_binding_raises_with_message():
+    import torch
+    with pytest.raises(M.MoeError, match="MOE_EINVAL"):
+        M._check(M.lib().moe_bias_update(None, 4, 8, 0.001, FAKE, None))

@@ -1,0 +1,85 @@
+"""GPU parity of moe_expert_gemm against the oracle's per-row expert FFN on
+the oracle's own layout: every real row y[row] = FFN_seg(x[row_token[row]])."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_expert_routing_sigmoid_amd as M
+import workloads as W
+from moe_testutil import f64_of, rel_l2
+from oracle import moe as O
+from test_gpu_permute import make_idx
+
+pytestmark = pytest.mark.gpu
+
+
+def upload_layout(lay):
+    c = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tiles = torch.zeros((max(lay.n_tiles, 1), 4), dtype=torch.int32)
+    tiles[: lay.n_tiles] = torch.from_numpy(lay.tile_map)
+    return c(lay.seg_offset), c(lay.row_token), tiles.cuda(), torch.tensor([lay.n_tiles], dtype=torch.int32).cuda()
+
+
+def gpu_expert_rows(cfg, x, x_scale, weights, lay, tile_m, y_dtype):
+    seg, rt, tm, nt = upload_layout(lay)
+    T = cfg.T
+    x_t = M.dtype_code(x)
+    P = len(lay.row_token)
+    ws = torch.empty((M.moe_gemm_workspace_bytes(T, cfg.K, cfg.Nr, cfg.Ns, cfg.d, cfg.I, tile_m, x_t,
+                                                 weights.w_t),), dtype=torch.uint8, device="cuda")
+    y = torch.full((P, cfg.d), float("nan"), dtype=y_dtype, device="cuda")
+    # the layout is sized for this tile_m and K, so the capacities agree
+    assert P == M.moe_permute_rows(T, cfg.K, cfg.Nr, cfg.Ns, tile_m)
+    M.moe_expert_gemm(x, x_scale, weights.w_t, weights.w13, weights.w13_scale, weights.w2, weights.w2_scale,
+                      T, cfg.K, cfg.Nr, cfg.Ns, cfg.d, cfg.I, tile_m, seg, rt, tm, nt, ws, y)
+    torch.cuda.synchronize()
+    return f64_of(y)
+
+
+def run_case(cfg, idx, tile_m=16, y_dtype=None, tol=1e-2):
+    u = W.make_tokens(cfg, 0, "cuda")
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    wt = M.MOE_F32 if cfg.weights == "f32" else M.MOE_BF16
+    weights = M.ExpertWeights(wt, w13, w2)
+    lay = O.permute_layout(idx.numpy(), cfg.Nr, cfg.Ns, tile_m, M.MOE_TILE_ROWS)
+    y_dtype = u.dtype if y_dtype is None else y_dtype
+    y = gpu_expert_rows(cfg, u, None, weights, lay, tile_m, y_dtype)
+    want = O.expert_rows(f64_of(u), f64_of(w13), f64_of(w2), lay, cfg.Nr, cfg.Ns)
+    real = lay.row_token[: lay.seg_offset[-1]] >= 0
+    got = y[: lay.seg_offset[-1]][real]
+    ref = want[real]
+    assert np.all(np.isfinite(got))
+    err = rel_l2(got, ref)
+    assert err <= tol, err
+    # every segment on its own (catches a wrong expert or a wrong tile)
+    for s in range(cfg.E):
+        r0, r1 = lay.seg_offset[s], lay.seg_offset[s + 1]
+        m = lay.row_token[r0:r1] >= 0
+        if m.any():
+            assert rel_l2(y[r0:r1][m], want[r0:r1][m]) <= 2 * tol, s
+    return err
+
+
+def test_f32_tiny_layer_rows():
+    cfg = W.CONFIGS["tiny_fp32"]
+    idx = make_idx(cfg.T, cfg.Nr, cfg.K, 3)
+    assert run_case(cfg, idx, tile_m=32, tol=1e-5) < 1e-5
+
+
+@pytest.mark.parametrize("T,I,tile_m", [(300, 128, 16), (300, 192, 32), (77, 64, 1), (600, 256, 256)])
+def test_bf16_ragged_tiles(T, I, tile_m):
+    cfg = W.CONFIGS["mid_bf16"].with_(T=T, d=256, I=I, Nr=8, Ns=1, K=2)
+    idx = make_idx(T, cfg.Nr, cfg.K, T + I, hot=[5])        # expert 5 gets every token: > 256 rows
+    run_case(cfg, idx, tile_m=tile_m)
+
+
+def test_bf16_f32_output():
+    cfg = W.CONFIGS["mid_bf16"].with_(T=200, d=384, I=128, Nr=6, Ns=2, K=3)
+    run_case(cfg, make_idx(cfg.T, cfg.Nr, cfg.K, 9), y_dtype=torch.float32)
+
+
+def test_bf16_mid_config_rows():
+    cfg = W.CONFIGS["mid_bf16"]
+    u = W.make_tokens(cfg, 0, "cpu")
+    r = O.route(f64_of(u), f64_of(W.make_centroids(cfg, "cpu")), f64_of(W.make_bias(cfg, "cpu")), cfg.K)
+    run_case(cfg, torch.from_numpy(r.idx), tile_m=32)
