@@ -1,0 +1,225 @@
+"""Benchmark of the DeepSeekMoE layer forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of T tokens already
+resident in HBM: moe_route -> moe_permute -> [fp8_quantize_tiles] ->
+moe_expert_gemm -> moe_combine -> moe_bias_update (the bias carries over to
+the next step, as in a training step).  W untimed warm-up steps, then exactly
+K timed steps between two device synchronisations.  Prints one JSON line.
+
+Workloads (synthetic, seeded; see workloads/):
+  v3_prefill_bf16  T=8192, d=7168, 256 routed + 1 shared SwiGLU experts
+                   (I=2048), top-8, bf16, Zipf-skewed loads (default)
+  v3_prefill_fp8   T=16384, same layer, E4M3 activations and weights
+  v3_decode_fp8w   T=128, same layer, E4M3 weights, bf16 activations
+  mid_bf16, tiny_fp32  smaller layers
+
+The roofline object describes the expert GEMM call (gate/up + SwiGLU, then
+down), the dominant cost of the step, timed with HIP events on the stream it
+is launched on.  The cpu_baseline object times the fp64 CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 256e/top-8 d7168; % MFMA peak (bf16/fp8), decode GB/s"
+PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12, "hbm": 8.0e12}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="v3_prefill_bf16")
+    p.add_argument("--tile-m", type=int, default=32)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the layer is built and measured on one "
+              "GPU; multi-GPU expert parallelism is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sparse_expert_routing_sigmoid_amd as M
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs, resident in HBM before timing
+    e = W.make_centroids(cfg, dev)
+    bias0 = W.make_bias(cfg, dev)
+    n_u = min(max(args.steps, 1), 10)
+    us = [W.make_tokens(cfg, s, dev) for s in range(n_u)]
+    w13, w2 = W.make_expert_weights(cfg, dev)
+    if cfg.weights == "e4m3":
+        weights = M.quantize_weights(w13, w2)
+        del w13, w2
+    else:
+        weights = M.ExpertWeights(M.MOE_F32 if cfg.weights == "f32" else M.MOE_BF16, w13, w2)
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, W.TORCH_DTYPE[cfg.act], weights,
+                       x_fp8=cfg.x_fp8, tile_m=args.tile_m, device=dev)
+    torch.cuda.synchronize()
+
+    bias = bias0.clone()
+    gemm_events = []
+
+    def step(s, timed):
+        u = us[s % n_u]
+        layer.route(u, e, bias)
+        layer.permute()
+        if timed:
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+        layer.experts(u)
+        if timed:
+            ev1.record(stream)
+            gemm_events.append((ev0, ev1))
+        layer.combine(u)
+        layer.update_bias(bias, cfg.gamma)
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / max(args.steps, 1)
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in gemm_events])) if gemm_events else float("nan")
+
+    # ---- algorithmic work of one step
+    loads = layer.expert_load.cpu().numpy().astype(np.int64)
+    rows = int(cfg.T * cfg.K + cfg.T * cfg.Ns)
+    gemm_flops = 6.0 * cfg.d * cfg.I * rows
+    touched = int((loads > 0).sum()) + cfg.Ns
+    wbytes_per_expert = 3 * cfg.I * cfg.d * (1 if cfg.weights == "e4m3" else (4 if cfg.weights == "f32" else 2))
+    if cfg.weights == "e4m3":
+        wbytes_per_expert += 4 * (2 * cfg.I // 128) * (cfg.d // 128) + 4 * (cfg.d // 128) * (cfg.I // 128)
+    act_b = 4 if cfg.act == "f32" else 2
+    x_b = 1 if cfg.x_fp8 else act_b
+    # weights of touched experts, the gathered activations read once per row set, h and y unexcluded
+    gemm_bytes = touched * wbytes_per_expert + cfg.T * cfg.d * x_b
+    layer_bytes = touched * wbytes_per_expert + cfg.Nr * cfg.d * 4 + 2 * cfg.T * cfg.d * act_b
+    dtype = {"bf16": "bf16", "f32": "f32", "e4m3": "fp8"}[cfg.weights] if not cfg.x_fp8 else "fp8"
+    if cfg.weights == "e4m3" and not cfg.x_fp8:
+        bound, peak, unit = "hbm", PEAK["hbm"], "GB/s"
+        achieved = gemm_bytes / (gemm_ms * 1e-3)
+        roof = {"bound": bound, "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": unit,
+                "frac": achieved / peak}
+        dtype = "bf16 x fp8-weights"
+    else:
+        mfma_peak = PEAK["fp8" if cfg.x_fp8 else ("f32" if cfg.weights == "f32" else "bf16")]
+        achieved = gemm_flops / (gemm_ms * 1e-3)
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": mfma_peak / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / mfma_peak}
+    roof["traffic"] = None
+    roof["kernel"] = "moe_expert_gemm (k_gateup + k_down)"
+    roof["units_per_launch"] = {"rows": rows, "flops": gemm_flops, "algorithmic_bytes": gemm_bytes}
+    roof["avg_launch_ms"] = gemm_ms
+
+    tokens_s = cfg.T / (ms_step * 1e-3)
+    layer_time = ms_step * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; random-init expert weights and centroids of the V3 MoE-layer shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "Nr": cfg.Nr, "Ns": cfg.Ns, "I": cfg.I,
+                   "K": cfg.K, "routing": cfg.routing, "weights": cfg.weights, "x_fp8": cfg.x_fp8,
+                   "tile_m": args.tile_m, "bias_update": "every step", "parallelism": "single GPU"},
+        "layer": {"tflops": gemm_flops / layer_time / 1e12,
+                  "mfma_frac": gemm_flops / layer_time / (PEAK["fp8"] if cfg.x_fp8 else PEAK["bf16"]),
+                  "hbm_gbs": layer_bytes / layer_time / 1e9, "hbm_frac": layer_bytes / layer_time / PEAK["hbm"],
+                  "experts_touched": touched, "max_load": int(loads.max()), "mean_load": float(loads.mean()),
+                  "padded_rows": int(layer.seg_offset[-1].item())},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, layer, us[0], e, bias0, weights, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, layer, u, e, b, weights, sample_tokens):
+    """Time the fp64 oracle on the first S tokens of step 0: routing, the 8
+    routed + shared SwiGLU experts of each sampled token, and the combine.
+    Weight conversion to fp64 is input preparation and is not timed."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import e4m3 as OE
+    from oracle import moe as O
+
+    S = sample_tokens or (16 if cfg.d >= 4096 else min(cfg.T, 512))
+    S = min(S, cfg.T)
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    u_s = f64(u[:S])
+    e_h = f64(e)
+    b_h = f64(b)
+    t_route = time.perf_counter()
+    r = O.route(u_s, e_h, b_h, cfg.K)
+    t_route = time.perf_counter() - t_route
+    x = O.quantize_activations(u_s) if cfg.x_fp8 else u_s
+    need = sorted(set(r.idx.ravel().tolist()) | set(range(cfg.Nr, cfg.Nr + cfg.Ns)))
+
+    def expert_w(i):
+        if weights.w_t == 2:   # E4M3 codes + 128x128 block scales
+            w13 = OE.dequantize_tiles(weights.w13[i].cpu().numpy(), weights.w13_scale[i].cpu().numpy(), 128, 128)
+            w2 = OE.dequantize_tiles(weights.w2[i].cpu().numpy(), weights.w2_scale[i].cpu().numpy(), 128, 128)
+            return w13, w2
+        return f64(weights.w13[i]), f64(weights.w2[i])
+
+    t_ffn = 0.0
+    y_routed = np.zeros((S, cfg.K, cfg.d))
+    y_shared = np.zeros((cfg.Ns, S, cfg.d))
+    for i in need:
+        w13, w2 = expert_w(i)
+        t1 = time.perf_counter()
+        if i >= cfg.Nr:
+            y_shared[i - cfg.Nr], _ = O.swiglu_ffn(x, w13, w2, h_quant=cfg.x_fp8)
+        else:
+            ts, ks = np.nonzero(r.idx == i)
+            y_routed[ts, ks], _ = O.swiglu_ffn(x[ts], w13, w2, h_quant=cfg.x_fp8)
+        t_ffn += time.perf_counter() - t1
+    t1 = time.perf_counter()
+    O.combine(u_s, y_shared, y_routed, r.gate)
+    t_comb = time.perf_counter() - t1
+    total = t_route + t_ffn + t_comb
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": S / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 routing over all {cfg.Nr} experts, "
+                      f"{cfg.K} routed + {cfg.Ns} shared SwiGLU experts per token, combine; "
+                      f"{len(need)} experts touched; weight conversion to fp64 not timed",
+            "seconds": total, "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

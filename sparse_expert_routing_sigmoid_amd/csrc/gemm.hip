@@ -10,6 +10,10 @@ size_t permute_tiles_max(int T, int K, int Nr, int Ns, int tile_m);
 void launch_ffn_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                      const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int d, int I, uint16_t* h,
                      void* y, bool y_f32, hipStream_t st);
+bool ffn_bf16_persistent_ok(int d, int I);
+void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
+                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
+                                uint16_t* h, void* y, bool y_f32, int* counters, hipStream_t st);
 void launch_ffn_f32(const float* x, const float* w13, const float* w2, const int32_t* row_token,
                     const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int d, int I, float* h, float* y,
                     hipStream_t st);
@@ -72,18 +76,27 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
   const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
   hipStream_t st = as_stream(stream);
   if (T == 0) return MOE_OK;
+  // Workspace: 256 bytes of scheduling counters, then h.
+  int* ws_counters = static_cast<int*>(ws);
+  uint8_t* ws_h = static_cast<uint8_t*>(ws) + 256;
   switch (p) {
     case Path::F32:
       MOE_REQUIRE(y_t == MOE_F32, MOE_EUNSUPPORTED, "fp32 path writes fp32 y");
       launch_ffn_f32(static_cast<const float*>(x), static_cast<const float*>(w13), static_cast<const float*>(w2),
-                     row_token, tile_map, n_tiles, tiles_max, d, I, static_cast<float*>(ws), static_cast<float*>(y),
-                     st);
+                     row_token, tile_map, n_tiles, tiles_max, d, I, reinterpret_cast<float*>(ws_h),
+                     static_cast<float*>(y), st);
       break;
     case Path::BF16:
       MOE_REQUIRE(d % 128 == 0 && I % 64 == 0, MOE_EUNSUPPORTED, "bf16 path needs d % 128 == 0 and I % 64 == 0");
-      launch_ffn_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
-                      static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, tiles_max, d, I,
-                      static_cast<uint16_t*>(ws), y, y_t == MOE_F32, st);
+      if (ffn_bf16_persistent_ok(d, I) && (unsigned long long)T * d * 2 < (1ull << 31) &&
+          (unsigned long long)P * I * 2 < (1ull << 31) && (unsigned long long)3 * I * d * 2 < (1ull << 31))
+        launch_ffn_bf16_persistent(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
+                                   static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, T, (long long)P, d,
+                                   I, reinterpret_cast<uint16_t*>(ws_h), y, y_t == MOE_F32, ws_counters, st);
+      else
+        launch_ffn_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
+                        static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, tiles_max, d, I,
+                        reinterpret_cast<uint16_t*>(ws_h), y, y_t == MOE_F32, st);
       break;
     default:
       MOE_REQUIRE(false, MOE_EUNSUPPORTED, "fp8 paths not built yet");

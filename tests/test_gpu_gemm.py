@@ -83,3 +83,15 @@ def test_bf16_mid_config_rows():
     u = W.make_tokens(cfg, 0, "cpu")
     r = O.route(f64_of(u), f64_of(W.make_centroids(cfg, "cpu")), f64_of(W.make_bias(cfg, "cpu")), cfg.K)
     run_case(cfg, torch.from_numpy(r.idx), tile_m=32)
+
+
+@pytest.mark.parametrize("T,d,I,Ns,tile_m,ydt", [(700, 512, 256, 2, 32, torch.bfloat16),
+                                                 (700, 512, 256, 1, 16, torch.float32),
+                                                 (1030, 768, 384, 1, 1, torch.bfloat16),
+                                                 (64, 2048, 1024, 1, 32, torch.bfloat16)])
+def test_bf16_persistent_kernel_shapes(T, d, I, Ns, tile_m, ydt):
+    """Shapes the persistent XCD-aware kernel takes (d % 256 == 0, I % 128 == 0):
+    segments of 1..T rows, multi-tile segments, partial 32-row groups."""
+    cfg = W.CONFIGS["mid_bf16"].with_(T=T, d=d, I=I, Nr=12, Ns=Ns, K=3)
+    idx = make_idx(T, cfg.Nr, cfg.K, T + d, hot=[4, 9])
+    run_case(cfg, idx, tile_m=tile_m, y_dtype=ydt)
