@@ -66,15 +66,23 @@ struct Item {
   int rows, row0, nk;
 };
 
-// Loads the K slab starting at byte `kb` of every row into stage buffer `dst`.
-__device__ __forceinline__ void issue_stage(const Item& it, uint8_t* __restrict__ dst, uint32_t kb) {
+// Loads part Q (of 4) of the K slab starting at byte `kb` into stage buffer
+// `dst`: instructions j = 2Q, 2Q+1 of the wave for A and for B.  Q = -1
+// loads the whole slab.
+template <int Q>
+__device__ __forceinline__ void issue_part(const Item& it, uint8_t* __restrict__ dst, uint32_t kb) {
   uint8_t* sb = dst + P_TM * P_ROWB;
+  constexpr int j0 = Q < 0 ? 0 : 2 * Q;
+  constexpr int j1 = Q < 0 ? 8 : 2 * Q + 2;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = j0; j < j1; ++j) {
     const int g = it.wave * 8 + j;
     if (g < it.a_groups) dma16(it.ra, dst + g * 1024, it.a_off[j], kb);
     dma16(it.rb, sb + g * 1024, it.b_off[j], kb);
   }
+}
+__device__ __forceinline__ void issue_stage(const Item& it, uint8_t* __restrict__ dst, uint32_t kb) {
+  issue_part<-1>(it, dst, kb);
 }
 
 template <int MT>
@@ -92,35 +100,41 @@ __device__ __forceinline__ void load_frags(bf16x8_v (&af)[4], bf16x8_v (&bf)[4],
     af[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(src + (it.mrow0 + i * 32 + lr) * P_ROWB + cofs));
 }
 
-// One 64-wide K slab of MFMAs from stage buffer `src` (A rows, then B rows).
-// Fragments are double-buffered by hand: the reads of k-step kk+1 are issued
-// before the MFMAs of k-step kk, and a scheduling barrier after each k-step
-// keeps the compiler from hoisting further reads.
-template <int MT>
-__device__ __forceinline__ void mma_stage(f32x16_v (&acc)[MT][4], const uint8_t* __restrict__ src, const Item& it) {
-  bf16x8_v af[2][4], bf[2][4];
-  load_frags<MT>(af[0], bf[0], src, it, 0);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    if (kk + 1 < 4) load_frags<MT>(af[(kk + 1) & 1], bf[(kk + 1) & 1], src, it, kk + 1);
+// One 64-wide K slab of MFMAs from stage buffer `src` (A rows, then B rows),
+// with the loads of the next slab into `dst` spread over its four k-steps
+// (a quarter before each k-step's MFMAs), so a wave never stalls behind a
+// long burst of memory instructions.  Fragments are double-buffered by hand:
+// the reads of k-step kk+1 are issued before the MFMAs of k-step kk, and a
+// scheduling barrier after each k-step keeps the compiler from moving work
+// across k-steps.  The stage pointers are restrict-qualified so the compiler
+// knows the loads into one stage never alias the fragment reads of the other
+// and does not wait for those loads before the MFMAs.
+template <int MT, int KK>
+__device__ __forceinline__ void kstep(f32x16_v (&acc)[MT > 0 ? MT : 1][4], bf16x8_v (&af)[2][4],
+                                      bf16x8_v (&bf)[2][4], const Item& it, uint8_t* __restrict__ dst,
+                                      const uint8_t* __restrict__ src, bool load_next, uint32_t next_kb) {
+  if (load_next) issue_part<KK>(it, dst, next_kb);
+  if constexpr (MT > 0) {
+    if (KK + 1 < 4) load_frags<MT>(af[(KK + 1) & 1], bf[(KK + 1) & 1], src, it, KK + 1);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bf[kk & 1][j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[KK & 1][i], bf[KK & 1][j], acc[i][j], 0, 0, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// One pipeline step: start loading the next slab into `dst`, multiply the
-// slab already in `src`.  The stage pointers are restrict-qualified so the
-// compiler knows the DMA into one stage never aliases the fragment reads of
-// the other and does not wait for those loads before the MFMAs.
 template <int MT>
-__device__ __forceinline__ void pipe_step(f32x16_v (&acc)[MT][4], const Item& it, uint8_t* __restrict__ dst,
-                                          const uint8_t* __restrict__ src, bool load_next, uint32_t next_kb) {
-  if (load_next) issue_stage(it, dst, next_kb);
-  mma_stage<MT>(acc, src, it);
+__device__ __forceinline__ void pipe_step(f32x16_v (&acc)[MT > 0 ? MT : 1][4], const Item& it,
+                                          uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+                                          bool load_next, uint32_t next_kb) {
+  bf16x8_v af[2][4], bf[2][4];
+  if constexpr (MT > 0) load_frags<MT>(af[0], bf[0], src, it, 0);
+  kstep<MT, 0>(acc, af, bf, it, dst, src, load_next, next_kb);
+  kstep<MT, 1>(acc, af, bf, it, dst, src, load_next, next_kb);
+  kstep<MT, 2>(acc, af, bf, it, dst, src, load_next, next_kb);
+  kstep<MT, 3>(acc, af, bf, it, dst, src, load_next, next_kb);
 }
 
 __device__ __forceinline__ void store8(uint16_t* p, float4 a, float4 b) {
@@ -205,16 +219,10 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
   for (int s = 0; s < it.nk; s += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (MT > 0)
-      pipe_step<MA>(acc, it, st1, st0, true, (uint32_t)(s + 1) * P_TK * 2u);
-    else
-      issue_stage(it, st1, (uint32_t)(s + 1) * P_TK * 2u);
+    pipe_step<MT>(acc, it, st1, st0, true, (uint32_t)(s + 1) * P_TK * 2u);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (MT > 0)
-      pipe_step<MA>(acc, it, st0, st1, s + 2 < it.nk, (uint32_t)(s + 2) * P_TK * 2u);
-    else if (s + 2 < it.nk)
-      issue_stage(it, st0, (uint32_t)(s + 2) * P_TK * 2u);
+    pipe_step<MT>(acc, it, st0, st1, s + 2 < it.nk, (uint32_t)(s + 2) * P_TK * 2u);
   }
   epilogue<PHASE_A, MT, MA, OT>(acc, it, st0, st1, wm, wn, tid, out, Nd, n);
 }
