@@ -5,12 +5,15 @@
 // selection on s + b, kept value s (gate equation); gates are the kept
 // values normalised over the selection; ties go to the lower expert index.
 //
-// Two kernels:
-//   k_router_logits  z[t, i] = u_t . e_i in fp32 on the vector ALUs, LDS
-//                    tiles of 64 tokens x 64 experts; every 32-wide K chunk
-//                    is summed into its own partial before it joins the
-//                    running sum, which keeps the fp32 error of a d = 7168
-//                    dot product near 1e-7.
+// Kernels:
+//   k_router_logits_mfma  (bf16 u, Nr <= 256) z = u . e on bf16 MFMA with e
+//                    split exactly into three bf16 parts; K split over
+//                    blocks into partial sums added in a fixed order later.
+//   k_router_logits  (fp32 u, or other shapes) z[t, i] = u_t . e_i in fp32 on
+//                    the vector ALUs, LDS tiles of 64 tokens x 64 experts;
+//                    every 32-wide K chunk is summed into its own partial
+//                    before it joins the running sum, which keeps the fp32
+//                    error of a d = 7168 dot product near 1e-7.
 //   k_route_select   one wave per token: sigmoid, + bias, K rounds of a
 //                    wave-wide max over 64-bit (order key of s+b, ~index)
 //                    keys, gate normalisation, load count (integer atomics:
@@ -84,6 +87,139 @@ __global__ __launch_bounds__(256) void k_router_logits(const UT* __restrict__ u,
   }
 }
 
+// ---- bf16 activations: logits on MFMA with a three-way bf16 split of e.
+// e = e1 + e2 + e3 with e1 = bf16(e), e2 = bf16(e - e1), e3 = bf16(e - e1 - e2)
+// (each remainder is exact in fp32), so e is represented to about 2^-27
+// relative, every product u * e_k is exact in fp32 and the MFMA sums them in
+// fp32.  The split is made once per call into the workspace.
+typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
+typedef float f32x16_r __attribute__((ext_vector_type(16)));
+
+__global__ void k_split_centroids(const float* __restrict__ e, long long n, uint16_t* __restrict__ e3) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = e[i];
+  const __bf16 a = static_cast<__bf16>(v);
+  const float r1 = v - static_cast<float>(a);
+  const __bf16 b = static_cast<__bf16>(r1);
+  const float r2 = r1 - static_cast<float>(b);
+  const __bf16 c = static_cast<__bf16>(r2);
+  e3[i] = __builtin_bit_cast(uint16_t, a);
+  e3[n + i] = __builtin_bit_cast(uint16_t, b);
+  e3[2 * n + i] = __builtin_bit_cast(uint16_t, c);
+}
+
+constexpr int RM_TT = 128;              // tokens per block
+constexpr int RM_TE = 256;              // experts per block (all, Nr <= 256)
+constexpr int RM_BK = 32;               // K per stage
+constexpr int RM_ROW = RM_BK * 2 + 16;  // LDS row bytes (64 B of data + 16 B pad against bank conflicts)
+constexpr int RM_BROWS = 3 * RM_TE;     // B rows: e1, e2, e3 of 256 experts
+
+// Partial logits zp[ks][t][i] = sum over the ks-th K chunk of u[t,k] * e[i,k].
+// Grid (T / 128, KS); 256 threads = 4 waves; wave w covers all 128 tokens of
+// the block and experts 64 w .. 64 w + 63 (4 x 2 MFMA 32x32 tiles), running
+// the three bf16 parts of e into the same fp32 accumulators.  Operands are
+// staged through registers into a padded, double-buffered LDS tile.
+__global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __restrict__ u,
+                                                            const uint16_t* __restrict__ e3, int T, int d, int Nr,
+                                                            int kchunk, float* __restrict__ zp) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t rs[];
+  constexpr int SBYTES = (RM_TT + RM_BROWS) * RM_ROW;  // one stage
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RM_TT;
+  const int ks = blockIdx.y;
+  const int k_begin = ks * kchunk;
+  const int nk = kchunk / RM_BK;
+  const long long nE = (long long)Nr * d;
+  // staging: A = 128 rows x 4 chunks (2 per thread), B = 768 rows x 4 chunks (12 per thread)
+  uint4 ra[2], rb[12];
+  auto gload = [&](int stage) {
+    const int kofs = k_begin + stage * RM_BK;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
+      const int t = t0 + r;
+      ra[q] = t < T ? *reinterpret_cast<const uint4*>(u + (long long)t * d + kofs + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+      const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
+      const int part = r / RM_TE, ex = r % RM_TE;
+      rb[q] = ex < Nr ? *reinterpret_cast<const uint4*>(e3 + part * nE + (long long)ex * d + kofs + ch * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](uint8_t* sb) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
+      *reinterpret_cast<uint4*>(sb + r * RM_ROW + ch * 16) = ra[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+      const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
+      *reinterpret_cast<uint4*>(sb + (RM_TT + r) * RM_ROW + ch * 16) = rb[q];
+    }
+  };
+  f32x16_r acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  const int e0 = wave * 64;  // this wave's experts
+  gload(0);
+  lstore(rs);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    uint8_t* cur = rs + (s & 1) * SBYTES;
+    if (s + 1 < nk) gload(s + 1);
+#pragma unroll
+    for (int kk = 0; kk < RM_BK / 16; ++kk) {
+      const int cofs = (kk * 2 + (lane >> 5)) * 16;
+      bf16x8_r af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = __builtin_bit_cast(bf16x8_r, *reinterpret_cast<const uint4*>(cur + (i * 32 + (lane & 31)) * RM_ROW + cofs));
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_r bfr = __builtin_bit_cast(
+              bf16x8_r, *reinterpret_cast<const uint4*>(
+                            cur + (RM_TT + part * RM_TE + e0 + j * 32 + (lane & 31)) * RM_ROW + cofs));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
+        }
+    }
+    if (s + 1 < nk) lstore(rs + ((s + 1) & 1) * SBYTES);
+    __syncthreads();
+  }
+  float* zo = zp + (long long)ks * T * Nr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int t = t0 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int ex = e0 + j * 32 + (lane & 31);
+        if (t < T && ex < Nr) zo[(long long)t * Nr + ex] = acc[i][j][q];
+      }
+}
+
+// K-split count of the MFMA router for T tokens and hidden size d (0 = the
+// MFMA router does not apply): enough blocks to fill the chip, each chunk a
+// multiple of the stage width.
+int router_ksplit(int T, int d, int Nr) {
+  if (Nr > RM_TE || d % RM_BK != 0) return 0;
+  const int tiles = (T + RM_TT - 1) / RM_TT;
+  int ks = 1;
+  while (ks < 8 && tiles * ks < 512 && d % (RM_BK * ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
 __global__ void k_zero_i32(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -91,8 +227,9 @@ __global__ void k_zero_i32(int32_t* p, int n) {
 
 // EPL = experts per lane (Nr <= 64 * EPL).
 template <int EPL>
-__global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ z, const float* __restrict__ bias,
-                                                      int T, int Nr, int K, int32_t* __restrict__ topk_idx,
+__global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ z, int nparts,
+                                                      const float* __restrict__ bias, int T, int Nr, int K,
+                                                      int32_t* __restrict__ topk_idx,
                                                       float* __restrict__ topk_gate, float* __restrict__ topk_score,
                                                       int32_t* __restrict__ load) {
   const int lane = threadIdx.x & 63;
@@ -104,7 +241,8 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
   for (int j = 0; j < EPL; ++j) {
     const int i = lane + 64 * j;
     if (i < Nr) {
-      const float zz = z[(long long)t * Nr + i];
+      float zz = z[(long long)t * Nr + i];
+      for (int p = 1; p < nparts; ++p) zz += z[(long long)p * T * Nr + (long long)t * Nr + i];  // fixed order
       s[j] = 1.0f / (1.0f + expf(-zz));
       const float v = s[j] + bias[i];
       key[j] = (static_cast<unsigned long long>(float_order_key(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
@@ -154,20 +292,24 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
 }
 
 template <int EPL>
-void launch_select(const float* z, const float* bias, int T, int Nr, int K, int32_t* idx, float* gate, float* score,
-                   int32_t* load, hipStream_t st) {
+void launch_select(const float* z, int nparts, const float* bias, int T, int Nr, int K, int32_t* idx, float* gate,
+                   float* score, int32_t* load, hipStream_t st) {
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block);
-  hipLaunchKernelGGL(k_route_select<EPL>, grid, dim3(64 * waves_per_block), 0, st, z, bias, T, Nr, K, idx, gate, score,
-                     load);
+  hipLaunchKernelGGL(k_route_select<EPL>, grid, dim3(64 * waves_per_block), 0, st, z, nparts, bias, T, Nr, K, idx,
+                     gate, score, load);
 }
 
 }  // namespace
 
+// Workspace: partial logits [KS][T][Nr] fp32 (KS = 1 on the fp32 path),
+// then the bf16 split of the centroids [3][Nr][d] for the MFMA path.
 size_t route_workspace_bytes(int T, int d, int Nr) {
-  (void)d;
-  if (T < 0 || Nr < 0) return 0;
-  return static_cast<size_t>(T) * static_cast<size_t>(Nr) * sizeof(float) + 256;
+  if (T < 0 || Nr < 0 || d < 0) return 0;
+  const int ks = router_ksplit(T, d, Nr);
+  const size_t z = (size_t)(ks > 0 ? ks : 1) * (size_t)T * (size_t)Nr * sizeof(float);
+  const size_t split = (size_t)3 * Nr * d * 2;
+  return ((z + 255) / 256) * 256 + split + 256;
 }
 
 moe_status route(const void* u, moe_dtype u_t, const float* centroids, const float* bias, int T, int d, int Nr, int K,
@@ -185,19 +327,42 @@ moe_status route(const void* u, moe_dtype u_t, const float* centroids, const flo
   hipLaunchKernelGGL(k_zero_i32, dim3((Nr + 255) / 256), dim3(256), 0, st, expert_load, Nr);
   if (T > 0) {
     float* z = static_cast<float*>(ws);
-    dim3 grid((T + LG_TT - 1) / LG_TT, (Nr + LG_TE - 1) / LG_TE);
-    if (u_t == MOE_F32)
-      hipLaunchKernelGGL(k_router_logits<float>, grid, dim3(256), 0, st, static_cast<const float*>(u), centroids, T, d,
-                         Nr, z);
-    else
-      hipLaunchKernelGGL(k_router_logits<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(u), centroids,
-                         T, d, Nr, z);
+    int nparts = 1;
+    const int ks = u_t == MOE_BF16 ? router_ksplit(T, d, Nr) : 0;
+    if (ks > 0) {
+      const size_t zbytes = (size_t)ks * T * Nr * sizeof(float);
+      uint16_t* e3 = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + ((zbytes + 255) / 256) * 256);
+      const long long n = (long long)Nr * d;
+      hipLaunchKernelGGL(k_split_centroids, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, centroids, n, e3);
+      dim3 grid((T + RM_TT - 1) / RM_TT, ks);
+      const size_t lds = 2 * (size_t)(RM_TT + RM_BROWS) * RM_ROW;
+      static bool attr_set = false;  // raising the dynamic LDS limit is idempotent
+      if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_router_logits_mfma),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+          set_error("moe_route: cannot raise the LDS limit of the router kernel");
+          return MOE_EHIP;
+        }
+        attr_set = true;
+      }
+      hipLaunchKernelGGL(k_router_logits_mfma, grid, dim3(256), lds, st, static_cast<const uint16_t*>(u), e3, T, d, Nr,
+                         d / ks, z);
+      nparts = ks;
+    } else {
+      dim3 grid((T + LG_TT - 1) / LG_TT, (Nr + LG_TE - 1) / LG_TE);
+      if (u_t == MOE_F32)
+        hipLaunchKernelGGL(k_router_logits<float>, grid, dim3(256), 0, st, static_cast<const float*>(u), centroids, T,
+                           d, Nr, z);
+      else
+        hipLaunchKernelGGL(k_router_logits<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(u),
+                           centroids, T, d, Nr, z);
+    }
     if (Nr <= 64)
-      launch_select<1>(z, bias, T, Nr, K, topk_idx, topk_gate, topk_score, expert_load, st);
+      launch_select<1>(z, nparts, bias, T, Nr, K, topk_idx, topk_gate, topk_score, expert_load, st);
     else if (Nr <= 256)
-      launch_select<4>(z, bias, T, Nr, K, topk_idx, topk_gate, topk_score, expert_load, st);
+      launch_select<4>(z, nparts, bias, T, Nr, K, topk_idx, topk_gate, topk_score, expert_load, st);
     else
-      launch_select<16>(z, bias, T, Nr, K, topk_idx, topk_gate, topk_score, expert_load, st);
+      launch_select<16>(z, nparts, bias, T, Nr, K, topk_idx, topk_gate, topk_score, expert_load, st);
   }
   return launch_status("moe_route");
 }
