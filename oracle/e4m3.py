@@ -19,9 +19,12 @@ Sources
 The pages name E4M3 and the tile shapes but print neither the variant nor the
 scale rule.  Readings taken here (the same readings the GPU side implements):
   * variant: OCP E4M3FN (largest finite 448), the native fp8 of the target;
-  * scale of a tile: sc = fl32(amax) / 448 in IEEE fp32, or 1 when amax == 0;
-  * code of x: round-to-nearest-even of clamp(fl32(x) / sc, -448, 448), the
-    division in IEEE fp32; NaN is never produced.
+  * scale of a tile: the smallest power of two 2^k with amax <= 448 * 2^k
+    (k >= -126; an all-zero tile has scale 1).  A power-of-two scale is what
+    the target's block-scaled matrix instructions apply (an E8M0 exponent),
+    and it makes x / scale and code * scale exact;
+  * code of x: round-to-nearest-even of x / scale (exact), which lies in
+    [-448, 448]; NaN is never produced.
 """
 from __future__ import annotations
 
@@ -95,13 +98,35 @@ def quantize_tiles(x: np.ndarray, tile_rows: int, tile_cols: int):
     if not np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64)):
         raise ValueError("quantize_tiles: input not exactly representable in fp32")
     rt, ct = rows // tile_rows, cols // tile_cols
-    tiles = x32.reshape(rt, tile_rows, ct, tile_cols)
-    amax = np.abs(tiles).max(axis=(1, 3))                       # fp32, exact
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    scaled = tiles / scale[:, None, :, None]                    # IEEE fp32 division
-    scaled = np.clip(scaled, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
-    codes = e4m3_encode_rne(scaled.astype(np.float64)).reshape(rows, cols)
-    return codes, scale
+    tiles = x32.reshape(rt, tile_rows, ct, tile_cols).astype(np.float64)
+    amax = np.abs(tiles).max(axis=(1, 3))                       # exact
+    scale = pow2_scales(amax)
+    scaled = tiles / scale[:, None, :, None]                    # exact: a power of two
+    codes = e4m3_encode_rne(scaled).reshape(rows, cols)
+    return codes, scale.astype(np.float32)
+
+
+def pow2_scales(amax: np.ndarray) -> np.ndarray:
+    """Smallest 2^k (k >= -126) with amax <= 448 * 2^k, elementwise; 1 where amax == 0.
+
+    With amax = m * 2^e (frexp: 0.5 <= m < 1) and 448 = 0.875 * 2^9, the
+    condition m * 2^e <= 0.875 * 2^(9 + k) holds first at k = e - 9 when
+    m <= 0.875 and at k = e - 8 otherwise."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(amax)
+    k = np.where(m <= 0.875, e - 9, e - 8)
+    k = np.maximum(k, -126)
+    return np.where(amax > 0, np.ldexp(1.0, k), 1.0)
+
+
+def pow2_scale(amax: float) -> float:
+    """The same scale found by search: the first k from -126 up that works."""
+    if amax == 0.0:
+        return 1.0
+    k = -126
+    while amax > E4M3_MAX * 2.0 ** k:
+        k += 1
+    return 2.0 ** k
 
 
 def dequantize_tiles(codes: np.ndarray, scale: np.ndarray, tile_rows: int, tile_cols: int) -> np.ndarray:

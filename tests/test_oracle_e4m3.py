@@ -89,22 +89,49 @@ def test_quantize_zero_tile_has_unit_scale():
     assert np.all(sc == 1.0) and np.all(q == 0)
 
 
+def test_pow2_scale_definition():
+    # smallest power of two with amax <= 448 * scale
+    assert e4m3.pow2_scale(448.0) == 1.0
+    assert e4m3.pow2_scale(448.0001) == 2.0
+    assert e4m3.pow2_scale(224.0) == 0.5
+    assert e4m3.pow2_scale(225.0) == 1.0
+    assert e4m3.pow2_scale(1.0) == 2.0 ** -8          # 448 * 2^-9 = 0.875 < 1 <= 1.75
+    assert e4m3.pow2_scale(0.0) == 1.0
+    assert e4m3.pow2_scale(1e-45) == 2.0 ** -126
+
+
+def test_vectorised_pow2_scale_matches_search():
+    rng = np.random.default_rng(21)
+    amax = np.concatenate([
+        np.abs(rng.standard_t(2, 3000)) * np.exp2(rng.integers(-40, 40, 3000)),
+        448.0 * np.exp2(np.arange(-30, 30)), 0.875 * 448.0 * np.exp2(np.arange(-5, 5)),
+        np.nextafter(448.0 * np.exp2(np.arange(-5, 5)), np.inf), [0.0, 1e-45, 1e-39],
+    ]).astype(np.float32).astype(np.float64)
+    got = e4m3.pow2_scales(amax)
+    want = np.array([e4m3.pow2_scale(float(a)) for a in amax])
+    assert np.array_equal(got, want)
+
+
 def test_quantize_tiles_scale_and_codes_match_torch():
     rng = np.random.default_rng(3)
     x = rng.normal(0, 1, (256, 384)).astype(np.float32)
+    x *= np.exp2(rng.integers(-20, 20, (256, 1))).astype(np.float32)
     x[5, :128] = 0.0
     for tr, tc in ((1, 128), (128, 128)):
         q, sc = e4m3.quantize_tiles(x, tr, tc)
         assert sc.dtype == np.float32 and sc.shape == (256 // tr, 384 // tc)
-        amax = np.abs(x.reshape(256 // tr, tr, 3, tc)).max(axis=(1, 3))
-        want_sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0))
-        assert np.array_equal(sc, want_sc)
-        scaled = torch.from_numpy(x) / torch.from_numpy(np.repeat(np.repeat(sc, tr, 0), tc, 1))
-        ref = scaled.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        amax = np.abs(x.reshape(256 // tr, tr, 3, tc)).max(axis=(1, 3)).astype(np.float64)
+        # scales are powers of two and put amax in (224, 448] (or 1 for a zero tile)
+        m, _ = np.frexp(sc.astype(np.float64))
+        assert np.all(m == 0.5)
+        nz = amax > 0
+        ratio = amax[nz] / sc[nz]
+        assert np.all(ratio <= 448.0) and np.all(ratio > 224.0)
+        assert np.all(sc[~nz] == 1.0)
+        # codes: torch's own E4M3 conversion of the (exactly) scaled values
+        scaled = torch.from_numpy(x.astype(np.float64)) / torch.from_numpy(np.repeat(np.repeat(sc, tr, 0), tc, 1).astype(np.float64))
+        ref = scaled.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         assert np.array_equal(q, ref)
-        # the largest magnitude of every non-zero tile lands on +-448
-        deq_codes = np.abs(e4m3.e4m3_decode(q)).reshape(256 // tr, tr, 3, tc).max(axis=(1, 3))
-        assert np.all(deq_codes[amax > 0] == 448.0)
 
 
 def test_dequantize_error_within_half_ulp():
@@ -114,7 +141,7 @@ def test_dequantize_error_within_half_ulp():
     deq = e4m3.dequantize_tiles(q, sc, 1, 128)
     s = np.repeat(sc.astype(np.float64), 128, axis=1)
     err = np.abs(deq - x)
-    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s) * (1 + 1e-6)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s)   # half an ulp, normal or subnormal
     assert np.all(err <= bound)
 
 
