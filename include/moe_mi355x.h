@@ -162,13 +162,17 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, in
  *   y, y_t      device [P_max, d] out, MOE_F32 or MOE_BF16
  * Supported (x_t, w_t, y_t): (F32, F32, F32); (BF16, BF16, BF16|F32);
  * (BF16, E4M3, BF16) - fp8 weights, bf16 activations, h kept in bf16;
- * (E4M3, E4M3, BF16) - fp8 activations and weights; h is re-quantised to
- * E4M3 in 1x128 tiles before the down projection.
- * fp8 block scales are applied per 128-wide K block in fp32; accumulation
- * is fp32 throughout.
+ * (E4M3, E4M3, BF16|F32) - fp8 activations and weights; h is re-quantised
+ * to E4M3 in 1x128 tiles (scale rule of fp8_quantize_tiles) before the down
+ * projection.
+ * E4M3 scales must be powers of two, as fp8_quantize_tiles writes them: the
+ * matrix instructions apply them as exponents per 128-wide K block, which is
+ * exact; only the exponent field of a scale is read.  Accumulation is fp32
+ * throughout.
  *   Errors: MOE_EINVAL for NULL pointers or bad sizes; MOE_EUNSUPPORTED for
- *   other dtype combinations or fp8 with d or I not a multiple of 128, or d,
- *   I not multiples of 64 on the MFMA paths; MOE_EWORKSPACE for a small ws.
+ *   other dtype combinations; bf16 with d % 128 or I % 64 nonzero; E4M3 x E4M3
+ *   with d or I not a multiple of 256 or above 8192; an operand of 2 GiB or
+ *   more on the MFMA paths; MOE_EWORKSPACE for a small ws.
  * ---------------------------------------------------------------------- */
 size_t moe_gemm_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m,
                                 moe_dtype x_t, moe_dtype w_t);
@@ -219,9 +223,12 @@ moe_status moe_bias_update(const int32_t* expert_load, int Nr, long long total_a
 /* ------------------------------------------------------------------------
  * fp8_quantize_tiles: tile-wise E4M3 quantisation ([RG-FP8]: 1x128 tiles for
  * activations, 128x128 blocks for weights).  The pages give no scale rule;
- * this library uses, per tile, sc = amax / 448 in IEEE fp32 (sc = 1 for an
- * all-zero tile) and code = round-to-nearest-even(clamp(x / sc, -448, 448)),
- * the division in IEEE fp32.  NaN is never produced for finite input.
+ * this library uses, per tile, the power of two sc = 2^k with the smallest
+ * k >= -126 such that amax <= 448 * sc (sc = 1 for an all-zero tile), and
+ * code = round-to-nearest-even(x / sc) (exact division).  A power-of-two
+ * scale is the E8M0 block scale the gfx950 scaled MFMA applies in hardware;
+ * code * sc is exact in fp32 and in bf16.  NaN is never produced for finite
+ * input.  Scales are stored as fp32 values.
  *
  *   x, x_t     device [rows, cols], MOE_F32 or MOE_BF16
  *   tile_rows  1 or 128 (rows must be a multiple of it); tile_cols 128

@@ -82,6 +82,28 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return code | sign;
 }
 
+// Power-of-two tile scale: the smallest 2^k (k >= -126) with amax <= 448 * 2^k,
+// or k = 0 for amax == 0.  With amax = 1.M * 2^(E-127): k = E - 135 when
+// 1.M <= 1.75 (mantissa field <= 0x600000), else E - 134.  Returns k.
+__host__ __device__ __forceinline__ int pow2_scale_exp(float amax) {
+  uint32_t b;
+  __builtin_memcpy(&b, &amax, 4);
+  b &= 0x7FFFFFFFu;
+  if (b == 0) return 0;
+  const int E = (int)(b >> 23);
+  if (E == 0) return -126;  // subnormal amax
+  const int k = (b & 0x7FFFFFu) <= 0x600000u ? E - 135 : E - 134;
+  return k < -126 ? -126 : k;
+}
+
+// 2^k as fp32 for -126 <= k <= 127.
+__host__ __device__ __forceinline__ float exp2_int(int k) {
+  const uint32_t b = (uint32_t)(k + 127) << 23;
+  float f;
+  __builtin_memcpy(&f, &b, 4);
+  return f;
+}
+
 // ---------------------------------------------------------- wave helpers --
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll

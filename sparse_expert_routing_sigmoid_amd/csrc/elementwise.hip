@@ -119,11 +119,9 @@ __device__ __forceinline__ float ld<float>(const float* p, long long i) { return
 template <>
 __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, long long i) { return bf16_to_f32(p[i]); }
 
-__device__ __forceinline__ uint32_t quant_one(float x, float sc) {
-  float q = x / sc;  // IEEE fp32 division
-  q = fminf(fmaxf(q, -448.0f), 448.0f);
-  return f32_to_e4m3(q);
-}
+// x * 2^-k is exact (a power of two) and lies in [-448, 448] for every x of
+// the tile, so the code is the round-to-nearest-even of x / scale.
+__device__ __forceinline__ uint32_t quant_one(float x, float inv_scale) { return f32_to_e4m3(x * inv_scale); }
 
 // 1 x 128 tiles: one wave per tile, two values per lane.
 template <typename XT>
@@ -138,8 +136,9 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const XT* __restrict__ x, l
   const long long o = r * cols + c;
   const float a = ld(x, o), b = ld(x, o + 1);
   const float amax = wave_max_f32(fmaxf(fabsf(a), fabsf(b)));
-  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-  const uint32_t qa = quant_one(a, sc), qb = quant_one(b, sc);
+  const int k = pow2_scale_exp(amax);
+  const float sc = exp2_int(k), inv = exp2_int(-k);
+  const uint32_t qa = quant_one(a, inv), qb = quant_one(b, inv);
   *reinterpret_cast<uint16_t*>(q + o) = static_cast<uint16_t>(qa | (qb << 8));
   if (lane == 0) scale[tile] = sc;
 }
@@ -164,12 +163,13 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const XT* __restrict__ x,
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  const int k = pow2_scale_exp(amax);
+  const float sc = exp2_int(k), inv = exp2_int(-k);
   for (int rr = row0; rr < 128; rr += 8) {
     const long long o = (tr * 128 + rr) * cols + tcol * 128 + col;
     uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w |= quant_one(ld(x, o + i), sc) << (8 * i);
+    for (int i = 0; i < 4; ++i) w |= quant_one(ld(x, o + i), inv) << (8 * i);
     *reinterpret_cast<uint32_t*>(q + o) = w;
   }
   if (tid == 0) scale[blockIdx.x] = sc;

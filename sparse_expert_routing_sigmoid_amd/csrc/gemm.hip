@@ -14,6 +14,11 @@ bool ffn_bf16_persistent_ok(int d, int I);
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                                 const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                 uint16_t* h, void* y, bool y_f32, int* counters, hipStream_t st);
+bool ffn_fp8_persistent_ok(int d, int I);
+void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
+                               const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
+                               const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
+                               uint8_t* h, float* h_scale, void* y, bool y_f32, int* counters, hipStream_t st);
 void launch_ffn_f32(const float* x, const float* w13, const float* w2, const int32_t* row_token,
                     const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int d, int I, float* h, float* y,
                     hipStream_t st);
@@ -98,8 +103,22 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
                         static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, tiles_max, d, I,
                         reinterpret_cast<uint16_t*>(ws_h), y, y_t == MOE_F32, st);
       break;
+    case Path::FP8: {
+      MOE_REQUIRE(ffn_fp8_persistent_ok(d, I), MOE_EUNSUPPORTED,
+                  "fp8 path needs d % 256 == 0, I % 256 == 0, d <= 8192 and I <= 8192");
+      MOE_REQUIRE((unsigned long long)T * d < (1ull << 31) && (unsigned long long)P * I < (1ull << 31) &&
+                      (unsigned long long)3 * I * d < (1ull << 31),
+                  MOE_EUNSUPPORTED, "fp8 path: operand larger than 2 GiB");
+      // h: E4M3 codes [P, I], then their 1x128 tile scales [P, I / 128].
+      uint8_t* h_codes = ws_h;
+      float* h_scale = reinterpret_cast<float*>(ws_h + P * (size_t)I);
+      launch_ffn_fp8_persistent(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale,
+                                static_cast<const uint8_t*>(w2), w2_scale, row_token, tile_map, n_tiles, T,
+                                (long long)P, d, I, h_codes, h_scale, y, y_t == MOE_F32, ws_counters, st);
+      break;
+    }
     default:
-      MOE_REQUIRE(false, MOE_EUNSUPPORTED, "fp8 paths not built yet");
+      MOE_REQUIRE(false, MOE_EUNSUPPORTED, "bf16 activations with E4M3 weights are not built yet");
   }
   return launch_status("moe_expert_gemm");
 }

@@ -1,8 +1,11 @@
-// Persistent, XCD-aware grouped SwiGLU expert GEMM on bf16 MFMA (gfx950).
+// Persistent, XCD-aware grouped SwiGLU expert GEMMs on MFMA (gfx950): bf16,
+// and E4M3 x E4M3 with tile / block scales.
 //
 // The expert FFNs of the combine equation in the "DeepSeek-V3 Technical
 // Report" reading guide (xyznot.com, Method section 2), in the SwiGLU form
-// this library uses: h = SiLU(x W_gate^T) * (x W_up^T), y = h W_down^T.
+// this library uses: h = SiLU(x W_gate^T) * (x W_up^T), y = h W_down^T.  The
+// FP8 variant follows the same page's "Key ideas" FP8 bullet: E4M3 operands,
+// 1x128 activation tiles and 128x128 weight blocks, each with a scale.
 //
 // Work decomposition.  A work item is (row tile of the tile map, N tile).
 // Phase A: N tile = 128 h columns = 128 gate rows + the 128 up rows of the
@@ -14,20 +17,24 @@
 // XCD from a per-XCD atomic counter, in (row tile, N tile) order.  Results do
 // not depend on which block runs an item.
 //
-// Block tile: 256 rows x 256 weight rows x 64 K, 256 threads = 4 waves in a
-// 2 x 2 grid, each wave 128 x 128 as up to 4 x 4 MFMA 32x32x16 tiles with
+// Block tile: 256 rows x 256 weight rows x 128 bytes of K (64 bf16 or 128
+// E4M3 values: one scale block), 256 threads = 4 waves in a 2 x 2 grid, each
+// wave 128 x 128 as up to 4 x 4 MFMA 32x32 tiles (bf16: 32x32x16; E4M3:
+// the block-scaled 32x32x64, whose per-lane E8M0 scales carry the power-of-two
+// tile and block scales, so scaling is exact and costs no extra work) with
 // fp32 accumulators.  Operands go global -> LDS with the direct 16-byte LDS
-// load of buffer instructions (no register staging), two stages,
-// XOR-swizzled 16-byte chunks so MFMA fragment reads (32 rows, one K chunk)
-// spread over the banks.  Row groups past the tile's row count are neither
-// loaded nor multiplied: each wave runs a variant compiled for its number of
-// live 32-row MFMA tiles (MT), so no accumulator is ever conditionally
-// updated.
+// load of buffer instructions (no register staging), two stages, XOR-swizzled
+// 16-byte chunks so MFMA fragment reads (32 rows, one K chunk) spread over
+// the banks.  Rows past the tile's row count are loaded as zeros (out-of-range
+// buffer loads fetch nothing) and 32-row MFMA tiles with no live row are not
+// multiplied: each wave runs a variant compiled for its number of live tiles
+// (MT), so no accumulator is ever conditionally updated.
 #include "common.h"
 
 namespace moe {
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef int i32x8_v __attribute__((ext_vector_type(8)));
 typedef float f32x16_v __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -35,14 +42,23 @@ namespace {
 
 constexpr int P_TM = 256;          // rows per tile
 constexpr int P_TN = 256;          // weight rows per tile
-constexpr int P_TK = 64;           // K elements per stage
-constexpr int P_ROWB = P_TK * 2;   // bytes per LDS row (128)
-constexpr int P_STAGE = (P_TM + P_TN) * P_ROWB;  // 64 KB
+constexpr int P_ROWB = 128;        // bytes of K per stage and row
+constexpr int P_OPS = (P_TM + P_TN) * P_ROWB;  // A and B bytes of a stage (64 KB)
 constexpr int P_THREADS = 256;
+
+template <bool FP8>
+struct Fmt {
+  static constexpr int EB = FP8 ? 1 : 2;                 // bytes per element
+  static constexpr int KSTEPS = FP8 ? 2 : 4;             // MFMA k-steps per stage
+  static constexpr int STAGE = P_OPS + (FP8 ? 1024 : 0); // + 256 A-row scales (fp32)
+};
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + expf(-a)); }
 
 __device__ __forceinline__ int acc_row32(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// E8M0 exponent byte of a power-of-two fp32 scale.
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFF); }
 
 // Buffer resource over [base, base + bytes): reads past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -57,37 +73,45 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
 
 // Everything one wave needs to run a work item.
 struct Item {
-  __amdgpu_buffer_rsrc_t ra, rb;
+  __amdgpu_buffer_rsrc_t ra, rb, rs;  // A operand, B operand, A-row scales (FP8)
   uint32_t a_off[8], b_off[8];  // byte offsets of this lane's 8 A and 8 B rows (swizzled chunk included)
-  int a_groups;                 // 8-row groups of A that hold tile rows (wave-uniform)
+  uint32_t s_off;               // FP8: byte offset of the scale row of tile row 64 * wave + lane
+  float bsc0, bsc1;             // FP8: lane l holds the B-block scale of K block l (gate / up, or the wave's block)
   int wave, lane, lsw;
   int brow[4];                  // B rows of this wave's four 32-column MFMA tiles
   int mrow0;                    // first tile row of this wave
   int rows, row0, nk;
 };
 
-// Loads part Q (of 4) of the K slab starting at byte `kb` into stage buffer
-// `dst`: instructions j = 2Q, 2Q+1 of the wave for A and for B.  Q = -1
-// loads the whole slab.
-template <int Q>
-__device__ __forceinline__ void issue_part(const Item& it, uint8_t* __restrict__ dst, uint32_t kb) {
+// Loads part Q (of P) of the K slab starting at byte `kb` into stage buffer
+// `dst`: A and B instructions j in [8Q/P, 8(Q+1)/P), plus (FP8, part 0) the
+// A-row scales of the slab.  Q = -1 loads the whole slab.  `oob` is 0 or
+// 0x80000000: the latter turns every load into an out-of-range one that only
+// writes zeros to LDS, which lets the last step of a tile issue the same
+// instructions as the others.  The K loop then has no branches, so the
+// compiler cannot sink a step's MFMAs past the next barrier.  Row groups past
+// the tile's rows carry out-of-range offsets for the same reason.
+template <bool FP8, int Q, int P>
+__device__ __forceinline__ void issue_part(const Item& it, uint8_t* __restrict__ dst, uint32_t kb, uint32_t oob) {
   uint8_t* sb = dst + P_TM * P_ROWB;
-  constexpr int j0 = Q < 0 ? 0 : 2 * Q;
-  constexpr int j1 = Q < 0 ? 8 : 2 * Q + 2;
+  constexpr int j0 = Q < 0 ? 0 : 8 * Q / P;
+  constexpr int j1 = Q < 0 ? 8 : 8 * (Q + 1) / P;
 #pragma unroll
   for (int j = j0; j < j1; ++j) {
     const int g = it.wave * 8 + j;
-    if (g < it.a_groups) dma16(it.ra, dst + g * 1024, it.a_off[j], kb);
-    dma16(it.rb, sb + g * 1024, it.b_off[j], kb);
+    dma16(it.ra, dst + g * 1024, it.a_off[j] | oob, kb);
+    dma16(it.rb, sb + g * 1024, it.b_off[j] | oob, kb);
   }
-}
-__device__ __forceinline__ void issue_stage(const Item& it, uint8_t* __restrict__ dst, uint32_t kb) {
-  issue_part<-1>(it, dst, kb);
+  if constexpr (FP8) {
+    if (Q <= 0)  // 4 bytes per lane: scale of tile row 64 * wave + lane for K block kb / 128
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(it.rs, (lds_void_t*)(dst + P_OPS + it.wave * 256), 4, it.s_off | oob,
+                                               kb / P_ROWB * 4u, 0, 0);
+  }
 }
 
 template <int MT>
-__device__ __forceinline__ void load_frags(bf16x8_v (&af)[4], bf16x8_v (&bf)[4], const uint8_t* __restrict__ src,
-                                           const Item& it, int kk) {
+__device__ __forceinline__ void load_frags_bf16(bf16x8_v (&af)[4], bf16x8_v (&bf)[4], const uint8_t* __restrict__ src,
+                                                const Item& it, int kk) {
   const uint8_t* sb = src + P_TM * P_ROWB;
   const int c = kk * 2 + (it.lane >> 5);
   const int cofs = ((c ^ it.lsw) << 4);
@@ -100,41 +124,107 @@ __device__ __forceinline__ void load_frags(bf16x8_v (&af)[4], bf16x8_v (&bf)[4],
     af[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(src + (it.mrow0 + i * 32 + lr) * P_ROWB + cofs));
 }
 
-// One 64-wide K slab of MFMAs from stage buffer `src` (A rows, then B rows),
-// with the loads of the next slab into `dst` spread over its four k-steps
-// (a quarter before each k-step's MFMAs), so a wave never stalls behind a
-// long burst of memory instructions.  Fragments are double-buffered by hand:
-// the reads of k-step kk+1 are issued before the MFMAs of k-step kk, and a
-// scheduling barrier after each k-step keeps the compiler from moving work
-// across k-steps.  The stage pointers are restrict-qualified so the compiler
-// knows the loads into one stage never alias the fragment reads of the other
-// and does not wait for those loads before the MFMAs.
-template <int MT, int KK>
-__device__ __forceinline__ void kstep(f32x16_v (&acc)[MT > 0 ? MT : 1][4], bf16x8_v (&af)[2][4],
-                                      bf16x8_v (&bf)[2][4], const Item& it, uint8_t* __restrict__ dst,
-                                      const uint8_t* __restrict__ src, bool load_next, uint32_t next_kb) {
-  if (load_next) issue_part<KK>(it, dst, next_kb);
+// E4M3 fragments: 32 bytes per lane (two 16-byte chunks of K step kk).  A and
+// B use the same byte layout, and every scale is constant over the 64 K values
+// of one MFMA, so the hardware's K order inside a lane does not matter.
+__device__ __forceinline__ i32x8_v frag32(const uint8_t* row, int c0, int lsw) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c0 ^ lsw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c0 + 1) ^ lsw) << 4));
+  i32x8_v v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+template <int MT>
+__device__ __forceinline__ void load_frags_fp8(i32x8_v (&af)[4], i32x8_v (&bf)[4], const uint8_t* __restrict__ src,
+                                               const Item& it, int kk) {
+  const uint8_t* sb = src + P_TM * P_ROWB;
+  const int c0 = kk * 4 + (it.lane >> 5) * 2;
+  const int lr = it.lane & 31;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bf[j] = frag32(sb + (it.brow[j] + lr) * P_ROWB, c0, it.lsw);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) af[i] = frag32(src + (it.mrow0 + i * 32 + lr) * P_ROWB, c0, it.lsw);
+}
+
+// One k-step: a share of the next slab's loads, the fragments of the next
+// k-step, the MFMAs of this one.  Fragments are double-buffered by hand and
+// a scheduling barrier closes each k-step.  The stage pointers are
+// restrict-qualified so the compiler knows the loads into one stage never
+// alias the fragment reads of the other and does not wait for those loads
+// before the MFMAs.
+template <bool FP8, int MT, int KK, typename FragT>
+__device__ __forceinline__ void kstep(f32x16_v (&acc)[MT > 0 ? MT : 1][4], FragT (&af)[2][4], FragT (&bf)[2][4],
+                                      const int (&sa)[4], const int (&sbs)[4], const Item& it,
+                                      uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, bool load_next,
+                                      uint32_t next_kb) {
+  constexpr int KS = Fmt<FP8>::KSTEPS;
+  issue_part<FP8, KK, KS>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
   if constexpr (MT > 0) {
-    if (KK + 1 < 4) load_frags<MT>(af[(KK + 1) & 1], bf[(KK + 1) & 1], src, it, KK + 1);
+    if (KK + 1 < KS) {
+      if constexpr (FP8)
+        load_frags_fp8<MT>(af[(KK + 1) & 1], bf[(KK + 1) & 1], src, it, KK + 1);
+      else
+        load_frags_bf16<MT>(af[(KK + 1) & 1], bf[(KK + 1) & 1], src, it, KK + 1);
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[KK & 1][i], bf[KK & 1][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (FP8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[KK & 1][i], bf[KK & 1][j], acc[i][j], 0, 0,
+                                                                      0, sa[i], 0, sbs[j]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[KK & 1][i], bf[KK & 1][j], acc[i][j], 0, 0, 0);
+      }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MT>
+template <bool FP8, int MT>
 __device__ __forceinline__ void pipe_step(f32x16_v (&acc)[MT > 0 ? MT : 1][4], const Item& it,
-                                          uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+                                          uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int s,
                                           bool load_next, uint32_t next_kb) {
-  bf16x8_v af[2][4], bf[2][4];
-  if constexpr (MT > 0) load_frags<MT>(af[0], bf[0], src, it, 0);
-  kstep<MT, 0>(acc, af, bf, it, dst, src, load_next, next_kb);
-  kstep<MT, 1>(acc, af, bf, it, dst, src, load_next, next_kb);
-  kstep<MT, 2>(acc, af, bf, it, dst, src, load_next, next_kb);
-  kstep<MT, 3>(acc, af, bf, it, dst, src, load_next, next_kb);
+  if constexpr (FP8) {
+    // 32-byte E4M3 fragments are not double-buffered (register budget); an
+    // FP8 k-step is long enough (16 MFMAs of 64 K) to cover the LDS reads.
+    int sa[4] = {127, 127, 127, 127}, sbs[4] = {127, 127, 127, 127};
+    if constexpr (MT > 0) {
+      const float* scl = reinterpret_cast<const float*>(src + P_OPS);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) sa[i] = e8m0_of(scl[it.mrow0 + i * 32 + (it.lane & 31)]);
+      const int b0 = e8m0_of(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_uint(it.bsc0), s)));
+      const int b1 = e8m0_of(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_uint(it.bsc1), s)));
+      sbs[0] = b0; sbs[1] = b0; sbs[2] = b1; sbs[3] = b1;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (kk == 0)
+        issue_part<true, 0, 2>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
+      else
+        issue_part<true, 1, 2>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
+      if constexpr (MT > 0) {
+        i32x8_v af[4], bf[4];
+        load_frags_fp8<MT>(af, bf, src, it, kk);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0,
+                                                                        sbs[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    bf16x8_v af[2][4], bf[2][4];
+    const int sa[4] = {0, 0, 0, 0}, sbs[4] = {0, 0, 0, 0};
+    if constexpr (MT > 0) load_frags_bf16<MT>(af[0], bf[0], src, it, 0);
+    kstep<false, MT, 0>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
+    kstep<false, MT, 1>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
+    kstep<false, MT, 2>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
+    kstep<false, MT, 3>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
+  }
 }
 
 __device__ __forceinline__ void store8(uint16_t* p, float4 a, float4 b) {
@@ -149,15 +239,25 @@ __device__ __forceinline__ void store8(float* p, float4 a, float4 b) {
   *reinterpret_cast<float4*>(p) = a;
   *reinterpret_cast<float4*>(p + 4) = b;
 }
+__device__ __forceinline__ void store8(uint8_t*, float4, float4) {}  // E4M3 h is written by the quantising path
+
+__device__ __forceinline__ float absmax8(float4 a, float4 b) {
+  return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+               fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+}
 
 // Epilogue.  Two passes of 128 rows (wave row 0, then 1): the waves of the
 // pass write their fp32 accumulators to LDS (64 rows per stage buffer, one
 // 1 KB row = 256 fp32), then all threads copy the rows out with 16-byte
 // stores, applying SwiGLU (phase A: gate in columns 0..127, up in 128..255)
-// and converting to the output type.  MT == 0: the wave has no rows.
-template <bool PHASE_A, int MT, int MA, typename OT>
+// and converting to the output type.  With H_FP8 the 128 h values of a row
+// are quantised as one 1x128 E4M3 tile (power-of-two scale, round to nearest
+// even): the 16 threads holding a row find its amax with lane shuffles.
+// MT == 0: the wave has no rows.
+template <bool PHASE_A, bool H_FP8, int MT, int MA, typename OT>
 __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Item& it, uint8_t* st0, uint8_t* st1,
-                                         int wm, int wn, int tid, OT* __restrict__ out, int Nd, int n) {
+                                         int wm, int wn, int tid, OT* __restrict__ out, float* __restrict__ out_scale,
+                                         int Nd, int n) {
   constexpr int NC = PHASE_A ? P_TN / 2 : P_TN;  // output columns of the tile
   constexpr int LSTR = P_TN * 4;
   const int lcol = it.lane & 31;
@@ -194,18 +294,35 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
         v0 = make_float4(silu_f(v0.x) * u0.x, silu_f(v0.y) * u0.y, silu_f(v0.z) * u0.z, silu_f(v0.w) * u0.w);
         v1 = make_float4(silu_f(v1.x) * u1.x, silu_f(v1.y) * u1.y, silu_f(v1.z) * u1.z, silu_f(v1.w) * u1.w);
       }
-      OT* dst = out + (long long)(it.row0 + pass * 128 + r) * Nd + col0 + ch * 8;
-      store8(dst, v0, v1);
+      const long long orow = it.row0 + pass * 128 + r;
+      if constexpr (H_FP8) {
+        float amax = absmax8(v0, v1);
+#pragma unroll
+        for (int o = 1; o < CH; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));  // the row's 16 threads
+        const int k = pow2_scale_exp(amax);
+        const float inv = exp2_int(-k);
+        uint2 wv;
+        wv.x = f32_to_e4m3(v0.x * inv) | (f32_to_e4m3(v0.y * inv) << 8) | (f32_to_e4m3(v0.z * inv) << 16) |
+               (f32_to_e4m3(v0.w * inv) << 24);
+        wv.y = f32_to_e4m3(v1.x * inv) | (f32_to_e4m3(v1.y * inv) << 8) | (f32_to_e4m3(v1.z * inv) << 16) |
+               (f32_to_e4m3(v1.w * inv) << 24);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(out) + orow * Nd + col0 + ch * 8;
+        *reinterpret_cast<uint2*>(dst) = wv;
+        if (ch == 0) out_scale[orow * (Nd / 128) + n] = exp2_int(k);
+      } else {
+        store8(out + orow * Nd + col0 + ch * 8, v0, v1);
+      }
     }
   }
 }
 
 // One work item for a wave with MT live 32-row MFMA tiles: accumulators,
 // K loop (two-stage pipeline, unrolled by two so each step names its
-// buffers) and epilogue, all in one instantiation.
-template <bool PHASE_A, int MT, typename OT>
+// buffers and the loop has a single exit) and epilogue, all in one
+// instantiation.
+template <bool FP8, bool PHASE_A, int MT, typename OT>
 __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* st1, int wm, int wn, int tid,
-                                         OT* __restrict__ out, int Nd, int n) {
+                                         OT* __restrict__ out, float* __restrict__ out_scale, int Nd, int n) {
   constexpr int MA = MT > 0 ? MT : 1;
   f32x16_v acc[MA][4];
 #pragma unroll
@@ -214,39 +331,48 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  // nk is even (K is a multiple of 128): the loop has a single exit.
-  issue_stage(it, st0, 0);
+  issue_part<FP8, -1, 1>(it, st0, 0, 0u);
   for (int s = 0; s < it.nk; s += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    pipe_step<MT>(acc, it, st1, st0, true, (uint32_t)(s + 1) * P_TK * 2u);
+    pipe_step<FP8, MT>(acc, it, st1, st0, s, true, (uint32_t)(s + 1) * P_ROWB);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    pipe_step<MT>(acc, it, st0, st1, s + 2 < it.nk, (uint32_t)(s + 2) * P_TK * 2u);
+    pipe_step<FP8, MT>(acc, it, st0, st1, s + 1, s + 2 < it.nk, (uint32_t)(s + 2) * P_ROWB);
   }
-  epilogue<PHASE_A, MT, MA, OT>(acc, it, st0, st1, wm, wn, tid, out, Nd, n);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's zero loads land before LDS is reused
+  epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT>(acc, it, st0, st1, wm, wn, tid, out, out_scale, Nd, n);
 }
 
 // PHASE_A: x = tokens [T, Kd] gathered by row_token, w = W13 [E, 2*Nd, Kd],
 //          out = h [P, Nd] with SwiGLU; Nd = I, Kd = d.
 // !PHASE_A: x = h [P, Kd], w = W2 [E, Nd, Kd], out = y [P, Nd]; Nd = d, Kd = I.
-template <bool PHASE_A, typename OT>
-__global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w,
+// FP8: x, w are E4M3 codes; x_scale [rows of x, Kd/128] and
+//      w_scale [E, rows of w / 128, Kd/128] are power-of-two fp32 scales;
+//      phase A writes h as E4M3 codes with scales out_scale [P, Nd/128].
+template <bool FP8, bool PHASE_A, typename OT>
+__global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __restrict__ x,
+                                                            const uint8_t* __restrict__ w,
+                                                            const float* __restrict__ x_scale,
+                                                            const float* __restrict__ w_scale,
                                                             const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ tile_map,
                                                             const int32_t* __restrict__ n_tiles, int Kd, int Nd,
-                                                            int nt_total, uint32_t x_bytes,
-                                                            int* __restrict__ counters, OT* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[P_STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[P_STAGE];
+                                                            int nt_total, uint32_t x_bytes, uint32_t xs_bytes,
+                                                            int* __restrict__ counters, OT* __restrict__ out,
+                                                            float* __restrict__ out_scale) {
+  constexpr int EB = Fmt<FP8>::EB;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[Fmt<FP8>::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[Fmt<FP8>::STAGE];
   __shared__ int s_item;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int xcd = blockIdx.x & 7;
   const int ntx = (nt_total - xcd + 7) >> 3;  // N tiles owned by this XCD
   const long long total = (long long)(*n_tiles) * ntx;
-  const long long w_expert = (long long)(PHASE_A ? 2 : 1) * Nd * Kd;  // elements per expert
+  const int wrows = PHASE_A ? 2 * Nd : Nd;     // weight rows per expert
+  const long long w_expert = (long long)wrows * Kd * EB;  // bytes per expert
+  const int kblocks = Kd * EB / P_ROWB;        // K blocks (stages) of a row
 
   for (;;) {
     __syncthreads();  // previous item done with LDS and s_item
@@ -265,13 +391,13 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint16_t* __
     Item it;
     it.rows = tm.z;
     it.row0 = tm.y;
-    it.nk = Kd / P_TK;
+    it.nk = kblocks;
     it.lane = lane;
     it.lsw = (lane & 7) ^ ((lane >> 3) & 1);
     it.wave = __builtin_amdgcn_readfirstlane(wave);
-    it.a_groups = __builtin_amdgcn_readfirstlane((it.rows + 7) >> 3);
-    it.rb = make_rsrc(w + (long long)seg * w_expert, (uint32_t)(w_expert * 2));
+    it.rb = make_rsrc(w + seg * w_expert, (uint32_t)w_expert);
     it.ra = make_rsrc(x, x_bytes);
+    const uint32_t row_bytes = (uint32_t)Kd * EB;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = (wave * 8 + j) * 8 + (lane >> 3);
@@ -279,12 +405,28 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint16_t* __
       if (PHASE_A) {
         const int tok = r < it.rows ? row_token[it.row0 + r] : -1;
         // padding rows read past the end of the buffer, which yields zeros
-        it.a_off[j] = tok >= 0 ? (uint32_t)tok * (uint32_t)Kd * 2u + c16 : 0x80000000u;
+        it.a_off[j] = tok >= 0 ? (uint32_t)tok * row_bytes + c16 : 0x80000000u;
       } else {
-        it.a_off[j] = r < it.rows ? (uint32_t)(it.row0 + r) * (uint32_t)Kd * 2u + c16 : 0x80000000u;
+        it.a_off[j] = r < it.rows ? (uint32_t)(it.row0 + r) * row_bytes + c16 : 0x80000000u;
       }
       const int wrow = PHASE_A ? (r < 128 ? n * 128 + r : Nd + n * 128 + (r - 128)) : n * 256 + r;
-      it.b_off[j] = (uint32_t)wrow * (uint32_t)Kd * 2u + c16;
+      it.b_off[j] = (uint32_t)wrow * row_bytes + c16;
+    }
+    if constexpr (FP8) {
+      it.rs = make_rsrc(x_scale, xs_bytes);
+      const int r = wave * 64 + lane;  // scale row streamed by this lane
+      int srow = -1;
+      if (PHASE_A)
+        srow = r < it.rows ? row_token[it.row0 + r] : -1;
+      else
+        srow = r < it.rows ? it.row0 + r : -1;
+      it.s_off = srow >= 0 ? (uint32_t)srow * (uint32_t)kblocks * 4u : 0x80000000u;
+      // B-block scales of this wave's columns, one K block per lane (kblocks <= 64)
+      const float* ws = w_scale + (long long)seg * (wrows / 128) * kblocks;
+      const int blk0 = PHASE_A ? n : 2 * n + wn;
+      const int blk1 = PHASE_A ? Nd / 128 + n : blk0;
+      it.bsc0 = lane < kblocks ? ws[(long long)blk0 * kblocks + lane] : 1.0f;
+      it.bsc1 = lane < kblocks ? ws[(long long)blk1 * kblocks + lane] : 1.0f;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -294,11 +436,11 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint16_t* __
     int mt_live = (it.rows - it.mrow0 + 31) >> 5;  // 32-row MFMA tiles of this wave that hold rows
     mt_live = __builtin_amdgcn_readfirstlane(mt_live < 0 ? 0 : (mt_live > 4 ? 4 : mt_live));
     switch (mt_live) {
-      case 4: run_tile<PHASE_A, 4, OT>(it, st0, st1, wm, wn, tid, out, Nd, n); break;
-      case 3: run_tile<PHASE_A, 3, OT>(it, st0, st1, wm, wn, tid, out, Nd, n); break;
-      case 2: run_tile<PHASE_A, 2, OT>(it, st0, st1, wm, wn, tid, out, Nd, n); break;
-      case 1: run_tile<PHASE_A, 1, OT>(it, st0, st1, wm, wn, tid, out, Nd, n); break;
-      default: run_tile<PHASE_A, 0, OT>(it, st0, st1, wm, wn, tid, out, Nd, n); break;
+      case 4: run_tile<FP8, PHASE_A, 4, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
+      case 3: run_tile<FP8, PHASE_A, 3, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
+      case 2: run_tile<FP8, PHASE_A, 2, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
+      case 1: run_tile<FP8, PHASE_A, 1, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
+      default: run_tile<FP8, PHASE_A, 0, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
     }
   }
 }
@@ -323,6 +465,7 @@ int persistent_blocks() {
 }  // namespace
 
 bool ffn_bf16_persistent_ok(int d, int I) { return d % 256 == 0 && I % 128 == 0; }
+bool ffn_fp8_persistent_ok(int d, int I) { return d % 256 == 0 && I % 256 == 0 && d / 128 <= 64 && I / 128 <= 64; }
 
 // counters: 16 ints of device memory (8 per phase).
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
@@ -331,15 +474,44 @@ void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const ui
   const int nb = persistent_blocks();
   const uint32_t x_bytes = (uint32_t)((long long)T * d * 2);
   const uint32_t h_bytes = (uint32_t)(P * I * 2);
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(64), 0, st, counters, 16);
-  hipLaunchKernelGGL((k_ffn_persistent<true, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, x, w13, row_token,
-                     tile_map, n_tiles, d, I, I / 128, x_bytes, counters, h);
+  hipLaunchKernelGGL((k_ffn_persistent<false, true, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, xb,
+                     reinterpret_cast<const uint8_t*>(w13), nullptr, nullptr, row_token, tile_map, n_tiles, d, I,
+                     I / 128, x_bytes, 0u, counters, h, nullptr);
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   if (y_f32)
-    hipLaunchKernelGGL((k_ffn_persistent<false, float>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, row_token,
-                       tile_map, n_tiles, I, d, d / 256, h_bytes, counters + 8, static_cast<float*>(y));
+    hipLaunchKernelGGL((k_ffn_persistent<false, false, float>), dim3(nb), dim3(P_THREADS), 0, st, hb,
+                       reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
+                       d / 256, h_bytes, 0u, counters + 8, static_cast<float*>(y), nullptr);
   else
-    hipLaunchKernelGGL((k_ffn_persistent<false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, row_token,
-                       tile_map, n_tiles, I, d, d / 256, h_bytes, counters + 8, static_cast<uint16_t*>(y));
+    hipLaunchKernelGGL((k_ffn_persistent<false, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, hb,
+                       reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
+                       d / 256, h_bytes, 0u, counters + 8, static_cast<uint16_t*>(y), nullptr);
+}
+
+// E4M3 x E4M3: x codes [T, d] with x_scale [T, d/128]; W13 / W2 codes with
+// block scales; h (workspace) = codes [P, I] then scales [P, I/128].
+void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
+                               const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
+                               const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
+                               uint8_t* h, float* h_scale, void* y, bool y_f32, int* counters, hipStream_t st) {
+  const int nb = persistent_blocks();
+  const uint32_t x_bytes = (uint32_t)((long long)T * d);
+  const uint32_t xs_bytes = (uint32_t)((long long)T * (d / 128) * 4);
+  const uint32_t h_bytes = (uint32_t)(P * I);
+  const uint32_t hs_bytes = (uint32_t)(P * (I / 128) * 4);
+  hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(64), 0, st, counters, 16);
+  hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t>), dim3(nb), dim3(P_THREADS), 0, st, x, w13, x_scale,
+                     w13_scale, row_token, tile_map, n_tiles, d, I, I / 128, x_bytes, xs_bytes, counters, h, h_scale);
+  if (y_f32)
+    hipLaunchKernelGGL((k_ffn_persistent<true, false, float>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
+                       w2_scale, row_token, tile_map, n_tiles, I, d, d / 256, h_bytes, hs_bytes, counters + 8,
+                       static_cast<float*>(y), nullptr);
+  else
+    hipLaunchKernelGGL((k_ffn_persistent<true, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
+                       w2_scale, row_token, tile_map, n_tiles, I, d, d / 256, h_bytes, hs_bytes, counters + 8,
+                       static_cast<uint16_t*>(y), nullptr);
 }
 
 }  // namespace moe

@@ -6,7 +6,7 @@ import torch
 
 import sparse_expert_routing_sigmoid_amd as M
 import workloads as W
-from moe_testutil import f64_of, rel_l2
+from moe_testutil import f64_of, np_of, rel_l2
 from oracle import moe as O
 from test_gpu_permute import make_idx
 
@@ -95,3 +95,63 @@ def test_bf16_persistent_kernel_shapes(T, d, I, Ns, tile_m, ydt):
     cfg = W.CONFIGS["mid_bf16"].with_(T=T, d=d, I=I, Nr=12, Ns=Ns, K=3)
     idx = make_idx(T, cfg.Nr, cfg.K, T + d, hot=[4, 9])
     run_case(cfg, idx, tile_m=tile_m, y_dtype=ydt)
+
+
+# ------------------------------------------------------------ E4M3 x E4M3 --
+def oracle_fp8_weights(w13, w2):
+    """Each expert matrix through the oracle's 128x128 block quantiser, decoded."""
+    from oracle.e4m3 import dequantize_tiles, quantize_tiles
+    deq = lambda m: dequantize_tiles(*quantize_tiles(m, 128, 128), 128, 128)
+    a13, a2 = np_of(w13).astype(np.float32), np_of(w2).astype(np.float32)
+    return (np.stack([deq(a13[e]) for e in range(a13.shape[0])]),
+            np.stack([deq(a2[e]) for e in range(a2.shape[0])]))
+
+
+def run_fp8_case(cfg, idx, tile_m=32, y_dtype=torch.bfloat16, tol=3e-2):
+    """GPU: u and the weights quantised by fp8_quantize_tiles, both GEMMs on
+    E4M3 codes, h re-quantised in 1x128 tiles.  Oracle: the same
+    quantisation points on the oracle's own quantiser (R8), in fp64."""
+    u = W.make_tokens(cfg, 0, "cuda")
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    weights = M.quantize_weights(w13, w2)
+    xq = torch.empty((cfg.T, cfg.d), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((cfg.T, cfg.d // 128), dtype=torch.float32, device="cuda")
+    M.fp8_quantize_tiles(u, 1, xq, xs)
+    lay = O.permute_layout(idx.numpy(), cfg.Nr, cfg.Ns, tile_m, M.MOE_TILE_ROWS)
+    y = gpu_expert_rows(cfg, xq, xs, weights, lay, tile_m, y_dtype)
+    w13q, w2q = oracle_fp8_weights(w13, w2)
+    want = O.expert_rows(O.quantize_activations(f64_of(u)), w13q, w2q, lay, cfg.Nr, cfg.Ns, h_quant=True)
+    real = lay.row_token[: lay.seg_offset[-1]] >= 0
+    got = y[: lay.seg_offset[-1]][real]
+    assert np.all(np.isfinite(got))
+    err = rel_l2(got, want[real])
+    assert err <= tol, err
+    for s in range(cfg.E):
+        r0, r1 = lay.seg_offset[s], lay.seg_offset[s + 1]
+        m = lay.row_token[r0:r1] >= 0
+        if m.any():
+            assert rel_l2(y[r0:r1][m], want[r0:r1][m]) <= 2 * tol, s
+    return err
+
+
+@pytest.mark.parametrize("T,d,I,Nr,Ns,tile_m,ydt", [(300, 256, 256, 12, 1, 16, torch.bfloat16),
+                                                    (700, 512, 256, 12, 2, 32, torch.bfloat16),
+                                                    (700, 512, 512, 12, 1, 16, torch.float32),
+                                                    (1030, 768, 256, 12, 1, 1, torch.bfloat16),
+                                                    (600, 256, 256, 12, 1, 256, torch.bfloat16),
+                                                    (64, 2048, 1024, 12, 1, 32, torch.bfloat16),
+                                                    (40, 8192, 256, 4, 1, 64, torch.bfloat16)])
+def test_fp8_persistent_kernel_shapes(T, d, I, Nr, Ns, tile_m, ydt):
+    """E4M3 x E4M3 kernel: ragged segments, tiles of 1..256 rows, several
+    K blocks, both output types, and the largest supported d (64 K blocks)."""
+    cfg = W.CONFIGS["v3_prefill_fp8"].with_(T=T, d=d, I=I, Nr=Nr, Ns=Ns, K=3)
+    idx = make_idx(T, cfg.Nr, cfg.K, T + d + 1, hot=[2, Nr - 1])
+    err = run_fp8_case(cfg, idx, tile_m=tile_m, y_dtype=ydt)
+    assert err < 1e-2, err     # well inside the bound: both sides use the same codes
+
+
+def test_fp8_rejects_unsupported_shapes():
+    cfg = W.CONFIGS["v3_prefill_fp8"].with_(T=32, d=384, I=256, Nr=4, Ns=1, K=2)
+    idx = make_idx(cfg.T, cfg.Nr, cfg.K, 5)
+    with pytest.raises(M.MoeError, match="fp8 path needs"):
+        run_fp8_case(cfg, idx)

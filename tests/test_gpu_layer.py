@@ -85,3 +85,28 @@ def test_layer_deterministic():
     o1 = layer.forward(u, e, b).clone()
     o2 = layer.forward(u, e, b).clone()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_fp8_layer_forward():
+    """The E4M3 layer (activations in 1x128 tiles, weights in 128x128 blocks,
+    h re-quantised) on a reduced V3 FP8 prefill shape with Zipf-skewed routing,
+    against the oracle layer with the same quantisation points (R8)."""
+    from test_gpu_gemm import oracle_fp8_weights
+    cfg = W.CONFIGS["v3_prefill_fp8"].with_(T=768, d=512, Nr=16, Ns=1, I=256, K=4)
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, W.TORCH_DTYPE[cfg.act],
+                       M.quantize_weights(w13, w2), x_fp8=True, tile_m=32)
+    u = W.make_tokens(cfg, 0, "cuda")
+    e = W.make_centroids(cfg, "cuda")
+    b = W.make_bias(cfg, "cuda")
+    out = layer.forward(u, e, b)
+    torch.cuda.synchronize()
+    w13q, w2q = oracle_fp8_weights(w13, w2)
+    o = O.layer_forward(f64_of(u), f64_of(e), f64_of(b), w13q, w2q, cfg.Nr, cfg.Ns, cfg.K,
+                        x_quant=True, h_quant=True, gamma=cfg.gamma)
+    ok, _ = check_routing(np_of(layer.topk_idx), np_of(layer.topk_gate), np_of(layer.expert_load),
+                          o.routing, cfg.Nr)
+    got = f64_of(out)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got[ok], o.out[ok]) <= 3e-2
+    assert rel_l2(got[ok] - f64_of(u)[ok], (o.out - f64_of(u))[ok]) <= 3e-2
