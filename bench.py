@@ -43,7 +43,44 @@ def parse():
     p.add_argument("--tile-m", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target length of the oracle's timed CPU work (the sample is sized for it)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (calibrates HBM byte counters) and exit")
     return p.parse_args()
+
+
+# HBM traffic of one moe_expert_gemm call, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs of this script (summed over the call's kernels, scaled by the
+# factor the same counters give for a plain copy of known size).  Valid only
+# for the kernel sources they were taken on: a changed source gives null.
+TRAFFIC = {
+    "v3_prefill_bf16": {"fetch_bytes": 41088028953, "write_bytes": 1436277440, "digest": "f9f2bc343a2485b9"},
+    "v3_prefill_fp8": {"fetch_bytes": 28592649200, "write_bytes": 2564257088, "digest": "f9f2bc343a2485b9"},
+}
+
+
+def gemm_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm_mfma.hip", "gemm_bf16.hip", "common.h"):
+        with open(os.path.join(ROOT, "sparse_expert_routing_sigmoid_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of `mib` MiB, launched 3 times: the
+    reference for scaling FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}), flush=True)
 
 
 def main():
@@ -52,6 +89,9 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the layer is built and measured on one "
               "GPU; multi-GPU expert parallelism is not part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     import numpy as np
     import torch
 
@@ -132,8 +172,12 @@ def main():
         achieved = gemm_flops / (gemm_ms * 1e-3)
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": mfma_peak / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / mfma_peak}
-    roof["traffic"] = None
-    roof["kernel"] = "moe_expert_gemm (k_gateup + k_down)"
+    digest = gemm_source_digest()
+    tr = TRAFFIC.get(cfg.name)
+    roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) / 1e9 if tr and tr["digest"] == digest else None
+    roof["traffic_unit"] = "GB per launch"
+    roof["kernel_digest"] = digest
+    roof["kernel"] = "moe_expert_gemm call: k_zero_counters + k_ffn_persistent phase A (gate/up + SwiGLU) + phase B (down)"
     roof["units_per_launch"] = {"rows": rows, "flops": gemm_flops, "algorithmic_bytes": gemm_bytes}
     roof["avg_launch_ms"] = gemm_ms
 
@@ -163,14 +207,17 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, layer, us[0], e, bias0, weights, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, layer, us[0], e, bias0, weights, args.cpu_sample_tokens,
+                                           args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, layer, u, e, b, weights, sample_tokens):
-    """Time the fp64 oracle on the first S tokens of step 0: routing, the 8
+def cpu_baseline(cfg, layer, u, e, b, weights, sample_tokens, seconds):
+    """Time the fp64 oracle on the first S tokens of step 0: routing, the
     routed + shared SwiGLU experts of each sampled token, and the combine.
-    Weight conversion to fp64 is input preparation and is not timed."""
+    S is sized so that the FFN work takes about `seconds` at the host's fp64
+    matrix-product rate (measured here first); weight conversion to fp64 is
+    input preparation and is not timed."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -178,8 +225,15 @@ def cpu_baseline(cfg, layer, u, e, b, weights, sample_tokens):
     from oracle import e4m3 as OE
     from oracle import moe as O
 
-    S = sample_tokens or (16 if cfg.d >= 4096 else min(cfg.T, 512))
-    S = min(S, cfg.T)
+    if not sample_tokens:
+        a = np.ones((256, cfg.d))
+        w = np.ones((cfg.d, cfg.I))
+        t1 = time.perf_counter()
+        a @ w
+        rate = 2.0 * 256 * cfg.d * cfg.I / max(time.perf_counter() - t1, 1e-6)
+        per_token = 6.0 * cfg.d * cfg.I * (cfg.K + cfg.Ns)
+        sample_tokens = int(seconds * rate / per_token)
+    S = max(16, min(sample_tokens, cfg.T))
     f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
     u_s = f64(u[:S])
     e_h = f64(e)
