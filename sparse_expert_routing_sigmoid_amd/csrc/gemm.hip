@@ -19,6 +19,11 @@ void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uin
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                uint8_t* h, float* h_scale, void* y, bool y_f32, int* counters, hipStream_t st);
+bool ffn_w8a16_ok(int d, int I);
+void launch_ffn_w8a16(const uint16_t* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                      const float* w2_scale, const int32_t* row_token, const int32_t* tile_map,
+                      const int32_t* n_tiles, int tiles_max, int T, long long P, int d, int I, uint16_t* h, void* y,
+                      bool y_f32, hipStream_t st);
 void launch_ffn_f32(const float* x, const float* w13, const float* w2, const int32_t* row_token,
                     const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int d, int I, float* h, float* y,
                     hipStream_t st);
@@ -117,8 +122,18 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
                                 (long long)P, d, I, h_codes, h_scale, y, y_t == MOE_F32, ws_counters, st);
       break;
     }
+    case Path::W8A16:
+      MOE_REQUIRE(ffn_w8a16_ok(d, I), MOE_EUNSUPPORTED,
+                  "bf16 x E4M3 path needs d % 256 == 0, I % 256 == 0, d <= 8192 and I <= 8192");
+      MOE_REQUIRE((unsigned long long)T * d * 2 < (1ull << 31) && (unsigned long long)P * I * 2 < (1ull << 31) &&
+                      (unsigned long long)2 * I * d < (1ull << 31),
+                  MOE_EUNSUPPORTED, "bf16 x E4M3 path: operand larger than 2 GiB");
+      launch_ffn_w8a16(static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(w13), w13_scale,
+                       static_cast<const uint8_t*>(w2), w2_scale, row_token, tile_map, n_tiles, tiles_max, T,
+                       (long long)P, d, I, reinterpret_cast<uint16_t*>(ws_h), y, y_t == MOE_F32, st);
+      break;
     default:
-      MOE_REQUIRE(false, MOE_EUNSUPPORTED, "bf16 activations with E4M3 weights are not built yet");
+      MOE_REQUIRE(false, MOE_EUNSUPPORTED, "unsupported (x_t, w_t) combination");
   }
   return launch_status("moe_expert_gemm");
 }

@@ -155,3 +155,50 @@ def test_fp8_rejects_unsupported_shapes():
     idx = make_idx(cfg.T, cfg.Nr, cfg.K, 5)
     with pytest.raises(M.MoeError, match="fp8 path needs"):
         run_fp8_case(cfg, idx)
+
+
+# ------------------------------------------------ bf16 x E4M3 (decode path) --
+def run_w8_case(cfg, idx, tile_m=32, y_dtype=torch.bfloat16, tol=1e-2):
+    """GPU: bf16 rows, weights quantised by fp8_quantize_tiles (128x128
+    blocks), h kept in bf16.  Oracle: the same weights through its own
+    quantiser, decoded, fp64 products."""
+    u = W.make_tokens(cfg, 0, "cuda")
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    weights = M.quantize_weights(w13, w2)
+    lay = O.permute_layout(idx.numpy(), cfg.Nr, cfg.Ns, tile_m, M.MOE_TILE_ROWS)
+    y = gpu_expert_rows(cfg, u, None, weights, lay, tile_m, y_dtype)
+    w13q, w2q = oracle_fp8_weights(w13, w2)
+    want = O.expert_rows(f64_of(u), w13q, w2q, lay, cfg.Nr, cfg.Ns)
+    real = lay.row_token[: lay.seg_offset[-1]] >= 0
+    got = y[: lay.seg_offset[-1]][real]
+    assert np.all(np.isfinite(got))
+    err = rel_l2(got, want[real])
+    assert err <= tol, err
+    for s in range(cfg.E):
+        r0, r1 = lay.seg_offset[s], lay.seg_offset[s + 1]
+        m = lay.row_token[r0:r1] >= 0
+        if m.any():
+            assert rel_l2(y[r0:r1][m], want[r0:r1][m]) <= 2 * tol, s
+    return err
+
+
+@pytest.mark.parametrize("T,d,I,Nr,Ns,tile_m,ydt", [(128, 512, 256, 16, 1, 32, torch.bfloat16),
+                                                    (128, 512, 512, 16, 1, 16, torch.float32),
+                                                    (300, 256, 256, 12, 2, 1, torch.bfloat16),
+                                                    (600, 768, 256, 12, 1, 256, torch.bfloat16),
+                                                    (50, 2048, 1024, 24, 1, 32, torch.bfloat16),
+                                                    (20, 8192, 256, 4, 1, 64, torch.bfloat16)])
+def test_w8a16_decode_kernel_shapes(T, d, I, Nr, Ns, tile_m, ydt):
+    """bf16 activations x E4M3 weights: segments of 1 to several hundred rows
+    (16- and 32-row passes, several passes per tile), shared segments, both
+    output types, and d = 8192 (64 scale blocks along K)."""
+    cfg = W.CONFIGS["v3_decode_fp8w"].with_(T=T, d=d, I=I, Nr=Nr, Ns=Ns, K=3)
+    idx = make_idx(T, cfg.Nr, cfg.K, T + d + 2, hot=[1, Nr - 2])
+    err = run_w8_case(cfg, idx, tile_m=tile_m, y_dtype=ydt)
+    assert err < 5e-3, err
+
+
+def test_w8a16_rejects_unsupported_shapes():
+    cfg = W.CONFIGS["v3_decode_fp8w"].with_(T=16, d=384, I=256, Nr=4, Ns=1, K=2)
+    with pytest.raises(M.MoeError, match="bf16 x E4M3 path needs"):
+        run_w8_case(cfg, make_idx(cfg.T, cfg.Nr, cfg.K, 6))

@@ -110,3 +110,27 @@ def test_fp8_layer_forward():
     assert np.all(np.isfinite(got))
     assert rel_l2(got[ok], o.out[ok]) <= 3e-2
     assert rel_l2(got[ok] - f64_of(u)[ok], (o.out - f64_of(u))[ok]) <= 3e-2
+
+
+def test_w8a16_layer_forward():
+    """The decode layer (bf16 activations, E4M3 weights in 128x128 blocks) on
+    a reduced V3 decode shape with uniform routing, against the oracle layer
+    on the same decoded weights."""
+    from test_gpu_gemm import oracle_fp8_weights
+    cfg = W.CONFIGS["v3_decode_fp8w"].with_(T=128, d=512, Nr=32, Ns=1, I=256, K=4)
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, W.TORCH_DTYPE[cfg.act],
+                       M.quantize_weights(w13, w2), tile_m=32)
+    u = W.make_tokens(cfg, 0, "cuda")
+    e = W.make_centroids(cfg, "cuda")
+    b = W.make_bias(cfg, "cuda")
+    out = layer.forward(u, e, b)
+    torch.cuda.synchronize()
+    w13q, w2q = oracle_fp8_weights(w13, w2)
+    o = O.layer_forward(f64_of(u), f64_of(e), f64_of(b), w13q, w2q, cfg.Nr, cfg.Ns, cfg.K, gamma=cfg.gamma)
+    ok, _ = check_routing(np_of(layer.topk_idx), np_of(layer.topk_gate), np_of(layer.expert_load),
+                          o.routing, cfg.Nr)
+    got = f64_of(out)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got[ok], o.out[ok]) <= 1e-2
+    assert rel_l2(got[ok] - f64_of(u)[ok], (o.out - f64_of(u))[ok]) <= 1e-2
