@@ -8,16 +8,18 @@
 // bf16.  With a handful of rows per expert the work is bound by streaming the
 // weights from HBM once, so the kernel is built around that stream.
 //
-// Work item: (tile of the tile map, N tile).  Phase A: N tile = 64 h columns
-// = 64 gate rows + the 64 up rows of the same columns of W13.  Phase B: N
-// tile = 128 columns of y (rows of W2).  A block is two waves; each wave owns
-// four 16-row weight fragments (phase A: two gate + the two matching up
-// fragments) over the whole K and keeps them out of LDS: weight bytes go
-// global -> registers with 16-byte buffer loads, two K steps in flight, are
-// widened to bf16 with the block scale folded in by the scaled E4M3 -> bf16
-// conversion (exact: the scale is a power of two), and feed 16x16x32 bf16
-// MFMAs with fp32 accumulators.  The rows of the tile are taken 16 * MC at a
-// time (MC = 1 or 2); their activations come from L2.
+// Work item: (tile of the tile map, N tile).  Phase A: N tile = 128 h
+// columns = 128 gate rows + the 128 up rows of the same columns of W13.
+// Phase B: N tile = 256 columns of y (rows of W2).  A block is four waves;
+// each wave owns four 16-row weight fragments (phase A: two gate + the two
+// matching up fragments) over the whole K and keeps them out of LDS: weight
+// bytes go global -> registers with 16-byte buffer loads, two K steps in
+// flight, are widened to bf16 with the block scale folded in by the scaled
+// E4M3 -> bf16 conversion (exact: the scale is a power of two), and feed
+// 16x16x32 bf16 MFMAs with fp32 accumulators.  The rows of the tile are taken
+// 16 * MC at a time (MC = 1 or 2); their activations come from L2.
+// Scheduling barriers keep each step's loads together and in issue order,
+// so the wait before a step's MFMAs covers only that step's loads.
 //
 // K order inside a step.  One K step covers 128 values (one scale block).
 // Lane l holds column (or row) l % 16 and, with g = l / 16, the 16 K values
@@ -37,7 +39,7 @@ typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
 
-constexpr int W8_THREADS = 128;  // two waves
+constexpr int W8_THREADS = 256;  // four waves
 constexpr int W8_NB = 4;         // 16-row weight fragments per wave
 constexpr uint32_t W8_OOB = 0x80000000u;
 
@@ -143,16 +145,22 @@ __device__ __forceinline__ void w8_pass(const W8Lanes& L, const int32_t* __restr
 
   W8Step<MC> s0, s1;
   w8_load<MC>(s0, L, a_off, 0, nk);
+  __builtin_amdgcn_sched_barrier(0);
   w8_load<MC>(s1, L, a_off, 1, nk);
+  __builtin_amdgcn_sched_barrier(0);
   for (int k = 0; k < nk; k += 2) {  // nk is even
     const float lo0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lo), k));
     const float hi0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_hi), k));
     w8_mma<MC>(acc, s0, lo0, hi0);
+    __builtin_amdgcn_sched_barrier(0);
     w8_load<MC>(s0, L, a_off, k + 2, nk);
+    __builtin_amdgcn_sched_barrier(0);
     const float lo1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_lo), k + 1));
     const float hi1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_hi), k + 1));
     w8_mma<MC>(acc, s1, lo1, hi1);
+    __builtin_amdgcn_sched_barrier(0);
     w8_load<MC>(s1, L, a_off, k + 3, nk);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Accumulator element i of lane l: row 4 (l / 16) + i, column l % 16.
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(W8_THREADS) void k_ffn_w8a16(const uint16_t* __rest
                                                           const int32_t* __restrict__ tile_map,
                                                           const int32_t* __restrict__ n_tiles, int Kd, int Nd,
                                                           uint32_t x_bytes, OT* __restrict__ out) {
-  constexpr int NCOL = PHASE_A ? 64 : 128;  // output columns per item
+  constexpr int NCOL = PHASE_A ? 128 : 256;  // output columns per item
   const int NT = Nd / NCOL;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nk = Kd / 128;  // K steps = K blocks
@@ -210,21 +218,21 @@ __global__ __launch_bounds__(W8_THREADS) void k_ffn_w8a16(const uint16_t* __rest
     for (int f = 0; f < W8_NB; ++f) {
       int wrow;
       if (PHASE_A)
-        wrow = (f < 2 ? 0 : Nd) + n * 64 + wave * 32 + (f & 1) * 16;  // gate, gate, up, up
+        wrow = (f < 2 ? 0 : Nd) + n * 128 + wave * 32 + (f & 1) * 16;  // gate, gate, up, up
       else
-        wrow = n * 128 + wave * 64 + f * 16;
+        wrow = n * 256 + wave * 64 + f * 16;
       L.b_off[f] = (uint32_t)(wrow + L.c) * (uint32_t)Kd + (uint32_t)L.g * 16u;
     }
     if (PHASE_A) {
-      blk_lo = (n * 64) / 128;
-      blk_hi = Nd / 128 + blk_lo;
+      blk_lo = n;
+      blk_hi = Nd / 128 + n;
     } else {
-      blk_lo = blk_hi = n;
+      blk_lo = blk_hi = 2 * n + (wave >> 1);
     }
     const float* ws = w_scale + (long long)seg * (wrows / 128) * nk;
     const float sc_lo = lane < nk ? ws[(long long)blk_lo * nk + lane] : 1.0f;
     const float sc_hi = lane < nk ? ws[(long long)blk_hi * nk + lane] : 1.0f;
-    const int col0 = PHASE_A ? n * 64 + wave * 32 : n * 128 + wave * 64;
+    const int col0 = PHASE_A ? n * 128 + wave * 32 : n * 256 + wave * 64;
     const uint32_t x_row_bytes = (uint32_t)Kd * 2u;
     for (int m0 = 0; m0 < rows;) {
       if (rows - m0 > 16) {
@@ -263,9 +271,9 @@ void launch_ffn_w8a16(const uint16_t* x, const uint8_t* w13, const float* w13_sc
                       bool y_f32, hipStream_t st) {
   const uint32_t x_bytes = (uint32_t)((long long)T * d * 2);
   const uint32_t h_bytes = (uint32_t)(P * I * 2);
-  hipLaunchKernelGGL((k_ffn_w8a16<true, uint16_t>), dim3(w8_grid((long long)tiles_max * (I / 64))),
+  hipLaunchKernelGGL((k_ffn_w8a16<true, uint16_t>), dim3(w8_grid((long long)tiles_max * (I / 128))),
                      dim3(W8_THREADS), 0, st, x, w13, w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, h);
-  const int gB = w8_grid((long long)tiles_max * (d / 128));
+  const int gB = w8_grid((long long)tiles_max * (d / 256));
   if (y_f32)
     hipLaunchKernelGGL((k_ffn_w8a16<false, float>), dim3(gB), dim3(W8_THREADS), 0, st, h, w2, w2_scale, row_token,
                        tile_map, n_tiles, I, d, h_bytes, static_cast<float*>(y));
