@@ -55,15 +55,20 @@ def parse():
 # factor the same counters give for a plain copy of known size).  Valid only
 # for the kernel sources they were taken on: a changed source gives null.
 TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 41088028953, "write_bytes": 1436277440, "digest": "f9f2bc343a2485b9"},
-    "v3_prefill_fp8": {"fetch_bytes": 28592649200, "write_bytes": 2564257088, "digest": "f9f2bc343a2485b9"},
+    "v3_prefill_bf16": {"fetch_bytes": 41088028953, "write_bytes": 1436277440, "digest": "b13eea276c0abc14"},
+    "v3_prefill_fp8": {"fetch_bytes": 28592649200, "write_bytes": 2564257088, "digest": "b13eea276c0abc14"},
+    "v3_decode_fp8w": {"fetch_bytes": 11664038460, "write_bytes": 149726805, "digest": "e92e9d0673c199c6"},
 }
 
+# Source files of the kernels each workload's expert GEMM runs.
+GEMM_SOURCES = {"v3_decode_fp8w": ("gemm_w8.hip", "common.h")}
+DEFAULT_GEMM_SOURCES = ("gemm_mfma.hip", "common.h")
 
-def gemm_source_digest():
+
+def gemm_source_digest(workload):
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_mfma.hip", "gemm_bf16.hip", "common.h"):
+    for f in GEMM_SOURCES.get(workload, DEFAULT_GEMM_SOURCES):
         with open(os.path.join(ROOT, "sparse_expert_routing_sigmoid_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -166,18 +171,20 @@ def main():
         achieved = gemm_bytes / (gemm_ms * 1e-3)
         roof = {"bound": bound, "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": unit,
                 "frac": achieved / peak}
-        dtype = "bf16 x fp8-weights"
+        dtype = "bf16"   # E4M3 weights are widened exactly to bf16 for the MFMAs
     else:
         mfma_peak = PEAK["fp8" if cfg.x_fp8 else ("f32" if cfg.weights == "f32" else "bf16")]
         achieved = gemm_flops / (gemm_ms * 1e-3)
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": mfma_peak / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / mfma_peak}
-    digest = gemm_source_digest()
+    digest = gemm_source_digest(cfg.name)
     tr = TRAFFIC.get(cfg.name)
     roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) / 1e9 if tr and tr["digest"] == digest else None
     roof["traffic_unit"] = "GB per launch"
     roof["kernel_digest"] = digest
-    roof["kernel"] = "moe_expert_gemm call: k_zero_counters + k_ffn_persistent phase A (gate/up + SwiGLU) + phase B (down)"
+    roof["kernel"] = ("moe_expert_gemm call: k_ffn_w8a16 phase A (gate/up + SwiGLU) + phase B (down)"
+                      if cfg.weights == "e4m3" and not cfg.x_fp8 else
+                      "moe_expert_gemm call: k_zero_counters + k_ffn_persistent phase A (gate/up + SwiGLU) + phase B (down)")
     roof["units_per_launch"] = {"rows": rows, "flops": gemm_flops, "algorithmic_bytes": gemm_bytes}
     roof["avg_launch_ms"] = gemm_ms
 
