@@ -11,14 +11,17 @@ void launch_ffn_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
                      const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int d, int I, uint16_t* h,
                      void* y, bool y_f32, hipStream_t st);
 bool ffn_bf16_persistent_ok(int d, int I);
+size_t ffn_schedule_bytes(long long tiles_cap, int ntA, int ntB);
+int ffn_schedule_max_tiles();
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                                 const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
-                                uint16_t* h, void* y, bool y_f32, int* counters, hipStream_t st);
+                                int Nr, int cap, uint16_t* h, void* y, bool y_f32, int* sched, hipStream_t st);
 bool ffn_fp8_persistent_ok(int d, int I);
 void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
-                               uint8_t* h, float* h_scale, void* y, bool y_f32, int* counters, hipStream_t st);
+                               int Nr, int cap, uint8_t* h, float* h_scale, void* y, bool y_f32, int* sched,
+                               hipStream_t st);
 bool ffn_w8a16_ok(int d, int I);
 void launch_ffn_w8a16(const uint16_t* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
                       const float* w2_scale, const int32_t* row_token, const int32_t* tile_map,
@@ -54,12 +57,17 @@ size_t h_row_bytes(Path p, int I) {
 
 }  // namespace
 
+// Workspace: the work schedule of the persistent kernels (counters and item
+// lists), then h.
+size_t gemm_sched_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  return ffn_schedule_bytes((long long)permute_tiles_max(T, K, Nr, Ns, tile_m), (I + 127) / 128, (d + 255) / 256);
+}
+
 size_t gemm_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m, moe_dtype x_t, moe_dtype w_t) {
-  (void)d;
   const Path p = path_of(x_t, w_t);
-  if (p == Path::NONE || T < 0 || I < 1) return 0;
+  if (p == Path::NONE || T < 0 || I < 1 || d < 1) return 0;
   const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
-  return P * h_row_bytes(p, I) + 256;
+  return gemm_sched_bytes(T, K, Nr, Ns, d, I, tile_m) + P * h_row_bytes(p, I);
 }
 
 moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_dtype w_t, const void* w13,
@@ -86,9 +94,10 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
   const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
   hipStream_t st = as_stream(stream);
   if (T == 0) return MOE_OK;
-  // Workspace: 256 bytes of scheduling counters, then h.
-  int* ws_counters = static_cast<int*>(ws);
-  uint8_t* ws_h = static_cast<uint8_t*>(ws) + 256;
+  // Workspace: the work schedule, then h.
+  int* ws_sched = static_cast<int*>(ws);
+  uint8_t* ws_h = static_cast<uint8_t*>(ws) + gemm_sched_bytes(T, K, Nr, Ns, d, I, tile_m);
+  const bool sched_fits = tiles_max <= ffn_schedule_max_tiles();
   switch (p) {
     case Path::F32:
       MOE_REQUIRE(y_t == MOE_F32, MOE_EUNSUPPORTED, "fp32 path writes fp32 y");
@@ -98,11 +107,12 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
       break;
     case Path::BF16:
       MOE_REQUIRE(d % 128 == 0 && I % 64 == 0, MOE_EUNSUPPORTED, "bf16 path needs d % 128 == 0 and I % 64 == 0");
-      if (ffn_bf16_persistent_ok(d, I) && (unsigned long long)T * d * 2 < (1ull << 31) &&
+      if (ffn_bf16_persistent_ok(d, I) && sched_fits && (unsigned long long)T * d * 2 < (1ull << 31) &&
           (unsigned long long)P * I * 2 < (1ull << 31) && (unsigned long long)3 * I * d * 2 < (1ull << 31))
         launch_ffn_bf16_persistent(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
                                    static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, T, (long long)P, d,
-                                   I, reinterpret_cast<uint16_t*>(ws_h), y, y_t == MOE_F32, ws_counters, st);
+                                   I, Nr, tiles_max, reinterpret_cast<uint16_t*>(ws_h), y, y_t == MOE_F32, ws_sched,
+                                   st);
       else
         launch_ffn_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
                         static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, tiles_max, d, I,
@@ -114,12 +124,13 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
       MOE_REQUIRE((unsigned long long)T * d < (1ull << 31) && (unsigned long long)P * I < (1ull << 31) &&
                       (unsigned long long)3 * I * d < (1ull << 31),
                   MOE_EUNSUPPORTED, "fp8 path: operand larger than 2 GiB");
+      MOE_REQUIRE(sched_fits, MOE_EUNSUPPORTED, "fp8 path: more GEMM tiles than the work schedule holds");
       // h: E4M3 codes [P, I], then their 1x128 tile scales [P, I / 128].
       uint8_t* h_codes = ws_h;
       float* h_scale = reinterpret_cast<float*>(ws_h + P * (size_t)I);
       launch_ffn_fp8_persistent(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale,
                                 static_cast<const uint8_t*>(w2), w2_scale, row_token, tile_map, n_tiles, T,
-                                (long long)P, d, I, h_codes, h_scale, y, y_t == MOE_F32, ws_counters, st);
+                                (long long)P, d, I, Nr, tiles_max, h_codes, h_scale, y, y_t == MOE_F32, ws_sched, st);
       break;
     }
     case Path::W8A16:

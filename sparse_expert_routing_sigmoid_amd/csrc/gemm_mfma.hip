@@ -358,9 +358,12 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
                                                             const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ tile_map,
                                                             const int32_t* __restrict__ n_tiles, int Kd, int Nd,
-                                                            int nt_total, uint32_t x_bytes, uint32_t xs_bytes,
-                                                            int* __restrict__ counters, OT* __restrict__ out,
-                                                            float* __restrict__ out_scale) {
+                                                            uint32_t x_bytes, uint32_t xs_bytes,
+                                                            int* __restrict__ counters,
+                                                            const int* __restrict__ totals,
+                                                            const int* __restrict__ offsets,
+                                                            const int* __restrict__ items,
+                                                            OT* __restrict__ out, float* __restrict__ out_scale) {
   constexpr int EB = Fmt<FP8>::EB;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[Fmt<FP8>::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[Fmt<FP8>::STAGE];
@@ -368,20 +371,29 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int xcd = blockIdx.x & 7;
-  const int ntx = (nt_total - xcd + 7) >> 3;  // N tiles owned by this XCD
-  const long long total = (long long)(*n_tiles) * ntx;
   const int wrows = PHASE_A ? 2 * Nd : Nd;     // weight rows per expert
   const long long w_expert = (long long)wrows * Kd * EB;  // bytes per expert
   const int kblocks = Kd * EB / P_ROWB;        // K blocks (stages) of a row
 
   for (;;) {
     __syncthreads();  // previous item done with LDS and s_item
-    if (tid == 0) s_item = atomicAdd(&counters[xcd], 1);
+    if (tid == 0) {
+      // this XCD's list first; when it is drained, help the other XCDs
+      int got = -1;
+      for (int k = 0; k < 8 && got < 0; ++k) {
+        const int y = (xcd + k) & 7;
+        const int tot = totals[y];
+        if (__atomic_load_n(&counters[y], __ATOMIC_RELAXED) >= tot) continue;
+        const int i = atomicAdd(&counters[y], 1);
+        if (i < tot) got = items[offsets[y] + i];
+      }
+      s_item = got;
+    }
     __syncthreads();
-    const long long item = s_item;
-    if (item >= total) break;
-    const int tile = (int)(item / ntx);
-    const int n = (int)(item % ntx) * 8 + xcd;
+    const int entry = s_item;
+    if (entry < 0) break;
+    const int tile = entry >> 8;
+    const int n = entry & 255;
     const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * tile);
     const int seg = tm.x;
 
@@ -445,8 +457,123 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
   }
 }
 
-__global__ void k_zero_counters(int* c, int n) {
-  if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+// Work lists of the two GEMM phases (one block of 1024 threads).
+//
+// A unit is a routed expert (all its tiles) or one tile of a shared expert.
+// Units are dealt to the 8 XCDs largest first, each to the least loaded XCD
+// (by rows), so an expert's weights and its row tiles meet in one L2 while
+// the work stays balanced; the big shared segments spread over all XCDs.
+// Within a unit the items run N-tile major (all row tiles of the unit for N
+// tile 0, then 1, ...), so concurrent blocks of an XCD share weight slabs.
+// An item is (tile << 8) | N tile.
+//
+// sched: [0, 16) work counters (phase A 0..7, B 8..15), [16, 24) / [24, 32)
+// items per XCD, [32, 40) / [40, 48) first item of each XCD, then the item
+// lists of phase A (cap * ntA) and B (cap * ntB).
+constexpr int SCHED_HDR = 64;
+constexpr int SCHED_MAXU = 4096;
+
+__global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict__ tile_map,
+                                                       const int32_t* __restrict__ n_tiles, int Nr, int ntA,
+                                                       int ntB, int cap, int* __restrict__ sched) {
+  __shared__ int s_seg[SCHED_MAXU];
+  __shared__ int s_ustart[SCHED_MAXU + 1], s_urows[SCHED_MAXU], s_order[SCHED_MAXU];
+  __shared__ int s_uoffA[SCHED_MAXU], s_uoffB[SCHED_MAXU];
+  __shared__ unsigned char s_uxcd[SCHED_MAXU];
+  __shared__ int s_part[1024];
+  __shared__ int s_nu, s_xA[8], s_xB[8];
+  const int tid = threadIdx.x;
+  const int tiles = min(*n_tiles, min(cap, SCHED_MAXU));
+  if (tid < 16) sched[tid] = 0;
+  for (int t = tid; t < tiles; t += 1024) s_seg[t] = tile_map[4LL * t];
+  __syncthreads();
+  // unit starts, numbered by a scan (4 tiles per thread)
+  int flags[4], cnt = 0;
+  for (int j = 0; j < 4; ++j) {
+    const int t = tid * 4 + j;
+    flags[j] = t < tiles && (t == 0 || s_seg[t] != s_seg[t - 1] || s_seg[t] >= Nr);
+    cnt += flags[j];
+  }
+  s_part[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int u = s_part[tid] - cnt - 1;
+  for (int j = 0; j < 4; ++j) {
+    const int t = tid * 4 + j;
+    if (t < tiles) {
+      u += flags[j];
+      if (flags[j]) s_ustart[u] = t;
+    }
+  }
+  if (tid == 1023) s_nu = s_part[1023];
+  __syncthreads();
+  const int nu = s_nu;
+  if (tid == 0) s_ustart[nu] = tiles;
+  __syncthreads();
+  for (int v = tid; v < nu; v += 1024) {
+    int rows = 0;
+    for (int t = s_ustart[v]; t < s_ustart[v + 1]; ++t) rows += tile_map[4LL * t + 2];
+    s_urows[v] = rows;
+  }
+  __syncthreads();
+  // largest units first (ties: lower index first); plain rank by counting
+  for (int v = tid; v < nu; v += 1024) {
+    int rank = 0;
+    if (nu <= 1024) {
+      const int rv = s_urows[v];
+      for (int w = 0; w < nu; ++w) rank += (s_urows[w] > rv) || (s_urows[w] == rv && w < v);
+    } else {
+      rank = v;  // many units: keep tile-map order
+    }
+    s_order[rank] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long long load[8];
+    int nA[8], nB[8];
+    for (int x = 0; x < 8; ++x) load[x] = 0, nA[x] = 0, nB[x] = 0;
+    for (int r = 0; r < nu; ++r) {
+      const int v = s_order[r];
+      int best = 0;
+      for (int x = 1; x < 8; ++x)
+        if (load[x] < load[best]) best = x;
+      const int len = s_ustart[v + 1] - s_ustart[v];
+      load[best] += s_urows[v] > 0 ? s_urows[v] : 1;
+      s_uxcd[v] = (unsigned char)best;
+      s_uoffA[v] = nA[best];
+      s_uoffB[v] = nB[best];
+      nA[best] += len * ntA;
+      nB[best] += len * ntB;
+    }
+    int oa = 0, ob = 0;
+    for (int x = 0; x < 8; ++x) {
+      sched[16 + x] = nA[x];
+      sched[24 + x] = nB[x];
+      sched[32 + x] = oa;
+      sched[40 + x] = ob;
+      s_xA[x] = oa;
+      s_xB[x] = ob;
+      oa += nA[x];
+      ob += nB[x];
+    }
+  }
+  __syncthreads();
+  int* listA = sched + SCHED_HDR;
+  int* listB = listA + (long long)cap * ntA;
+  for (int v = tid; v < nu; v += 1024) {
+    const int t0 = s_ustart[v], len = s_ustart[v + 1] - t0, x = s_uxcd[v];
+    int* la = listA + s_xA[x] + s_uoffA[v];
+    for (int n = 0; n < ntA; ++n)
+      for (int j = 0; j < len; ++j) la[n * len + j] = ((t0 + j) << 8) | n;
+    int* lb = listB + s_xB[x] + s_uoffB[v];
+    for (int n = 0; n < ntB; ++n)
+      for (int j = 0; j < len; ++j) lb[n * len + j] = ((t0 + j) << 8) | n;
+  }
 }
 
 int persistent_blocks() {
@@ -464,30 +591,59 @@ int persistent_blocks() {
 
 }  // namespace
 
-bool ffn_bf16_persistent_ok(int d, int I) { return d % 256 == 0 && I % 128 == 0; }
+bool ffn_bf16_persistent_ok(int d, int I) { return d % 256 == 0 && I % 128 == 0 && I / 128 <= 255 && d / 256 <= 255; }
 bool ffn_fp8_persistent_ok(int d, int I) { return d % 256 == 0 && I % 256 == 0 && d / 128 <= 64 && I / 128 <= 64; }
 
-// counters: 16 ints of device memory (8 per phase).
+size_t ffn_schedule_bytes(long long tiles_cap, int ntA, int ntB) {
+  const size_t b = 4 * ((size_t)SCHED_HDR + (size_t)tiles_cap * (ntA + ntB));
+  return (b + 255) / 256 * 256;
+}
+int ffn_schedule_max_tiles() { return SCHED_MAXU; }
+
+namespace {
+
+struct PhaseSched {
+  int* cnt;
+  const int* tot;
+  const int* off;
+  const int* items;
+};
+
+PhaseSched phase_sched(int* sched, int phase, int cap, int ntA) {
+  PhaseSched p;
+  p.cnt = sched + 8 * phase;
+  p.tot = sched + 16 + 8 * phase;
+  p.off = sched + 32 + 8 * phase;
+  p.items = sched + SCHED_HDR + (phase ? (long long)cap * ntA : 0);
+  return p;
+}
+
+}  // namespace
+
+// sched: ffn_schedule_bytes(cap, I / 128, d / 256) bytes of device memory;
+// cap >= the tile count (at most ffn_schedule_max_tiles()).
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                                 const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
-                                uint16_t* h, void* y, bool y_f32, int* counters, hipStream_t st) {
+                                int Nr, int cap, uint16_t* h, void* y, bool y_f32, int* sched, hipStream_t st) {
   const int nb = persistent_blocks();
   const uint32_t x_bytes = (uint32_t)((long long)T * d * 2);
   const uint32_t h_bytes = (uint32_t)(P * I * 2);
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
-  hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(64), 0, st, counters, 16);
+  const int ntA = I / 128, ntB = d / 256;
+  hipLaunchKernelGGL(k_ffn_schedule, dim3(1), dim3(1024), 0, st, tile_map, n_tiles, Nr, ntA, ntB, cap, sched);
+  const PhaseSched a = phase_sched(sched, 0, cap, ntA), b = phase_sched(sched, 1, cap, ntA);
   hipLaunchKernelGGL((k_ffn_persistent<false, true, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, xb,
                      reinterpret_cast<const uint8_t*>(w13), nullptr, nullptr, row_token, tile_map, n_tiles, d, I,
-                     I / 128, x_bytes, 0u, counters, h, nullptr);
+                     x_bytes, 0u, a.cnt, a.tot, a.off, a.items, h, nullptr);
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<false, false, float>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
-                       d / 256, h_bytes, 0u, counters + 8, static_cast<float*>(y), nullptr);
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<false, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
-                       d / 256, h_bytes, 0u, counters + 8, static_cast<uint16_t*>(y), nullptr);
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<uint16_t*>(y), nullptr);
 }
 
 // E4M3 x E4M3: x codes [T, d] with x_scale [T, d/128]; W13 / W2 codes with
@@ -495,22 +651,26 @@ void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const ui
 void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
-                               uint8_t* h, float* h_scale, void* y, bool y_f32, int* counters, hipStream_t st) {
+                               int Nr, int cap, uint8_t* h, float* h_scale, void* y, bool y_f32, int* sched,
+                               hipStream_t st) {
   const int nb = persistent_blocks();
   const uint32_t x_bytes = (uint32_t)((long long)T * d);
   const uint32_t xs_bytes = (uint32_t)((long long)T * (d / 128) * 4);
   const uint32_t h_bytes = (uint32_t)(P * I);
   const uint32_t hs_bytes = (uint32_t)(P * (I / 128) * 4);
-  hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(64), 0, st, counters, 16);
+  const int ntA = I / 128, ntB = d / 256;
+  hipLaunchKernelGGL(k_ffn_schedule, dim3(1), dim3(1024), 0, st, tile_map, n_tiles, Nr, ntA, ntB, cap, sched);
+  const PhaseSched a = phase_sched(sched, 0, cap, ntA), b = phase_sched(sched, 1, cap, ntA);
   hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t>), dim3(nb), dim3(P_THREADS), 0, st, x, w13, x_scale,
-                     w13_scale, row_token, tile_map, n_tiles, d, I, I / 128, x_bytes, xs_bytes, counters, h, h_scale);
+                     w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, xs_bytes, a.cnt, a.tot, a.off, a.items,
+                     h, h_scale);
   if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<true, false, float>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
-                       w2_scale, row_token, tile_map, n_tiles, I, d, d / 256, h_bytes, hs_bytes, counters + 8,
+                       w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
                        static_cast<float*>(y), nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<true, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
-                       w2_scale, row_token, tile_map, n_tiles, I, d, d / 256, h_bytes, hs_bytes, counters + 8,
+                       w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
                        static_cast<uint16_t*>(y), nullptr);
 }
 
