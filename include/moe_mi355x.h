@@ -125,7 +125,8 @@ moe_status moe_route(const void* u, moe_dtype u_t, const float* centroids, const
  *   inv_row    device [T, K] int32 out: row that holds (t, k)
  *   tile_map   device [tiles_max, 4] int32 out: in segment order, each
  *              segment cut into tiles of MOE_TILE_ROWS rows (the last one
- *              shorter): {segment, first row, rows, 0}
+ *              shorter): {segment, first row, rows, token rows}; the token
+ *              rows of a tile come first, its padding rows after them
  *   n_tiles    device [1] int32 out: entries of tile_map in use
  *   P_max = moe_permute_rows(...), tiles_max = moe_permute_tiles_max(...)
  *   Errors: MOE_EINVAL for NULL pointers, bad sizes or tile_m;
@@ -144,8 +145,8 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, in
  * FFN^(s)_j and FFN^(r)_i of the [RG-MoE] combine equation; the pages do not
  * print the FFN form, this library uses SwiGLU:
  *   FFN(x) = W2 (SiLU(W_gate x) * (W_up x)),  SiLU(a) = a * sigmoid(a).
- * y[row] = FFN_{segment(row)}(x[row_token[row]]) for every row of every
- * tile (padding rows produce zeros or finite garbage that is never read).
+ * y[row] = FFN_{segment(row)}(x[row_token[row]]) for every token row of
+ * every tile; padding rows of y (and of h in ws) may be left unwritten.
  *
  *   x, x_t      device [T, d]: MOE_F32, MOE_BF16, or MOE_E4M3 codes
  *   x_scale     device [T, d/128] fp32 for x_t == MOE_E4M3 (1x128 tiles,

@@ -225,7 +225,7 @@ class Layout:
     seg_offset: np.ndarray   # [N_r+N_s+1] int32, first padded row of each segment
     row_token: np.ndarray    # [P_max] int32, token of each row, -1 for padding
     inv_row: np.ndarray      # [T, K] int32, row holding (t, k)
-    tile_map: np.ndarray     # [n_tiles, 4] int32: segment, first row, rows, 0
+    tile_map: np.ndarray     # [n_tiles, 4] int32: segment, first row, rows, token rows
     n_tiles: int
 
 
@@ -265,7 +265,7 @@ def permute_layout(idx: np.ndarray, Nr: int, Ns: int, tile_m: int, tile_rows: in
             inv_row[t_sel, k_sel] = pos + np.arange(n)
         padded = -(-n // tile_m) * tile_m
         for r0 in range(0, padded, tile_rows):
-            tiles.append((seg, pos + r0, min(tile_rows, padded - r0), 0))
+            tiles.append((seg, pos + r0, min(tile_rows, padded - r0), max(0, min(tile_rows, n - r0))))
         pos += padded
     seg_offset[Nr + Ns] = pos
     tile_map = np.array(tiles, dtype=np.int32).reshape(-1, 4)

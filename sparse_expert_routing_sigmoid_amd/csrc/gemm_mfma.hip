@@ -401,7 +401,7 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
     // 8 * (8 * wave + j) .. + 7 (lane l: row l / 8, physical chunk l & 7); the
     // lane fetches logical chunk c with physical = c ^ (row & 7) ^ ((row >> 3) & 1).
     Item it;
-    it.rows = tm.z;
+    it.rows = tm.w;  // token rows; the tile's padding rows are skipped
     it.row0 = tm.y;
     it.nk = kblocks;
     it.lane = lane;
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
   __syncthreads();
   for (int v = tid; v < nu; v += 1024) {
     int rows = 0;
-    for (int t = s_ustart[v]; t < s_ustart[v + 1]; ++t) rows += tile_map[4LL * t + 2];
+    for (int t = s_ustart[v]; t < s_ustart[v + 1]; ++t) rows += tile_map[4LL * t + 3];
     s_urows[v] = rows;
   }
   __syncthreads();

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(W8_THREADS) void k_ffn_w8a16(const uint16_t* __rest
     const int tile = tiles - 1 - (int)(item / NT);
     const int n = (int)(item % NT);
     const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * tile);
-    const int seg = tm.x, row0 = tm.y, rows = tm.z;
+    const int seg = tm.x, row0 = tm.y, rows = tm.w;  // token rows only
 
     W8Lanes L;
     L.lane = lane;

@@ -83,7 +83,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts
       m[0] = e;
       m[1] = row0 + j * MOE_TILE_ROWS;
       m[2] = rows;
-      m[3] = 0;
+      const int real = load - j * MOE_TILE_ROWS;  // token rows come first, padding last
+      m[3] = real < 0 ? 0 : (real > rows ? rows : real);
     }
   }
   if (e == E - 1) {

@@ -166,7 +166,7 @@ def test_layout_matches_python_construction(tile_m, tile_rows):
         r0 = start
         while r0 < len(rows):
             n = min(tile_rows, len(rows) - r0)
-            tiles.append([seg, r0, n, 0])
+            tiles.append([seg, r0, n, sum(1 for r in rows[r0:r0 + n] if r >= 0)])   # token rows of the tile
             r0 += n
     offs.append(len(rows))
     assert lay.seg_offset.tolist() == offs
