@@ -50,9 +50,45 @@ struct Vec8<float> {
   }
 };
 
-constexpr int CB_THREADS = 256;
-constexpr int CB_COLS = CB_THREADS * 8;
+// Raw 8-element vectors, kept as loaded until they are added (bf16 rows take
+// 4 registers instead of 8).
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  uint4 q;
+  __device__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ void get(float (&v)[8]) const {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ void get(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
 
+constexpr int CB_THREADS = 128;
+constexpr int CB_COLS = CB_THREADS * 8;  // 1024 columns per block: d = 7168 is 7 blocks
+constexpr int CB_SHARED = 2;              // shared rows gathered up front (more are added one by one)
+
+// One block per (token, 1024 columns); a thread holds 8 columns.  The rows
+// of the token are loaded before they are added, so their latencies
+// overlap; the sum is formed in the fixed order u, shared rows, routed rows
+// k = 0..K-1 (fp32, one rounding at the end), which keeps the result
+// independent of the launch shape.
 template <typename UT, typename YT, typename OT>
 __global__ __launch_bounds__(CB_THREADS) void k_combine(const UT* __restrict__ u, const YT* __restrict__ y,
                                                         const int32_t* __restrict__ inv_row,
@@ -62,30 +98,48 @@ __global__ __launch_bounds__(CB_THREADS) void k_combine(const UT* __restrict__ u
   const int t = blockIdx.x;
   const int c = blockIdx.y * CB_COLS + threadIdx.x * 8;
   if (c >= d) return;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float v[8];
-  if (!(flags & MOE_COMBINE_NO_RESIDUAL)) {
-    Vec8<UT>::load(u + (long long)t * d + c, v);
+  const bool res = !(flags & MOE_COMBINE_NO_RESIDUAL), sh = !(flags & MOE_COMBINE_NO_SHARED),
+             ro = !(flags & MOE_COMBINE_NO_ROUTED);
+  Raw8<UT> vu;
+  Raw8<YT> vs[CB_SHARED], vr[MOE_MAX_K];
+  float g[MOE_MAX_K];
+  if (res) vu.load(u + (long long)t * d + c);
+#pragma unroll
+  for (int j = 0; j < CB_SHARED; ++j)
+    if (sh && j < Ns) vs[j].load(y + ((long long)seg_offset[Nr + j] + t) * d + c);
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_K; ++k)
+    if (ro && k < K) {
+      g[k] = gate[(long long)t * K + k];
+      vr[k].load(y + (long long)inv_row[(long long)t * K + k] * d + c);
+    }
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, v[8];
+  if (res) {
+    vu.get(v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
-  if (!(flags & MOE_COMBINE_NO_SHARED)) {
-    for (int j = 0; j < Ns; ++j) {
-      const long long row = (long long)seg_offset[Nr + j] + t;
-      Vec8<YT>::load(y + row * d + c, v);
+  if (sh) {
+#pragma unroll
+    for (int j = 0; j < CB_SHARED; ++j)
+      if (j < Ns) {
+        vs[j].get(v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
+    for (int j = CB_SHARED; j < Ns; ++j) {
+      Vec8<YT>::load(y + ((long long)seg_offset[Nr + j] + t) * d + c, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
   }
-  if (!(flags & MOE_COMBINE_NO_ROUTED)) {
-    for (int k = 0; k < K; ++k) {
-      const long long row = inv_row[(long long)t * K + k];
-      const float g = gate[(long long)t * K + k];
-      Vec8<YT>::load(y + row * d + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+  for (int k = 0; k < MOE_MAX_K; ++k)
+    if (ro && k < K) {
+      vr[k].get(v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[k], v[i], acc[i]);
     }
-  }
   Vec8<OT>::store(out + (long long)t * d + c, acc);
 }
 

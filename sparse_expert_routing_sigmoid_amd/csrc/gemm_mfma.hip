@@ -460,9 +460,9 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
 // Work lists of the two GEMM phases (one block of 1024 threads).
 //
 // A unit is a routed expert (all its tiles) or one tile of a shared expert.
-// Units are dealt to the 8 XCDs largest first, each to the least loaded XCD
-// (by rows), so an expert's weights and its row tiles meet in one L2 while
-// the work stays balanced; the big shared segments spread over all XCDs.
+// Units are dealt to the 8 XCDs largest first in snake order, so an expert's
+// weights and its row tiles meet in one L2 while the work stays balanced;
+// the big shared segments spread over all XCDs.
 // Within a unit the items run N-tile major (all row tiles of the unit for N
 // tile 0, then 1, ...), so concurrent blocks of an XCD share weight slabs.
 // An item is (tile << 8) | N tile.
@@ -533,33 +533,39 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
     s_order[rank] = v;
   }
   __syncthreads();
-  if (tid == 0) {
-    long long load[8];
-    int nA[8], nB[8];
-    for (int x = 0; x < 8; ++x) load[x] = 0, nA[x] = 0, nB[x] = 0;
-    for (int r = 0; r < nu; ++r) {
+  // Deal the units in rank order in snake rounds (0..7, 7..0, ...), each
+  // round's largest to the XCD that got the smallest of the last round.  Then
+  // one thread per XCD walks its units to place their items.
+  if (tid < 8) {
+    const int x = tid;
+    int nA = 0, nB = 0;
+    for (int i = 0;; ++i) {
+      const int r = 8 * i + ((i & 1) ? 7 - x : x);
+      if (r >= nu) break;
       const int v = s_order[r];
-      int best = 0;
-      for (int x = 1; x < 8; ++x)
-        if (load[x] < load[best]) best = x;
       const int len = s_ustart[v + 1] - s_ustart[v];
-      load[best] += s_urows[v] > 0 ? s_urows[v] : 1;
-      s_uxcd[v] = (unsigned char)best;
-      s_uoffA[v] = nA[best];
-      s_uoffB[v] = nB[best];
-      nA[best] += len * ntA;
-      nB[best] += len * ntB;
+      s_uxcd[v] = (unsigned char)x;
+      s_uoffA[v] = nA;
+      s_uoffB[v] = nB;
+      nA += len * ntA;
+      nB += len * ntB;
     }
+    s_xA[x] = nA;
+    s_xB[x] = nB;
+  }
+  __syncthreads();
+  if (tid == 0) {
     int oa = 0, ob = 0;
     for (int x = 0; x < 8; ++x) {
-      sched[16 + x] = nA[x];
-      sched[24 + x] = nB[x];
+      const int na = s_xA[x], nb = s_xB[x];
+      sched[16 + x] = na;
+      sched[24 + x] = nb;
       sched[32 + x] = oa;
       sched[40 + x] = ob;
       s_xA[x] = oa;
       s_xB[x] = ob;
-      oa += nA[x];
-      ob += nB[x];
+      oa += na;
+      ob += nb;
     }
   }
   __syncthreads();

@@ -216,7 +216,7 @@ int router_ksplit(int T, int d, int Nr) {
   if (Nr > RM_TE || d % RM_BK != 0) return 0;
   const int tiles = (T + RM_TT - 1) / RM_TT;
   int ks = 1;
-  while (ks < 8 && tiles * ks < 512 && d % (RM_BK * ks * 2) == 0) ks *= 2;
+  while (ks < 32 && tiles * ks < 512 && d % (RM_BK * ks * 2) == 0) ks *= 2;
   return ks;
 }
 
@@ -225,16 +225,22 @@ __global__ void k_zero_i32(int32_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// EPL = experts per lane (Nr <= 64 * EPL).
+// EPL = experts per lane (Nr <= 64 * EPL).  One wave per token; each wave
+// takes tpw consecutive tokens.  Loads are counted in an LDS histogram and
+// added to expert_load once per block, which keeps the global atomics on a
+// popular expert few.
 template <int EPL>
 __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ z, int nparts,
-                                                      const float* __restrict__ bias, int T, int Nr, int K,
+                                                      const float* __restrict__ bias, int T, int Nr, int K, int tpw,
                                                       int32_t* __restrict__ topk_idx,
                                                       float* __restrict__ topk_gate, float* __restrict__ topk_score,
                                                       int32_t* __restrict__ load) {
+  __shared__ int s_hist[64 * EPL];
+  for (int i = threadIdx.x; i < Nr; i += blockDim.x) s_hist[i] = 0;
+  __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int t_first = (blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)) * tpw;
+  for (int t = t_first; t < t_first + tpw && t < T; ++t) {
   float s[EPL];
   unsigned long long key[EPL];
 #pragma unroll
@@ -287,17 +293,23 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
     topk_idx[o] = my_idx;
     topk_gate[o] = my_s / sum;
     if (topk_score) topk_score[o] = my_s;
-    atomicAdd(&load[my_idx], 1);
+    atomicAdd(&s_hist[my_idx], 1);
   }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < Nr; i += blockDim.x)
+    if (s_hist[i]) atomicAdd(&load[i], s_hist[i]);
 }
 
 template <int EPL>
 void launch_select(const float* z, int nparts, const float* bias, int T, int Nr, int K, int32_t* idx, float* gate,
                    float* score, int32_t* load, hipStream_t st) {
   const int waves_per_block = 4;
-  dim3 grid((T + waves_per_block - 1) / waves_per_block);
-  hipLaunchKernelGGL(k_route_select<EPL>, grid, dim3(64 * waves_per_block), 0, st, z, nparts, bias, T, Nr, K, idx,
-                     gate, score, load);
+  const int tpw = T >= 16384 ? 8 : (T >= 4096 ? 4 : 1);  // tokens per wave
+  const int per_block = waves_per_block * tpw;
+  dim3 grid((T + per_block - 1) / per_block);
+  hipLaunchKernelGGL(k_route_select<EPL>, grid, dim3(64 * waves_per_block), 0, st, z, nparts, bias, T, Nr, K, tpw,
+                     idx, gate, score, load);
 }
 
 }  // namespace
