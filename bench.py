@@ -55,9 +55,9 @@ def parse():
 # factor the same counters give for a plain copy of known size).  Valid only
 # for the kernel sources they were taken on: a changed source gives null.
 TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 41088028953, "write_bytes": 1436277440, "digest": "b13eea276c0abc14"},
-    "v3_prefill_fp8": {"fetch_bytes": 28592649200, "write_bytes": 2564257088, "digest": "b13eea276c0abc14"},
-    "v3_decode_fp8w": {"fetch_bytes": 11664038460, "write_bytes": 149726805, "digest": "e92e9d0673c199c6"},
+    "v3_prefill_bf16": {"fetch_bytes": 36806709582, "write_bytes": 1359584235, "digest": "e008e27dc175fce9"},
+    "v3_prefill_fp8": {"fetch_bytes": 29990197370, "write_bytes": 2471242517, "digest": "e008e27dc175fce9"},
+    "v3_decode_fp8w": {"fetch_bytes": 11327980887, "write_bytes": 21379744, "digest": "16efb1431ec91602"},
 }
 
 # Source files of the kernels each workload's expert GEMM runs.
