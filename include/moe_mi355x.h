@@ -170,6 +170,7 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, in
  * matrix instructions apply them as exponents per 128-wide K block, which is
  * exact; only the exponent field of a scale is read.  Accumulation is fp32
  * throughout.
+ *   T == 0 is valid (x and x_scale may then be NULL): nothing is written.
  *   Errors: MOE_EINVAL for NULL pointers or bad sizes; MOE_EUNSUPPORTED for
  *   other dtype combinations; bf16 with d % 128 or I % 64 nonzero; E4M3 x E4M3
  *   with d or I not a multiple of 256 or above 8192; an operand of 2 GiB or

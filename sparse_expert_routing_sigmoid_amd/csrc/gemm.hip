@@ -82,11 +82,12 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
   MOE_REQUIRE(x_t == MOE_F32 || x_t == MOE_BF16 || x_t == MOE_E4M3, MOE_EINVAL, "bad x_t");
   MOE_REQUIRE(w_t == MOE_F32 || w_t == MOE_BF16 || w_t == MOE_E4M3, MOE_EINVAL, "bad w_t");
   MOE_REQUIRE(y_t == MOE_F32 || y_t == MOE_BF16, MOE_EINVAL, "bad y_t");
-  MOE_REQUIRE(x && w13 && w2 && seg_offset && row_token && tile_map && n_tiles && y, MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(w13 && w2 && seg_offset && row_token && tile_map && n_tiles && y, MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(T == 0 || x, MOE_EINVAL, "NULL pointer");
   const Path p = path_of(x_t, w_t);
   MOE_REQUIRE(p != Path::NONE, MOE_EUNSUPPORTED, "unsupported (x_t, w_t) combination");
   MOE_REQUIRE(w_t != MOE_E4M3 || (w13_scale && w2_scale), MOE_EINVAL, "E4M3 weights need block scales");
-  MOE_REQUIRE(x_t != MOE_E4M3 || x_scale, MOE_EINVAL, "E4M3 activations need tile scales");
+  MOE_REQUIRE(T == 0 || x_t != MOE_E4M3 || x_scale, MOE_EINVAL, "E4M3 activations need tile scales");
   MOE_REQUIRE(ws && ws_bytes >= gemm_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t), MOE_EWORKSPACE,
               "workspace smaller than moe_gemm_workspace_bytes");
   const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
