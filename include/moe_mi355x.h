@@ -28,6 +28,11 @@
  *    enqueues kernels on it and returns without synchronising; calls on
  *    distinct streams may run concurrently from different threads.
  *  - Tensors are row-major and contiguous, element offsets are 64-bit.
+ *    Data tensors (u, centroids, x, weights, y, out, q and the workspaces)
+ *    must be 16-byte aligned (hipMalloc and torch allocations are 256-byte
+ *    aligned); index, gate, load, bias and scale arrays need only the
+ *    alignment of their element type.  A misaligned data tensor is
+ *    MOE_EINVAL.
  *    bf16 is stored as raw 16-bit patterns, E4M3 as one byte per value (OCP
  *    E4M3FN: exponent bias 7, largest finite 448, no infinities).
  *  - Arguments are checked on the host before any launch.  A bad argument

@@ -25,6 +25,10 @@ void clear_error();
     }                                         \
   } while (0)
 
+// Data tensors (activations, weights, outputs, workspaces) are read and
+// written with 16-byte vector accesses.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 // Checks the launch status after enqueueing kernels.
 moe_status launch_status(const char* where);
 
@@ -58,28 +62,17 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return __uint_as_float(__float_as_uint(mag) | sign);
 }
 
-// Round-to-nearest-even of |x| <= 448 (already clamped) to an E4M3FN code,
-// done in integer arithmetic on the fp32 bit pattern.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t bits = __float_as_uint(x);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t a = bits & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a < 0x3C800000u) {                 // |x| < 2^-6: subnormal range, step 2^-9
-    // q = RNE(|x| * 2^9); exact because the scale is a power of two.
-    const float s = __uint_as_float(a) * 512.0f;
-    const float r = __builtin_rintf(s);  // round half to even
-    code = static_cast<uint32_t>(r);     // 0..8; 8 is the smallest normal's code
-  } else {
-    // Normal: keep 3 mantissa bits with RNE on the 20 dropped bits.
-    const uint32_t lsb = (a >> 20) & 1u;
-    const uint32_t rounded = a + 0x7FFFFu + lsb;
-    const uint32_t e = (rounded >> 23) - 120u;  // biased exponent for bias 7
-    const uint32_t m = (rounded >> 20) & 7u;
-    code = (e << 3) | m;
-    if (code > 0x7Eu) code = 0x7Eu;      // cannot happen after clamping to 448
-  }
-  return code | sign;
+// Values of magnitude <= 448 (x divided by its power-of-two scale, which is
+// exact) to E4M3FN codes, round to nearest even, packed little-endian: the
+// packed conversion of gfx950 (OCP E4M3).  Over every fp32 magnitude in
+// [0, 448], both signs, it gives the same code as rounding the fp32 value to
+// 3 mantissa bits with ties to even (subnormal step 2^-9 below 2^-6).
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), true));
 }
 
 // Power-of-two tile scale: the smallest 2^k (k >= -126) with amax <= 448 * 2^k,

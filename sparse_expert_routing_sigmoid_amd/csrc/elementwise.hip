@@ -174,27 +174,49 @@ template <>
 __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, long long i) { return bf16_to_f32(p[i]); }
 
 // x * 2^-k is exact (a power of two) and lies in [-448, 448] for every x of
-// the tile, so the code is the round-to-nearest-even of x / scale.
-__device__ __forceinline__ uint32_t quant_one(float x, float inv_scale) { return f32_to_e4m3(x * inv_scale); }
+// the tile, so each code is the round-to-nearest-even of x / scale.
+// 1 x 128 tiles: 16 lanes per tile, 8 values per lane, 16 tiles per block.
+// A 1 x 128 tile of a row-major [rows, cols] array with cols % 128 == 0 is
+// the contiguous run x[128 t, 128 t + 128), t = row * cols / 128 + column
+// block, which is also the index of its scale.
+__device__ __forceinline__ void load8(const float* x, long long o, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(x + o);
+  const float4 b = *reinterpret_cast<const float4*>(x + o + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* x, long long o, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(x + o);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
 
-// 1 x 128 tiles: one wave per tile, two values per lane.
 template <typename XT>
-__global__ __launch_bounds__(256) void k_quant_1x128(const XT* __restrict__ x, long long rows, long long cols,
+__global__ __launch_bounds__(256) void k_quant_1x128(const XT* __restrict__ x, long long ntiles,
                                                      uint8_t* __restrict__ q, float* __restrict__ scale) {
-  const long long tiles_per_row = cols / 128;
-  const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tile >= rows * tiles_per_row) return;
-  const int lane = threadIdx.x & 63;
-  const long long r = tile / tiles_per_row;
-  const long long c = (tile % tiles_per_row) * 128 + lane * 2;
-  const long long o = r * cols + c;
-  const float a = ld(x, o), b = ld(x, o + 1);
-  const float amax = wave_max_f32(fmaxf(fabsf(a), fabsf(b)));
+  const long long tile = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool live = tile < ntiles;  // every lane takes part in the shuffles
+  const long long o = tile * 128 + sub * 8;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (live) load8(x, o, v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));  // the tile's 16 lanes
   const int k = pow2_scale_exp(amax);
-  const float sc = exp2_int(k), inv = exp2_int(-k);
-  const uint32_t qa = quant_one(a, inv), qb = quant_one(b, inv);
-  *reinterpret_cast<uint16_t*>(q + o) = static_cast<uint16_t>(qa | (qb << 8));
-  if (lane == 0) scale[tile] = sc;
+  const float inv = exp2_int(-k);
+  if (live) {
+    uint2 w;
+    w.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    w.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    *reinterpret_cast<uint2*>(q + o) = w;
+    if (sub == 0) scale[tile] = exp2_int(k);
+  }
 }
 
 // 128 x 128 blocks: one block of 256 threads per tile, 64 values per thread.
@@ -221,10 +243,8 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const XT* __restrict__ x,
   const float sc = exp2_int(k), inv = exp2_int(-k);
   for (int rr = row0; rr < 128; rr += 8) {
     const long long o = (tr * 128 + rr) * cols + tcol * 128 + col;
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w |= quant_one(ld(x, o + i), inv) << (8 * i);
-    *reinterpret_cast<uint32_t*>(q + o) = w;
+    *reinterpret_cast<uint32_t*>(q + o) =
+        e4m3x4(ld(x, o) * inv, ld(x, o + 1) * inv, ld(x, o + 2) * inv, ld(x, o + 3) * inv);
   }
   if (tid == 0) scale[blockIdx.x] = sc;
 }
@@ -243,6 +263,7 @@ moe_status combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_t, c
   MOE_REQUIRE(out_t == MOE_F32 || out_t == MOE_BF16, MOE_EINVAL, "out_t must be MOE_F32 or MOE_BF16");
   MOE_REQUIRE(T == 0 || (u && y && inv_row && topk_gate && seg_offset && out), MOE_EINVAL, "NULL pointer");
   MOE_REQUIRE(out != y, MOE_EINVAL, "out aliases y");
+  MOE_REQUIRE(aligned16(u) && aligned16(y) && aligned16(out), MOE_EINVAL, "u, y and out must be 16-byte aligned");
   if (T == 0) return MOE_OK;
   hipStream_t st = as_stream(stream);
   const int key = (u_t == MOE_BF16) * 4 + (y_t == MOE_BF16) * 2 + (out_t == MOE_BF16);
@@ -280,18 +301,18 @@ moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long lon
   MOE_REQUIRE(rows >= 0 && cols >= 0 && cols % 128 == 0 && rows % tile_rows == 0, MOE_EINVAL,
               "rows/cols must be multiples of the tile");
   MOE_REQUIRE(rows == 0 || cols == 0 || (x && q && scale), MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(q), MOE_EINVAL, "x and q must be 16-byte aligned");
   const long long ntiles = (rows / tile_rows) * (cols / 128);
   if (ntiles == 0) return MOE_OK;
   MOE_REQUIRE(ntiles < (1LL << 31) * 4, MOE_EINVAL, "too many tiles");
   hipStream_t st = as_stream(stream);
   if (tile_rows == 1) {
-    dim3 grid((unsigned)ceil_div(ntiles, 4));
+    dim3 grid((unsigned)ceil_div(ntiles, 16));
     if (x_t == MOE_F32)
-      hipLaunchKernelGGL(k_quant_1x128<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), rows, cols, q,
-                         scale);
+      hipLaunchKernelGGL(k_quant_1x128<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), ntiles, q, scale);
     else
-      hipLaunchKernelGGL(k_quant_1x128<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x), rows, cols,
-                         q, scale);
+      hipLaunchKernelGGL(k_quant_1x128<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x), ntiles, q,
+                         scale);
   } else {
     dim3 grid((unsigned)ntiles);
     if (x_t == MOE_F32)

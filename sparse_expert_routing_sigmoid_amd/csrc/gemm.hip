@@ -84,6 +84,8 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
   MOE_REQUIRE(y_t == MOE_F32 || y_t == MOE_BF16, MOE_EINVAL, "bad y_t");
   MOE_REQUIRE(w13 && w2 && seg_offset && row_token && tile_map && n_tiles && y, MOE_EINVAL, "NULL pointer");
   MOE_REQUIRE(T == 0 || x, MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(w13) && aligned16(w2) && aligned16(y) && aligned16(ws), MOE_EINVAL,
+              "x, w13, w2, y and ws must be 16-byte aligned");
   const Path p = path_of(x_t, w_t);
   MOE_REQUIRE(p != Path::NONE, MOE_EUNSUPPORTED, "unsupported (x_t, w_t) combination");
   MOE_REQUIRE(w_t != MOE_E4M3 || (w13_scale && w2_scale), MOE_EINVAL, "E4M3 weights need block scales");

@@ -302,10 +302,8 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
         const int k = pow2_scale_exp(amax);
         const float inv = exp2_int(-k);
         uint2 wv;
-        wv.x = f32_to_e4m3(v0.x * inv) | (f32_to_e4m3(v0.y * inv) << 8) | (f32_to_e4m3(v0.z * inv) << 16) |
-               (f32_to_e4m3(v0.w * inv) << 24);
-        wv.y = f32_to_e4m3(v1.x * inv) | (f32_to_e4m3(v1.y * inv) << 8) | (f32_to_e4m3(v1.z * inv) << 16) |
-               (f32_to_e4m3(v1.w * inv) << 24);
+        wv.x = e4m3x4(v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv);
+        wv.y = e4m3x4(v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv);
         uint8_t* dst = reinterpret_cast<uint8_t*>(out) + orow * Nd + col0 + ch * 8;
         *reinterpret_cast<uint2*>(dst) = wv;
         if (ch == 0) out_scale[orow * (Nd / 128) + n] = exp2_int(k);

@@ -333,6 +333,8 @@ moe_status route(const void* u, moe_dtype u_t, const float* centroids, const flo
   MOE_REQUIRE(K >= 1 && K <= MOE_MAX_K && K <= Nr, MOE_EINVAL, "K out of range");
   MOE_REQUIRE(expert_load != nullptr, MOE_EINVAL, "expert_load is NULL");
   MOE_REQUIRE(T == 0 || (u && centroids && bias && topk_idx && topk_gate), MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(aligned16(u) && aligned16(centroids) && aligned16(ws), MOE_EINVAL,
+              "u, centroids and ws must be 16-byte aligned");
   MOE_REQUIRE(T == 0 || (ws && ws_bytes >= route_workspace_bytes(T, d, Nr)), MOE_EWORKSPACE,
               "workspace smaller than moe_route_workspace_bytes");
   hipStream_t st = as_stream(stream);

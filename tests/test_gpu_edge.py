@@ -116,3 +116,39 @@ def test_fp8_tiles_of_zeros_and_extremes():
     assert np.array_equal(np_of(q), codes)
     assert np.array_equal(np_of(s).view(np.uint32), scales.view(np.uint32))
     assert np_of(s)[0].tolist() == [1.0, 1.0]                 # all-zero tiles
+
+
+def test_misaligned_data_tensors_are_rejected():
+    """Data tensors are accessed 16 bytes at a time: a view two bytes off is
+    refused on the host with MOE_EINVAL, before anything is launched."""
+    cfg = W.CONFIGS["mid_bf16"].with_(T=64, **SMALL)
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16,
+                       M.ExpertWeights(M.MOE_BF16, w13, w2), tile_m=32)
+    u = W.make_tokens(cfg, 0, "cuda")
+    e = W.make_centroids(cfg, "cuda")
+    b = W.make_bias(cfg, "cuda")
+    base = torch.empty(u.numel() + 8, dtype=u.dtype, device="cuda")
+    u_off = base[1:1 + u.numel()].view(u.shape)
+    u_off.copy_(u)
+    assert u_off.data_ptr() % 16 == 2
+    with pytest.raises(M.MoeError) as err:
+        layer.route(u_off, e, b)
+    assert err.value.status == M.MOE_EINVAL
+    layer.route(u, e, b)
+    layer.permute()
+    with pytest.raises(M.MoeError) as err:
+        layer.experts(u_off)
+    assert err.value.status == M.MOE_EINVAL
+    layer.experts(u)
+    with pytest.raises(M.MoeError) as err:
+        layer.combine(u_off)
+    assert err.value.status == M.MOE_EINVAL
+    q = torch.empty((cfg.T, cfg.d), dtype=torch.uint8, device="cuda")
+    s = torch.empty((cfg.T, cfg.d // 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(M.MoeError) as err:
+        M.fp8_quantize_tiles(u_off, 1, q, s)
+    assert err.value.status == M.MOE_EINVAL
+    out = layer.combine(u)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
