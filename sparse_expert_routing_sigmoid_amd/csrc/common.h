@@ -25,6 +25,14 @@ void clear_error();
     }                                         \
   } while (0)
 
+// SiLU(a) = a * sigmoid(a) of the expert FFNs, from the hardware base-2
+// exponential and reciprocal (each within about 1 ulp): a few ulp in fp32,
+// far below the bf16 / E4M3 rounding of h that follows.  Large negative a
+// gives exp2 = inf, reciprocal 0 and SiLU = -0.
+__device__ __forceinline__ float silu(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+}
+
 // Data tensors (activations, weights, outputs, workspaces) are read and
 // written with 16-byte vector accesses.
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

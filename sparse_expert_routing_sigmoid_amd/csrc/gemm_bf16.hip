@@ -55,7 +55,6 @@ __device__ __forceinline__ TileInfo tile_of_block(const int32_t* tile_map, const
   return ti;
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
 // Loads one 128 x 64 bf16 slab (4 x 16 B per thread) from row pointers.
 struct Slab {

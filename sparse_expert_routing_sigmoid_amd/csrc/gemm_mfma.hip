@@ -53,7 +53,6 @@ struct Fmt {
   static constexpr int STAGE = P_OPS + (FP8 ? 1024 : 0); // + 256 A-row scales (fp32)
 };
 
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + expf(-a)); }
 
 __device__ __forceinline__ int acc_row32(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
@@ -291,8 +290,8 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
       if (PHASE_A) {  // h = SiLU(gate) * up
         const float4 u0 = *reinterpret_cast<const float4*>(er + 512 + ch * 32);
         const float4 u1 = *reinterpret_cast<const float4*>(er + 512 + ch * 32 + 16);
-        v0 = make_float4(silu_f(v0.x) * u0.x, silu_f(v0.y) * u0.y, silu_f(v0.z) * u0.z, silu_f(v0.w) * u0.w);
-        v1 = make_float4(silu_f(v1.x) * u1.x, silu_f(v1.y) * u1.y, silu_f(v1.z) * u1.z, silu_f(v1.w) * u1.w);
+        v0 = make_float4(silu(v0.x) * u0.x, silu(v0.y) * u0.y, silu(v0.z) * u0.z, silu(v0.w) * u0.w);
+        v1 = make_float4(silu(v1.x) * u1.x, silu(v1.y) * u1.y, silu(v1.z) * u1.z, silu(v1.w) * u1.w);
       }
       const long long orow = it.row0 + pass * 128 + r;
       if constexpr (H_FP8) {

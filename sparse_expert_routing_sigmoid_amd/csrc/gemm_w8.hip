@@ -51,7 +51,6 @@ __device__ __forceinline__ u32x4_v ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
-__device__ __forceinline__ float w8_silu(float a) { return a / (1.0f + expf(-a)); }
 
 // 16 E4M3 codes (one 16-byte load) times `scale` -> 2 x 8 bf16, K order kept.
 __device__ __forceinline__ void widen16(u32x4_v q, float scale, bf16x8_v& lo, bf16x8_v& hi) {
@@ -173,7 +172,7 @@ __device__ __forceinline__ void w8_pass(const W8Lanes& L, const int32_t* __restr
       OT* orow = out + (long long)(row0 + r) * out_ld + col0 + L.c;
       if (PHASE_A) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) w8_store(orow + f * 16, w8_silu(acc[m][f][i]) * acc[m][f + 2][i]);
+        for (int f = 0; f < 2; ++f) w8_store(orow + f * 16, silu(acc[m][f][i]) * acc[m][f + 2][i]);
       } else {
 #pragma unroll
         for (int f = 0; f < W8_NB; ++f) w8_store(orow + f * 16, acc[m][f][i]);
