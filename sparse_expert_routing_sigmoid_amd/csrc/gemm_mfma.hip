@@ -10,12 +10,14 @@
 // Work decomposition.  A work item is (row tile of the tile map, N tile).
 // Phase A: N tile = 128 h columns = 128 gate rows + the 128 up rows of the
 // same columns of W13.  Phase B: N tile = 256 columns of y (rows of W2).
-// N tile n belongs to XCD n % 8, so every weight byte is fetched by one XCD
-// only and all row tiles of an expert that share an N tile meet in that
+// k_ffn_schedule deals whole experts to the 8 XCDs (largest first, snake
+// order; a shared expert's tiles one by one), so an expert's weights are
+// fetched by one XCD, and lists each XCD's items N-tile major, so the row
+// tiles of an expert that share a weight slab run close together in that
 // XCD's L2.  The kernel is persistent: 8 * (CUs / 8) blocks, block b runs on
-// XCD b % 8 (workgroups are dealt to XCDs round robin) and pulls items of its
-// XCD from a per-XCD atomic counter, in (row tile, N tile) order.  Results do
-// not depend on which block runs an item.
+// XCD b % 8 (workgroups are dealt to XCDs round robin) and pulls items from
+// its XCD's list through an atomic counter, then helps the other XCDs.
+// Results do not depend on which block runs an item.
 //
 // Block tile: 256 rows x 256 weight rows x 128 bytes of K (64 bf16 or 128
 // E4M3 values: one scale block), 256 threads = 4 waves in a 2 x 2 grid, each
