@@ -51,13 +51,19 @@ struct Vec8<float> {
 };
 
 // Raw 8-element vectors, kept as loaded until they are added (bf16 rows take
-// 4 registers instead of 8).
+// 4 registers instead of 8).  Every byte is read once, so the loads are
+// non-temporal (264 -> 231 us for the combine at T = 8192, d = 7168).
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
 template <typename T>
 struct Raw8;
 template <>
 struct Raw8<uint16_t> {
   uint4 q;
-  __device__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ void load(const uint16_t* p) {
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    q = make_uint4(v.x, v.y, v.z, v.w);
+  }
   __device__ void get(float (&v)[8]) const {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -71,8 +77,10 @@ template <>
 struct Raw8<float> {
   float4 a, b;
   __device__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
+    const f32x4_nt x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+    const f32x4_nt y = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p + 4));
+    a = make_float4(x.x, x.y, x.z, x.w);
+    b = make_float4(y.x, y.y, y.z, y.w);
   }
   __device__ void get(float (&v)[8]) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
