@@ -247,8 +247,30 @@ __global__ __launch_bounds__(256) void k_route_select(const float* __restrict__ 
   for (int j = 0; j < EPL; ++j) {
     const int i = lane + 64 * j;
     if (i < Nr) {
-      float zz = z[(long long)t * Nr + i];
-      for (int p = 1; p < nparts; ++p) zz += z[(long long)p * T * Nr + (long long)t * Nr + i];  // fixed order
+      // partial sums added in the fixed order 0, 1, ..., nparts - 1; loaded
+      // eight at a time so their latencies overlap
+      const float* zi = z + (long long)t * Nr + i;
+      const long long ps = (long long)T * Nr;
+      float zz;
+      int p;
+      if (nparts >= 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = zi[q * ps];
+        zz = v[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) zz += v[q];
+        for (p = 8; p + 8 <= nparts; p += 8) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = zi[(p + q) * ps];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zz += v[q];
+        }
+      } else {
+        zz = zi[0];
+        p = 1;
+      }
+      for (; p < nparts; ++p) zz += zi[p * ps];
       s[j] = 1.0f / (1.0f + expf(-zz));
       const float v = s[j] + bias[i];
       key[j] = (static_cast<unsigned long long>(float_order_key(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
