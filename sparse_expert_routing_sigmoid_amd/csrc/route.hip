@@ -7,8 +7,9 @@
 //
 // Kernels:
 //   k_router_logits_mfma  (bf16 u, Nr <= 256) z = u . e on bf16 MFMA with e
-//                    split exactly into three bf16 parts; K split over
-//                    blocks into partial sums added in a fixed order later.
+//                    split exactly into three bf16 parts, 128 or 256 tokens
+//                    per block; K split over blocks into partial sums added
+//                    in a fixed order later.
 //   k_router_logits  (fp32 u, or other shapes) z[t, i] = u_t . e_i in fp32 on
 //                    the vector ALUs, LDS tiles of 64 tokens x 64 experts;
 //                    every 32-wide K chunk is summed into its own partial
@@ -109,40 +110,52 @@ __global__ void k_split_centroids(const float* __restrict__ e, long long n, uint
   e3[2 * n + i] = __builtin_bit_cast(uint16_t, c);
 }
 
-constexpr int RM_TT = 128;              // tokens per block
 constexpr int RM_TE = 256;              // experts per block (all, Nr <= 256)
 constexpr int RM_BK = 32;               // K per stage
-constexpr int RM_ROW = RM_BK * 2 + 16;  // LDS row bytes (64 B of data + 16 B pad against bank conflicts)
+constexpr int RM_ROW = RM_BK * 2;       // LDS row bytes: four 16-byte chunks
 constexpr int RM_BROWS = 3 * RM_TE;     // B rows: e1, e2, e3 of 256 experts
 
+// Tokens per block: 256 when there are enough tokens to fill the chip with
+// them (the centroid rows, the bulk of each stage, then serve twice as many
+// tokens), else 128.
+inline int router_tile_tokens(int T) { return T >= 4096 ? 256 : 128; }
+
+// LDS offset of 16-byte chunk c of row r: the chunk index is XORed with
+// (r >> 1) & 3, so the 8 rows one fragment read touches at a time (row pairs
+// 128 bytes apart) fall on distinct banks.
+__device__ __forceinline__ int rm_off(int r, int c) { return r * RM_ROW + ((c ^ ((r >> 1) & 3)) << 4); }
+
 // Partial logits zp[ks][t][i] = sum over the ks-th K chunk of u[t,k] * e[i,k].
-// Grid (T / 128, KS); 256 threads = 4 waves; wave w covers all 128 tokens of
-// the block and experts 64 w .. 64 w + 63 (4 x 2 MFMA 32x32 tiles), running
-// the three bf16 parts of e into the same fp32 accumulators.  Operands are
-// staged through registers into a padded, double-buffered LDS tile.
+// Grid (T / TT, KS); 256 threads = 4 waves; wave w covers all TT tokens of
+// the block and experts 64 w .. 64 w + 63 (TT/32 x 2 MFMA 32x32 tiles),
+// running the three bf16 parts of e into the same fp32 accumulators.
+// Operands are staged through registers into a double-buffered LDS tile.
+template <int TT>
 __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __restrict__ u,
                                                             const uint16_t* __restrict__ e3, int T, int d, int Nr,
                                                             int kchunk, float* __restrict__ zp) {
+  constexpr int MI = TT / 32;                          // 32-token MFMA tiles
+  constexpr int QA = TT * 4 / 256;                     // A chunks per thread and stage
+  constexpr int QB = RM_BROWS * 4 / 256;               // B chunks per thread and stage
+  constexpr int SBYTES = (TT + RM_BROWS) * RM_ROW;     // one stage
   extern __shared__ __attribute__((aligned(16))) uint8_t rs[];
-  constexpr int SBYTES = (RM_TT + RM_BROWS) * RM_ROW;  // one stage
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RM_TT;
+  const int t0 = blockIdx.x * TT;
   const int ks = blockIdx.y;
   const int k_begin = ks * kchunk;
   const int nk = kchunk / RM_BK;
   const long long nE = (long long)Nr * d;
-  // staging: A = 128 rows x 4 chunks (2 per thread), B = 768 rows x 4 chunks (12 per thread)
-  uint4 ra[2], rb[12];
+  uint4 ra[QA], rb[QB];
   auto gload = [&](int stage) {
     const int kofs = k_begin + stage * RM_BK;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < QA; ++q) {
       const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
       const int t = t0 + r;
       ra[q] = t < T ? *reinterpret_cast<const uint4*>(u + (long long)t * d + kofs + ch * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 12; ++q) {
+    for (int q = 0; q < QB; ++q) {
       const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
       const int part = r / RM_TE, ex = r % RM_TE;
       rb[q] = ex < Nr ? *reinterpret_cast<const uint4*>(e3 + part * nE + (long long)ex * d + kofs + ch * 8)
@@ -151,19 +164,19 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
   };
   auto lstore = [&](uint8_t* sb) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < QA; ++q) {
       const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
-      *reinterpret_cast<uint4*>(sb + r * RM_ROW + ch * 16) = ra[q];
+      *reinterpret_cast<uint4*>(sb + rm_off(r, ch)) = ra[q];
     }
 #pragma unroll
-    for (int q = 0; q < 12; ++q) {
+    for (int q = 0; q < QB; ++q) {
       const int c = tid + 256 * q, r = c >> 2, ch = c & 3;
-      *reinterpret_cast<uint4*>(sb + (RM_TT + r) * RM_ROW + ch * 16) = rb[q];
+      *reinterpret_cast<uint4*>(sb + rm_off(TT + r, ch)) = rb[q];
     }
   };
-  f32x16_r acc[4][2];
+  f32x16_r acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -177,20 +190,20 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
     if (s + 1 < nk) gload(s + 1);
 #pragma unroll
     for (int kk = 0; kk < RM_BK / 16; ++kk) {
-      const int cofs = (kk * 2 + (lane >> 5)) * 16;
-      bf16x8_r af[4];
+      const int c = kk * 2 + (lane >> 5);
+      bf16x8_r af[MI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = __builtin_bit_cast(bf16x8_r, *reinterpret_cast<const uint4*>(cur + (i * 32 + (lane & 31)) * RM_ROW + cofs));
+      for (int i = 0; i < MI; ++i)
+        af[i] = __builtin_bit_cast(bf16x8_r, *reinterpret_cast<const uint4*>(cur + rm_off(i * 32 + (lane & 31), c)));
 #pragma unroll
       for (int part = 0; part < 3; ++part)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const bf16x8_r bfr = __builtin_bit_cast(
               bf16x8_r, *reinterpret_cast<const uint4*>(
-                            cur + (RM_TT + part * RM_TE + e0 + j * 32 + (lane & 31)) * RM_ROW + cofs));
+                            cur + rm_off(TT + part * RM_TE + e0 + j * 32 + (lane & 31), c)));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
+          for (int i = 0; i < MI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[i][j], 0, 0, 0);
         }
     }
     if (s + 1 < nk) lstore(rs + ((s + 1) & 1) * SBYTES);
@@ -198,7 +211,7 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
   }
   float* zo = zp + (long long)ks * T * Nr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -210,14 +223,35 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
 }
 
 // K-split count of the MFMA router for T tokens and hidden size d (0 = the
-// MFMA router does not apply): enough blocks to fill the chip, each chunk a
-// multiple of the stage width.
+// MFMA router does not apply): enough blocks to fill the chip (one per CU
+// with 256-token tiles, whose LDS takes a whole CU; two rounds with 128),
+// each chunk a multiple of the stage width.
 int router_ksplit(int T, int d, int Nr) {
   if (Nr > RM_TE || d % RM_BK != 0) return 0;
-  const int tiles = (T + RM_TT - 1) / RM_TT;
+  const int tt = router_tile_tokens(T);
+  const int tiles = (T + tt - 1) / tt;
+  const int target = tt == 256 ? 256 : 512;
   int ks = 1;
-  while (ks < 32 && tiles * ks < 512 && d % (RM_BK * ks * 2) == 0) ks *= 2;
+  while (ks < 32 && tiles * ks < target && d % (RM_BK * ks * 2) == 0) ks *= 2;
   return ks;
+}
+
+template <int TT>
+moe_status launch_router_mfma(const uint16_t* u, const uint16_t* e3, int T, int d, int Nr, int ks, float* z,
+                              hipStream_t st) {
+  dim3 grid((T + TT - 1) / TT, ks);
+  const size_t lds = 2 * (size_t)(TT + RM_BROWS) * RM_ROW;
+  static bool attr_set = false;  // raising the dynamic LDS limit is idempotent
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_router_logits_mfma<TT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+      set_error("moe_route: cannot raise the LDS limit of the router kernel");
+      return MOE_EHIP;
+    }
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_router_logits_mfma<TT>, grid, dim3(256), lds, st, u, e3, T, d, Nr, d / ks, z);
+  return MOE_OK;
 }
 
 __global__ void k_zero_i32(int32_t* p, int n) {
@@ -370,19 +404,10 @@ moe_status route(const void* u, moe_dtype u_t, const float* centroids, const flo
       uint16_t* e3 = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + ((zbytes + 255) / 256) * 256);
       const long long n = (long long)Nr * d;
       hipLaunchKernelGGL(k_split_centroids, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, centroids, n, e3);
-      dim3 grid((T + RM_TT - 1) / RM_TT, ks);
-      const size_t lds = 2 * (size_t)(RM_TT + RM_BROWS) * RM_ROW;
-      static bool attr_set = false;  // raising the dynamic LDS limit is idempotent
-      if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_router_logits_mfma),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-          set_error("moe_route: cannot raise the LDS limit of the router kernel");
-          return MOE_EHIP;
-        }
-        attr_set = true;
-      }
-      hipLaunchKernelGGL(k_router_logits_mfma, grid, dim3(256), lds, st, static_cast<const uint16_t*>(u), e3, T, d, Nr,
-                         d / ks, z);
+      const moe_status ls = router_tile_tokens(T) == 256
+                                ? launch_router_mfma<256>(static_cast<const uint16_t*>(u), e3, T, d, Nr, ks, z, st)
+                                : launch_router_mfma<128>(static_cast<const uint16_t*>(u), e3, T, d, Nr, ks, z, st);
+      if (ls != MOE_OK) return ls;
       nparts = ks;
     } else {
       dim3 grid((T + LG_TT - 1) / LG_TT, (Nr + LG_TE - 1) / LG_TE);
