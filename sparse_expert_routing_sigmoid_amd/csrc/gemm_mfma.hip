@@ -247,11 +247,12 @@ __device__ __forceinline__ float absmax8(float4 a, float4 b) {
                fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
 }
 
-// Epilogue.  Two passes of 128 rows (wave row 0, then 1): the waves of the
-// pass write their fp32 accumulators to LDS (64 rows per stage buffer, one
-// 1 KB row = 256 fp32), then all threads copy the rows out with 16-byte
-// stores, applying SwiGLU (phase A: gate in columns 0..127, up in 128..255)
-// and converting to the output type.  With H_FP8 the 128 h values of a row
+// Epilogue.  Phase B with bf16 output stores straight from the
+// accumulators.  Otherwise two passes of 128 rows (wave row 0, then 1): the
+// waves of the pass write their fp32 accumulators to LDS (64 rows per stage
+// buffer, one 1 KB row = 256 fp32), then all threads copy the rows out with
+// 16-byte stores, applying SwiGLU (phase A: gate in columns 0..127, up in
+// 128..255) and converting to the output type.  With H_FP8 the 128 h values of a row
 // are quantised as one 1x128 E4M3 tile (power-of-two scale, round to nearest
 // even): the 16 threads holding a row find its amax with lane shuffles.
 // MT == 0: the wave has no rows.
@@ -263,6 +264,29 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
   constexpr int LSTR = P_TN * 4;
   const int lcol = it.lane & 31;
   const long long col0 = (long long)n * NC;
+  if constexpr (!PHASE_A && sizeof(OT) == 2) {
+    // bf16 y straight from the accumulators, one 2-byte store per value: no
+    // LDS round trip and no barriers (6.4 -> 5.4 us per 256 x 256 item).
+    // Each accumulator is read on its own; left to itself the compiler
+    // copies all of them to VGPRs first and spills.
+    uint16_t* ob = reinterpret_cast<uint16_t*>(out) + col0 + wn * 128 + lcol;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = wm * 128 + i * 32 + acc_row32(e, it.lane);
+        if (r < it.rows) {
+          uint16_t* rowp = ob + (long long)(it.row0 + r) * Nd;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc[i][j][e]));
+            rowp[j * 32] = f32_to_bf16(v);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
