@@ -499,7 +499,7 @@ constexpr int SCHED_MAXU = 4096;
 __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict__ tile_map,
                                                        const int32_t* __restrict__ n_tiles, int Nr, int ntA,
                                                        int ntB, int cap, int* __restrict__ sched) {
-  __shared__ int s_seg[SCHED_MAXU];
+  __shared__ int s_seg[SCHED_MAXU], s_trows[SCHED_MAXU];
   __shared__ int s_ustart[SCHED_MAXU + 1], s_urows[SCHED_MAXU], s_order[SCHED_MAXU];
   __shared__ int s_uoffA[SCHED_MAXU], s_uoffB[SCHED_MAXU];
   __shared__ unsigned char s_uxcd[SCHED_MAXU];
@@ -508,7 +508,11 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
   const int tid = threadIdx.x;
   const int tiles = min(*n_tiles, min(cap, SCHED_MAXU));
   if (tid < 16) sched[tid] = 0;
-  for (int t = tid; t < tiles; t += 1024) s_seg[t] = tile_map[4LL * t];
+  for (int t = tid; t < tiles; t += 1024) {
+    const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * t);
+    s_seg[t] = tm.x;
+    s_trows[t] = tm.w;
+  }
   __syncthreads();
   // unit starts, numbered by a scan (4 tiles per thread)
   int flags[4], cnt = 0;
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
   __syncthreads();
   for (int v = tid; v < nu; v += 1024) {
     int rows = 0;
-    for (int t = s_ustart[v]; t < s_ustart[v + 1]; ++t) rows += tile_map[4LL * t + 3];
+    for (int t = s_ustart[v]; t < s_ustart[v + 1]; ++t) rows += s_trows[t];
     s_urows[v] = rows;
   }
   __syncthreads();
@@ -594,14 +598,18 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
   __syncthreads();
   int* listA = sched + SCHED_HDR;
   int* listB = listA + (long long)cap * ntA;
-  for (int v = tid; v < nu; v += 1024) {
-    const int t0 = s_ustart[v], len = s_ustart[v + 1] - t0, x = s_uxcd[v];
-    int* la = listA + s_xA[x] + s_uoffA[v];
-    for (int n = 0; n < ntA; ++n)
-      for (int j = 0; j < len; ++j) la[n * len + j] = ((t0 + j) << 8) | n;
-    int* lb = listB + s_xB[x] + s_uoffB[v];
-    for (int n = 0; n < ntB; ++n)
-      for (int j = 0; j < len; ++j) lb[n * len + j] = ((t0 + j) << 8) | n;
+  // one thread per (unit, N tile): the unit's row tiles for that N tile
+  for (int q = tid; q < nu * ntA; q += 1024) {
+    const int v = q / ntA, n = q - v * ntA;
+    const int t0 = s_ustart[v], len = s_ustart[v + 1] - t0;
+    int* la = listA + s_xA[s_uxcd[v]] + s_uoffA[v] + n * len;
+    for (int j = 0; j < len; ++j) la[j] = ((t0 + j) << 8) | n;
+  }
+  for (int q = tid; q < nu * ntB; q += 1024) {
+    const int v = q / ntB, n = q - v * ntB;
+    const int t0 = s_ustart[v], len = s_ustart[v + 1] - t0;
+    int* lb = listB + s_xB[s_uxcd[v]] + s_uoffB[v] + n * len;
+    for (int j = 0; j < len; ++j) lb[j] = ((t0 + j) << 8) | n;
   }
 }
 
