@@ -1,0 +1,122 @@
+"""Plain fp64 CPU oracle of the DeepSeekMoE layer backward (test infrastructure).
+
+THIS IS TEST INFRASTRUCTURE.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import it; the HIP library shares nothing
+with it.  Every step is the derivative of the corresponding forward step of
+oracle/moe.py, written out in fp64 with NumPy matmuls.
+
+Sources: the forward equations of the "DeepSeek-V3 Technical Report" reading
+guide (xyznot.com), Method section 2 ([RG-MoE]: combine equation, affinity
+sentence, gate equation, bias rule), with the readings R1 (gate = s / sum of
+the selected s), R2 (selection order), R6 (SwiGLU FFN) and R7 (shared gate 1,
+residual) of oracle/moe.py.  The pages print no backward pass; it follows
+from the forward by the chain rule:
+
+  out_t = u_t + sum_j FFN_j(u_t) + sum_k g_{t,k} FFN_{i_k}(u_t)
+  g_{t,k} = s_{t,k} / S_t,  S_t = sum_k s_{t,k},  s = sigmoid(u_t . e_i)
+  FFN(x) = W2 (SiLU(a) * b),  [a; b] = W13 x
+
+Reading B1: the selection (top-K of s + b) is piecewise constant, so it gets
+no derivative: gradients flow through the gates of the selected experts
+only, and the bias b gets none.  This holds everywhere except on the
+measure-zero set of exact ties, where the layer is not differentiable.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .moe import route, sigmoid
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(a: np.ndarray) -> np.ndarray:
+    return a * sigmoid(a)
+
+
+def silu_grad(a: np.ndarray) -> np.ndarray:
+    """d/da [a * sigmoid(a)] = sigmoid(a) * (1 + a * (1 - sigmoid(a)))."""
+    sg = sigmoid(a)
+    return sg * (1.0 + a * (1.0 - sg))
+
+
+@dataclass
+class LayerGrads:
+    du: np.ndarray      # [T, d]       dL/du (residual + experts + router)
+    de: np.ndarray      # [N_r, d]     dL/de (centroids)
+    dw13: np.ndarray    # [E, 2I, d]   dL/dW13 (gate rows, then up rows)
+    dw2: np.ndarray     # [E, d, I]    dL/dW2
+    dgate: np.ndarray   # [T, K]       dL/dg of the selected experts
+    dz: np.ndarray      # [T, K]       dL/d(u_t . e_i) of the selected experts
+    du_ffn: np.ndarray  # [T, d]       the part of du that flows through the expert FFNs
+    du_router: np.ndarray  # [T, d]    the part of du that flows through the gates
+
+
+def ffn_backward(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray):
+    """Backward of y = W2 (SiLU(a) * b), [a; b] = W13 x, for rows x [n, d]
+    and output gradients dy [n, d].  Returns (dx [n, d], dw13 [2I, d],
+    dw2 [d, I], y [n, d])."""
+    x, w13, w2, dy = _f64(x), _f64(w13), _f64(w2), _f64(dy)
+    I = w2.shape[1]
+    ab = x @ w13.T
+    a, b = ab[:, :I], ab[:, I:]
+    h = silu(a) * b
+    y = h @ w2.T
+    dw2 = dy.T @ h                      # [d, I]
+    dh = dy @ w2                        # [n, I]
+    da = dh * b * silu_grad(a)
+    db = dh * silu(a)
+    dab = np.concatenate([da, db], axis=1)   # [n, 2I]
+    dw13 = dab.T @ x                    # [2I, d]
+    dx = dab @ w13                      # [n, d]
+    return dx, dw13, dw2, y
+
+
+def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out) -> LayerGrads:
+    """Gradients of L = sum(grad_out * out) for the layer of
+    oracle.moe.layer_forward (bf16 / fp32 path, no FP8 quantisation).
+
+    u [T, d], e [N_r, d], b [N_r], w13 [N_r+N_s, 2I, d], w2 [N_r+N_s, d, I],
+    grad_out [T, d] = dL/dout."""
+    u, e, G = _f64(u), _f64(e), _f64(grad_out)
+    w13, w2 = _f64(w13), _f64(w2)
+    T, d = u.shape
+    r = route(u, e, b, K)
+    du_ffn = np.zeros((T, d))
+    dw13 = np.zeros_like(w13)
+    dw2 = np.zeros_like(w2)
+    dgate = np.zeros((T, K))
+
+    # shared experts: gate 1 (R7), every token
+    for j in range(Ns):
+        dx, dw13[Nr + j], dw2[Nr + j], _ = ffn_backward(u, w13[Nr + j], w2[Nr + j], G)
+        du_ffn += dx
+
+    # routed experts: the output gradient reaches FFN_i scaled by the gate;
+    # the gate's own gradient is <dL/dout_t, FFN_i(u_t)>
+    for i in range(Nr):
+        t_sel, k_sel = np.nonzero(r.idx == i)
+        if t_sel.size == 0:
+            continue
+        dy = r.gate[t_sel, k_sel][:, None] * G[t_sel]
+        dx, dw13[i], dw2[i], y = ffn_backward(u[t_sel], w13[i], w2[i], dy)
+        np.add.at(du_ffn, t_sel, dx)
+        dgate[t_sel, k_sel] = np.sum(G[t_sel] * y, axis=1)
+
+    # gates g_k = s_k / S (R1): dL/ds_k = (dL/dg_k - sum_j g_j dL/dg_j) / S;
+    # s = sigmoid(z): dz = ds * s (1 - s); z = u . e_i
+    S = np.sum(r.score, axis=1, keepdims=True)
+    ds = (dgate - np.sum(r.gate * dgate, axis=1, keepdims=True)) / S
+    dz = ds * r.score * (1.0 - r.score)
+    du_router = np.zeros((T, d))
+    de = np.zeros_like(e)
+    for k in range(K):
+        du_router += dz[:, k:k + 1] * e[r.idx[:, k]]
+        np.add.at(de, r.idx[:, k], dz[:, k:k + 1] * u)
+
+    du = G + du_ffn + du_router         # the residual passes grad_out through
+    return LayerGrads(du, de, dw13, dw2, dgate, dz, du_ffn, du_router)
