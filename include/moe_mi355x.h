@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Limits of this implementation. */
 #define MOE_MAX_EXPERTS 1024   /* routed + shared experts */
@@ -246,6 +246,111 @@ moe_status moe_bias_update(const int32_t* expert_load, int Nr, long long total_a
  * ---------------------------------------------------------------------- */
 moe_status fp8_quantize_tiles(const void* x, moe_dtype x_t, long long rows, long long cols,
                               int tile_rows, int tile_cols, uint8_t* q, float* scale, void* stream);
+
+/* ========================================================================
+ * Backward pass (bf16 activations and weights).  The pages print no
+ * backward pass; these calls compute the chain rule through the forward
+ * above.  The top-K selection and the bias b are piecewise constant in the
+ * inputs, so no gradient flows through them and b receives none; the
+ * gradient reaches the affinities only through the gates of the selected
+ * experts.  With G = dL/dh' (the gradient of the layer output), one step is
+ *   moe_expert_gemm_train (forward, keeping h and [a | b])
+ *   moe_combine_backward  -> dy (gradient of every expert row), dgate, dz
+ *   moe_expert_gemm_backward -> dx (gradient of every expert row's input),
+ *                               dW13, dW2
+ *   moe_route_backward    -> du, de
+ * after moe_route / moe_permute of the forward (same buffers).
+ * ====================================================================== */
+
+/* ------------------------------------------------------------------------
+ * moe_expert_gemm_train: moe_expert_gemm for (x_t, w_t) = (BF16, BF16) that
+ * also keeps what the backward needs: h [P_max, I] (bf16, SiLU(a) * b) and
+ * ab [P_max, 2I] (bf16: columns 0..I-1 a = W_gate x, I..2I-1 b = W_up x) of
+ * every token row (padding rows unwritten).  y as in moe_expert_gemm.
+ *   ws  device, moe_gemm_train_workspace_bytes(...) bytes (work schedule)
+ *   Errors: as moe_expert_gemm; MOE_EUNSUPPORTED unless d % 256 == 0,
+ *   I % 128 == 0 (d <= 65280, I <= 32640) and every operand < 2 GiB.
+ * ---------------------------------------------------------------------- */
+size_t moe_gemm_train_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status moe_expert_gemm_train(const void* x, const void* w13, const void* w2,
+                                 int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                 const int32_t* seg_offset, const int32_t* row_token,
+                                 const int32_t* tile_map, const int32_t* n_tiles,
+                                 void* ws, size_t ws_bytes, void* h, void* ab,
+                                 void* y, moe_dtype y_t, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine_backward: gradients of the [RG-MoE] combine equation and of
+ * the gate equation (g = s / sum of the selected s) for one step.
+ *   grad_out, g_t  device [T, d] G = dL/dh', MOE_F32 or MOE_BF16
+ *   y, y_t         device [P_max, d] expert outputs of the forward
+ *   inv_row, topk_gate, topk_score: device [T, K] from moe_permute/moe_route
+ *   seg_offset     device [Nr+Ns+1]
+ *   dy             device [P_max, d] bf16 out: g[t,k] * G_t on row (t, k),
+ *                  G_t on the shared rows of t (padding rows unwritten)
+ *   dgate          device [T, K] fp32 out: <G_t, y[row(t, k)]>
+ *   dz             device [T, K] fp32 out: dL/d(u_t . e_i) of the selected
+ *                  experts, (dgate_k - sum_j g_j dgate_j) / S_t * s (1 - s)
+ *   dz_row         device [P_max] fp32 out: dz of row (t, k) at that row
+ * The dot products are summed in fp32 in a fixed order (deterministic).
+ *   Errors: MOE_EINVAL for NULL pointers, bad sizes, d % 8 != 0.
+ * ---------------------------------------------------------------------- */
+moe_status moe_combine_backward(const void* grad_out, moe_dtype g_t, const void* y, moe_dtype y_t,
+                                const int32_t* inv_row, const float* topk_gate, const float* topk_score,
+                                const int32_t* seg_offset, int T, int d, int K, int Nr, int Ns,
+                                void* dy, float* dgate, float* dz, float* dz_row, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_expert_gemm_backward: gradients of every expert's SwiGLU FFN on its
+ * rows (bf16 operands, fp32 accumulation on the matrix cores):
+ *   dh = dy W2,  da = dh * b * SiLU'(a),  db = dh * SiLU(a)
+ *   dx = [da | db] W13 (per row),  dW2_e = sum_rows dy^T h,
+ *   dW13_e = sum_rows [da | db]^T x
+ *   x              device [T, d] bf16 tokens of the forward
+ *   w13, w2        device bf16 weights as in moe_expert_gemm
+ *   h, ab          device, from moe_expert_gemm_train
+ *   dy             device [P_max, d] bf16 from moe_combine_backward
+ *   ws             device, moe_gemm_backward_workspace_bytes(...) bytes
+ *                  (holds [da | db] of every row)
+ *   dx             device [P_max, d] bf16 out (padding rows unwritten)
+ *   dw13, dw2      device [Nr+Ns, 2I, d] and [Nr+Ns, d, I] out (overwritten;
+ *                  experts with no rows get zeros), dw_t MOE_F32 or MOE_BF16
+ * Every output element is summed by one thread in a fixed order.
+ *   Errors: MOE_EINVAL for NULL pointers or bad sizes; MOE_EUNSUPPORTED
+ *   unless d % 256 == 0, I % 128 == 0 and every operand < 2 GiB;
+ *   MOE_EWORKSPACE for a small ws.
+ * ---------------------------------------------------------------------- */
+size_t moe_gemm_backward_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status moe_expert_gemm_backward(const void* x, const void* w13, const void* w2,
+                                    const void* h, const void* ab, const void* dy,
+                                    int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                    const int32_t* seg_offset, const int32_t* row_token,
+                                    const int32_t* tile_map, const int32_t* n_tiles,
+                                    void* ws, size_t ws_bytes, void* dx,
+                                    void* dw13, void* dw2, moe_dtype dw_t, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_route_backward: the layer's input and centroid gradients.
+ *   du_t = G_t + sum of dx over the token's shared and routed rows
+ *          + sum_k dz[t,k] e_{topk_idx[t,k]}           (fp32, that order)
+ *   de_i = sum over the rows of segment i, in row order, of dz_row * u_t
+ *   grad_out, g_t  device [T, d] G, MOE_F32 or MOE_BF16
+ *   dx             device [P_max, d] bf16 from moe_expert_gemm_backward
+ *   u, u_t         device [T, d] tokens, MOE_F32 or MOE_BF16
+ *   centroids      device [Nr, d] fp32
+ *   topk_idx, inv_row, dz: device [T, K]; dz_row device [P_max]
+ *   seg_offset, row_token: from moe_permute
+ *   du, du_t       device [T, d] out, MOE_F32 or MOE_BF16
+ *   de             device [Nr, d] fp32 out (overwritten)
+ *   Errors: MOE_EINVAL for NULL pointers, bad sizes, d % 8 != 0.
+ * ---------------------------------------------------------------------- */
+moe_status moe_route_backward(const void* grad_out, moe_dtype g_t, const void* dx,
+                              const void* u, moe_dtype u_t, const float* centroids,
+                              const int32_t* topk_idx, const int32_t* inv_row,
+                              const float* dz, const float* dz_row,
+                              const int32_t* seg_offset, const int32_t* row_token,
+                              int T, int d, int K, int Nr, int Ns,
+                              void* du, moe_dtype du_t, float* de, void* stream);
 
 #ifdef __cplusplus
 }

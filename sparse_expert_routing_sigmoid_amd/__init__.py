@@ -1,4 +1,4 @@
-"""Python binding of libmoe_mi355x (DeepSeekMoE layer forward on MI355X).
+"""Python binding of libmoe_mi355x (DeepSeekMoE layer forward and backward on MI355X).
 
 Argument marshalling only: every step of the layer runs in the library's HIP
 kernels.  Tensors are torch tensors on the current HIP device; their data
@@ -44,6 +44,12 @@ SIGNATURES = {
     "moe_combine": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _u, _vp, _i, _vp]),
     "moe_bias_update": (_i, [_vp, _i, _ll, _f, _vp, _vp]),
     "fp8_quantize_tiles": (_i, [_vp, _i, _ll, _ll, _i, _i, _vp, _vp, _vp]),
+    "moe_gemm_train_workspace_bytes": (_sz, [_i] * 7),
+    "moe_expert_gemm_train": (_i, [_vp] * 3 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
+    "moe_combine_backward": (_i, [_vp, _i, _vp, _i] + [_vp] * 4 + [_i] * 5 + [_vp] * 5),
+    "moe_gemm_backward_workspace_bytes": (_sz, [_i] * 7),
+    "moe_expert_gemm_backward": (_i, [_vp] * 6 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
+    "moe_route_backward": (_i, [_vp, _i, _vp, _vp, _i] + [_vp] * 7 + [_i] * 5 + [_vp, _i, _vp, _vp]),
 }
 
 _lib = None
@@ -127,6 +133,18 @@ def moe_gemm_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t):
     return lib().moe_gemm_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t)
 
 
+def moe_gemm_train_workspace_bytes(T, K, Nr, Ns, d, I, tile_m):
+    return lib().moe_gemm_train_workspace_bytes(T, K, Nr, Ns, d, I, tile_m)
+
+
+def moe_gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tile_m):
+    return lib().moe_gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tile_m)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
 # ------------------------------------------------------------ entry points --
 def moe_route(u, centroids, bias, K, topk_idx, topk_gate, topk_score, expert_load, ws, stream=None):
     T, d = u.shape
@@ -151,6 +169,40 @@ def moe_expert_gemm(x, x_scale, w_t, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns,
                                  _ptr(tile_map), _ptr(n_tiles), _ptr(ws),
                                  ws.numel() * ws.element_size() if ws is not None else 0,
                                  _ptr(y), dtype_code(y), _stream(stream)))
+
+
+def moe_expert_gemm_train(x, w13, w2, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token, tile_map, n_tiles,
+                          ws, h, ab, y, stream=None):
+    _check(lib().moe_expert_gemm_train(_ptr(x), _ptr(w13), _ptr(w2), T, K, Nr, Ns, d, I, tile_m, _ptr(seg_offset),
+                                       _ptr(row_token), _ptr(tile_map), _ptr(n_tiles), _ptr(ws), _nbytes(ws),
+                                       _ptr(h), _ptr(ab), _ptr(y), dtype_code(y), _stream(stream)))
+
+
+def moe_combine_backward(grad_out, y, inv_row, topk_gate, topk_score, seg_offset, Nr, Ns, dy, dgate, dz, dz_row,
+                         stream=None):
+    T, d = grad_out.shape
+    K = inv_row.shape[1]
+    _check(lib().moe_combine_backward(_ptr(grad_out), dtype_code(grad_out), _ptr(y), dtype_code(y), _ptr(inv_row),
+                                      _ptr(topk_gate), _ptr(topk_score), _ptr(seg_offset), T, d, K, Nr, Ns, _ptr(dy),
+                                      _ptr(dgate), _ptr(dz), _ptr(dz_row), _stream(stream)))
+
+
+def moe_expert_gemm_backward(x, w13, w2, h, ab, dy, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token, tile_map,
+                             n_tiles, ws, dx, dw13, dw2, stream=None):
+    _check(lib().moe_expert_gemm_backward(_ptr(x), _ptr(w13), _ptr(w2), _ptr(h), _ptr(ab), _ptr(dy), T, K, Nr, Ns,
+                                          d, I, tile_m, _ptr(seg_offset), _ptr(row_token), _ptr(tile_map),
+                                          _ptr(n_tiles), _ptr(ws), _nbytes(ws), _ptr(dx), _ptr(dw13), _ptr(dw2),
+                                          dtype_code(dw13), _stream(stream)))
+
+
+def moe_route_backward(grad_out, dx, u, centroids, topk_idx, inv_row, dz, dz_row, seg_offset, row_token, Nr, Ns,
+                       du, de, stream=None):
+    T, d = u.shape
+    K = topk_idx.shape[1]
+    _check(lib().moe_route_backward(_ptr(grad_out), dtype_code(grad_out), _ptr(dx), _ptr(u), dtype_code(u),
+                                    _ptr(centroids), _ptr(topk_idx), _ptr(inv_row), _ptr(dz), _ptr(dz_row),
+                                    _ptr(seg_offset), _ptr(row_token), T, d, K, Nr, Ns, _ptr(du), dtype_code(du),
+                                    _ptr(de), _stream(stream)))
 
 
 def moe_combine(u, y, inv_row, topk_gate, seg_offset, Nr, Ns, out, flags=0, stream=None):
@@ -208,7 +260,7 @@ class MoeLayer:
     synchronisation happens inside forward()."""
 
     def __init__(self, T, d, Nr, Ns, I, K, act_dtype, weights: ExpertWeights, x_fp8=False,
-                 tile_m=32, out_dtype=None, device="cuda"):
+                 tile_m=32, out_dtype=None, device="cuda", train=False, grad_dtype=None):
         self.T, self.d, self.Nr, self.Ns, self.I, self.K = T, d, Nr, Ns, I, K
         self.tile_m, self.x_fp8, self.w = tile_m, x_fp8, weights
         dev = torch.device(device)
@@ -239,6 +291,30 @@ class MoeLayer:
         out_dtype = act_dtype if out_dtype is None else out_dtype
         self.y = torch.empty((P, d), dtype=out_dtype, device=dev)
         self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
+        self.train = train
+        if train:
+            # the training forward keeps h and the pre-activations [a | b]
+            # for the backward (bf16 path only)
+            if x_fp8 or weights.w_t != MOE_BF16 or act_dtype != torch.bfloat16:
+                raise ValueError("training needs bf16 activations and weights")
+            bf16 = dict(dtype=torch.bfloat16, device=dev)
+            E = Nr + Ns
+            self.h = torch.empty((P, I), **bf16)
+            self.ab = torch.empty((P, 2 * I), **bf16)
+            self.train_ws = torch.empty((max(moe_gemm_train_workspace_bytes(T, K, Nr, Ns, d, I, tile_m), 1),),
+                                        dtype=torch.uint8, device=dev)
+            gd = weights.w13.dtype if grad_dtype is None else grad_dtype
+            self.dy = torch.empty((P, d), **bf16)
+            self.dx = torch.empty((P, d), **bf16)
+            self.dgate = torch.empty((T, K), **f32)
+            self.dz = torch.empty((T, K), **f32)
+            self.dz_row = torch.empty((P,), **f32)
+            self.bwd_ws = torch.empty((max(moe_gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tile_m), 1),),
+                                      dtype=torch.uint8, device=dev)
+            self.dw13 = torch.empty((E, 2 * I, d), dtype=gd, device=dev)
+            self.dw2 = torch.empty((E, d, I), dtype=gd, device=dev)
+            self.du = torch.empty((T, d), dtype=act_dtype, device=dev)
+            self.de = torch.empty((Nr, d), **f32)
 
     def route(self, u, centroids, bias, stream=None):
         moe_route(u, centroids, bias, self.K, self.topk_idx, self.topk_gate, self.topk_score, self.expert_load,
@@ -255,6 +331,11 @@ class MoeLayer:
             x, xs = self.xq, self.xs
         else:
             x, xs = u, None
+        if self.train:
+            moe_expert_gemm_train(u, w.w13, w.w2, self.T, self.K, self.Nr, self.Ns, self.d, self.I, self.tile_m,
+                                  self.seg_offset, self.row_token, self.tile_map, self.n_tiles, self.train_ws,
+                                  self.h, self.ab, self.y, stream)
+            return
         moe_expert_gemm(x, xs, w.w_t, w.w13, w.w13_scale, w.w2, w.w2_scale, self.T, self.K, self.Nr, self.Ns,
                         self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map, self.n_tiles,
                         self.gemm_ws, self.y, x_t=self.x_t, stream=stream)
@@ -269,6 +350,21 @@ class MoeLayer:
         self.permute(stream)
         self.experts(u, stream)
         return self.combine(u, stream=stream)
+
+    def backward(self, grad_out, u, centroids, stream=None):
+        """Gradients of the last training forward for dL/dh' = grad_out:
+        returns (du, de, dW13, dW2); the bias gets none."""
+        if not self.train:
+            raise RuntimeError("backward needs a layer built with train=True")
+        w = self.w
+        moe_combine_backward(grad_out, self.y, self.inv_row, self.topk_gate, self.topk_score, self.seg_offset,
+                             self.Nr, self.Ns, self.dy, self.dgate, self.dz, self.dz_row, stream)
+        moe_expert_gemm_backward(u, w.w13, w.w2, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns, self.d,
+                                 self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map, self.n_tiles,
+                                 self.bwd_ws, self.dx, self.dw13, self.dw2, stream)
+        moe_route_backward(grad_out, self.dx, u, centroids, self.topk_idx, self.inv_row, self.dz, self.dz_row,
+                           self.seg_offset, self.row_token, self.Nr, self.Ns, self.du, self.de, stream)
+        return self.du, self.de, self.dw13, self.dw2
 
     def update_bias(self, bias, gamma=0.001, stream=None):
         moe_bias_update(self.expert_load, self.T * self.K, gamma, bias, stream)

@@ -30,6 +30,26 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
                        const int32_t* tile_map, const int32_t* n_tiles, void* ws, size_t ws_bytes, void* y,
                        moe_dtype y_t, void* stream);
 
+size_t gemm_train_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status expert_gemm_train(const void* x, const void* w13, const void* w2, int T, int K, int Nr, int Ns, int d,
+                             int I, int tile_m, const int32_t* seg_offset, const int32_t* row_token,
+                             const int32_t* tile_map, const int32_t* n_tiles, void* ws, size_t ws_bytes, void* h,
+                             void* ab, void* y, moe_dtype y_t, void* stream);
+moe_status combine_backward(const void* grad_out, moe_dtype g_t, const void* y, moe_dtype y_t,
+                            const int32_t* inv_row, const float* topk_gate, const float* topk_score,
+                            const int32_t* seg_offset, int T, int d, int K, int Nr, int Ns, void* dy, float* dgate,
+                            float* dz, float* dz_row, void* stream);
+size_t gemm_backward_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status expert_gemm_backward(const void* x, const void* w13, const void* w2, const void* h, const void* ab,
+                                const void* dy, int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                const int32_t* seg_offset, const int32_t* row_token, const int32_t* tile_map,
+                                const int32_t* n_tiles, void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2,
+                                moe_dtype dw_t, void* stream);
+moe_status route_backward(const void* grad_out, moe_dtype g_t, const void* dx, const void* u, moe_dtype u_t,
+                          const float* centroids, const int32_t* topk_idx, const int32_t* inv_row, const float* dz,
+                          const float* dz_row, const int32_t* seg_offset, const int32_t* row_token, int T, int d,
+                          int K, int Nr, int Ns, void* du, moe_dtype du_t, float* de, void* stream);
+
 namespace {
 thread_local std::string g_last_error;
 }
@@ -123,6 +143,52 @@ moe_status fp8_quantize_tiles(const void* x, moe_dtype x_t, long long rows, long
                               int tile_cols, uint8_t* q, float* scale, void* stream) {
   moe::clear_error();
   return moe::quantize_tiles(x, x_t, rows, cols, tile_rows, tile_cols, q, scale, stream);
+}
+
+size_t moe_gemm_train_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  return moe::gemm_train_workspace_bytes(T, K, Nr, Ns, d, I, tile_m);
+}
+
+moe_status moe_expert_gemm_train(const void* x, const void* w13, const void* w2, int T, int K, int Nr, int Ns, int d,
+                                 int I, int tile_m, const int32_t* seg_offset, const int32_t* row_token,
+                                 const int32_t* tile_map, const int32_t* n_tiles, void* ws, size_t ws_bytes, void* h,
+                                 void* ab, void* y, moe_dtype y_t, void* stream) {
+  moe::clear_error();
+  return moe::expert_gemm_train(x, w13, w2, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token, tile_map, n_tiles, ws,
+                                ws_bytes, h, ab, y, y_t, stream);
+}
+
+moe_status moe_combine_backward(const void* grad_out, moe_dtype g_t, const void* y, moe_dtype y_t,
+                                const int32_t* inv_row, const float* topk_gate, const float* topk_score,
+                                const int32_t* seg_offset, int T, int d, int K, int Nr, int Ns, void* dy,
+                                float* dgate, float* dz, float* dz_row, void* stream) {
+  moe::clear_error();
+  return moe::combine_backward(grad_out, g_t, y, y_t, inv_row, topk_gate, topk_score, seg_offset, T, d, K, Nr, Ns,
+                               dy, dgate, dz, dz_row, stream);
+}
+
+size_t moe_gemm_backward_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  return moe::gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tile_m);
+}
+
+moe_status moe_expert_gemm_backward(const void* x, const void* w13, const void* w2, const void* h, const void* ab,
+                                    const void* dy, int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                    const int32_t* seg_offset, const int32_t* row_token, const int32_t* tile_map,
+                                    const int32_t* n_tiles, void* ws, size_t ws_bytes, void* dx, void* dw13,
+                                    void* dw2, moe_dtype dw_t, void* stream) {
+  moe::clear_error();
+  return moe::expert_gemm_backward(x, w13, w2, h, ab, dy, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token, tile_map,
+                                   n_tiles, ws, ws_bytes, dx, dw13, dw2, dw_t, stream);
+}
+
+moe_status moe_route_backward(const void* grad_out, moe_dtype g_t, const void* dx, const void* u, moe_dtype u_t,
+                              const float* centroids, const int32_t* topk_idx, const int32_t* inv_row,
+                              const float* dz, const float* dz_row, const int32_t* seg_offset,
+                              const int32_t* row_token, int T, int d, int K, int Nr, int Ns, void* du,
+                              moe_dtype du_t, float* de, void* stream) {
+  moe::clear_error();
+  return moe::route_backward(grad_out, g_t, dx, u, u_t, centroids, topk_idx, inv_row, dz, dz_row, seg_offset,
+                             row_token, T, d, K, Nr, Ns, du, du_t, de, stream);
 }
 
 }  // extern "C"

@@ -15,7 +15,8 @@ size_t ffn_schedule_bytes(long long tiles_cap, int ntA, int ntB);
 int ffn_schedule_max_tiles();
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                                 const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
-                                int Nr, int cap, uint16_t* h, void* y, bool y_f32, int* sched, hipStream_t st);
+                                int Nr, int cap, uint16_t* h, uint16_t* ab, void* y, bool y_f32, int* sched,
+                                hipStream_t st);
 bool ffn_fp8_persistent_ok(int d, int I);
 void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
@@ -114,8 +115,8 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
           (unsigned long long)P * I * 2 < (1ull << 31) && (unsigned long long)3 * I * d * 2 < (1ull << 31))
         launch_ffn_bf16_persistent(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
                                    static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, T, (long long)P, d,
-                                   I, Nr, tiles_max, reinterpret_cast<uint16_t*>(ws_h), y, y_t == MOE_F32, ws_sched,
-                                   st);
+                                   I, Nr, tiles_max, reinterpret_cast<uint16_t*>(ws_h), nullptr, y, y_t == MOE_F32,
+                                   ws_sched, st);
       else
         launch_ffn_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w13),
                         static_cast<const uint16_t*>(w2), row_token, tile_map, n_tiles, tiles_max, d, I,

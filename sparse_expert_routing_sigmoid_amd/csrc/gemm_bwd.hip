@@ -1,0 +1,484 @@
+// Backward of the grouped SwiGLU expert GEMMs on MFMA (gfx950, bf16).
+//
+// The forward (expert FFNs of the combine equation, "DeepSeek-V3 Technical
+// Report" reading guide, Method section 2, in SwiGLU form) computes per row
+// [a | b] = x W13^T, h = SiLU(a) * b, y = h W2^T.  Its gradients, by the
+// chain rule, given dy (the gradient reaching y, gate already applied):
+//   dh = dy W2                              (dgrad, down)   K = d,  N = I
+//   da = dh * b * SiLU'(a),  db = dh * SiLU(a)  (fused into the dgrad epilogue)
+//   dx = [da | db] W13                      (dgrad, gate/up) K = 2I, N = d
+//   dW2_e  = dy_e^T h_e                     (wgrad, down)   M = d,  N = I, K = rows of e
+//   dW13_e = [da | db]_e^T x_e              (wgrad, gate/up) M = 2I, N = d, K = rows of e
+//
+// The forward multiplies row-major operands that are contiguous along K on
+// both sides.  Here one (dgrad) or both (wgrad) operands are contiguous along
+// M or N instead.  Such an operand is staged in LDS as it lies in memory
+// (64 K-rows of 256 values per stage) and read into MFMA fragments with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane j names the 8 bytes (4 values along M/N) at K-row j / 4 and
+// column 4 (j % 4), and lane i receives column i of the four K-rows.  Two such
+// reads give a lane the 8 consecutive K values of its column that
+// v_mfma_f32_32x32x16_bf16 takes, so no operand is ever transposed in memory.
+//
+// Block tile 256 x 256 x 64 (K per stage), 4 waves in 2 x 2, each wave
+// 128 x 128 as 4 x 4 MFMA tiles of 32x32, fp32 accumulators; operands go
+// global -> LDS by the direct 16-byte buffer-to-LDS load, two stages.  LDS
+// tiles are XOR-swizzled at 16-byte granularity so that fragment reads hit
+// distinct banks: K-contiguous tiles as in the forward, M/N-contiguous tiles
+// with chunk ^= 2 * (K-row & 3), which spreads the four K-rows of one
+// transposing read over the 128 bytes of one bank cycle.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+
+constexpr int BT = 256;        // tile rows (M) and columns (N)
+constexpr int BKS = 64;        // K values per stage
+constexpr int BOP = 32768;     // bytes of one operand per stage
+constexpr int BTHREADS = 256;
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer: the load writes zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Lane l writes LDS bytes [16 l, 16 l + 16) of the 1 KB block at `lds`.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Row (within the 32 x 32 MFMA tile) of accumulator element e of a lane.
+__device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+// K-contiguous tile (256 rows x 128 bytes): fragment of rows r0 .. r0 + 31
+// (r0 % 32 == 0) for k-step kk (16 K values): lane l gets row r0 + l % 32,
+// K values 8 (l / 32) .. + 7 of the step.
+__device__ __forceinline__ bf16x8_t frag_kc(const uint8_t* t, int r0, int kk, int lane) {
+  const int c = kk * 2 + (lane >> 5);
+  const int sw = (lane & 7) ^ ((lane >> 3) & 1);
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(t + (r0 + (lane & 31)) * 128 + ((c ^ sw) << 4)));
+}
+
+// M/N-contiguous tile (64 K-rows x 512 bytes): the same fragment shape (column
+// c0 + l % 32, K values 8 (l / 32) .. + 7 of k-step kk) by two transposing
+// reads of four K-rows each.  In a group of 16 lanes, lane j names K-row
+// kk * 16 + 8 (group / 2) + j / 4 (+ 4 for the second read) and columns
+// c0 + 16 (group % 2) + 4 (j % 4) .. + 3, i.e. logical chunk c0 / 8 + x with
+// x = 2 (group % 2) + (j % 4) / 2, stored at chunk (c0 / 8 + x) ^ 2 (j / 4).
+// With c0 = 128 wm + 32 i that address splits into a lane part that depends
+// only on i % 2 (MncLane) and a constant, so the reads take immediate offsets.
+struct MncLane {
+  int base[2];  // byte address of the lane's first read for i % 2 == 0, 1 (wm folded in)
+  __device__ void init(int wmn, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int kr = 8 * (g >> 1) + (j >> 2);
+    const int z = (2 * (g & 1) + ((j & 3) >> 1)) ^ (2 * (j >> 2));
+    const int b = kr * 512 + wmn * 256 + (j & 1) * 8;
+    base[0] = b + (z << 4);
+    base[1] = b + ((z ^ 4) << 4);
+  }
+};
+
+template <int I, int KK>
+__device__ __forceinline__ bf16x8_t frag_mnc(const uint8_t* t, const MncLane& ml) {
+  constexpr int c = KK * 8192 + (I >> 1) * 128;
+  const uint8_t* p = t + ml.base[I & 1] + c;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 512));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// ---------------------------------------------------------- operand loads --
+// Instruction j (0..7) of wave w fills the 1 KB block g = 8 w + j of an
+// operand's 32 KB stage buffer.
+
+// K-contiguous rows: block g holds tile rows 8 g .. 8 g + 7, lane l row
+// 8 g + l / 8, physical chunk l % 8, which holds logical chunk
+// (l % 8) ^ (row % 8) ^ ((row / 8) % 2); rows past `rows` load zeros.
+struct KcRows {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off[8];
+  __device__ void init(const void* base, uint32_t bytes, long long row0, int rows, uint32_t row_bytes, int wave,
+                       int lane) {
+    r = rsrc(base, bytes);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tr = (wave * 8 + j) * 8 + (lane >> 3);
+      const uint32_t c16 = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (j & 1)) * 16u;
+      off[j] = tr < rows ? (uint32_t)(row0 + tr) * row_bytes + c16 : OOB;
+    }
+  }
+  __device__ void issue(uint8_t* st, int wave, int s, uint32_t oob) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(r, st + (wave * 8 + j) * 1024, off[j] | oob, (uint32_t)s * 128u);
+  }
+};
+
+// M/N-contiguous, K-rows consecutive from the start of the matrix (a weight
+// matrix [K, N] of one expert): block g holds K-rows 2 g, 2 g + 1, lane l
+// K-row 2 g + l / 32, physical chunk l % 32 = logical chunk ^ 2 (K-row % 4).
+struct MncRows {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off[8];
+  uint32_t kstride;  // bytes per stage (64 K-rows)
+  __device__ void init(const void* base, uint32_t bytes, uint32_t row_bytes, int col0, int wave, int lane) {
+    r = rsrc(base, bytes);
+    kstride = row_bytes * BKS;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kr = 2 * (wave * 8 + j) + (lane >> 5);
+      const uint32_t c = (uint32_t)((lane & 31) ^ (2 * (kr & 3)));
+      off[j] = (uint32_t)kr * row_bytes + (uint32_t)col0 * 2u + c * 16u;
+    }
+  }
+  __device__ void issue(uint8_t* st, int wave, int s, uint32_t oob) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(r, st + (wave * 8 + j) * 1024, off[j] | oob, (uint32_t)s * kstride);
+  }
+};
+
+// The K-rows of one segment of the permuted layout (rows seg0 .. seg0 +
+// seglen - 1), for both operands of a weight gradient.  A K-row is live if it
+// lies in the segment and holds a token (row_token >= 0); dead K-rows load
+// zeros on both sides.  Operand A reads permuted row seg0 + k; operand B the
+// same row, or (GATHER) the token's row of x.  The tokens of the next stage
+// are fetched one stage ahead.
+template <bool GATHER>
+struct SegRows {
+  __amdgpu_buffer_rsrc_t ra, rb, rt;  // A, B, row_token
+  int seg0, seglen;
+  uint32_t a_rb, b_rb, a_c, b_c;  // row bytes and tile column byte offsets
+  int tok[8];
+  __device__ void fetch(int s, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = s * BKS + 2 * (wave * 8 + j) + (lane >> 5);
+      const int v = __builtin_amdgcn_raw_buffer_load_b32(rt, k < seglen ? (uint32_t)(seg0 + k) * 4u : OOB, 0, 0);
+      tok[j] = k < seglen ? v : -1;
+    }
+  }
+  __device__ void issue(uint8_t* sa, uint8_t* sb, int wave, int lane, int s, bool live) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kr = 2 * (wave * 8 + j) + (lane >> 5);
+      const uint32_t c16 = (uint32_t)((lane & 31) ^ (2 * (kr & 3))) * 16u;
+      const int row = seg0 + s * BKS + kr;
+      const bool ok = live && tok[j] >= 0;
+      const uint32_t oa = ok ? (uint32_t)row * a_rb + a_c + c16 : OOB;
+      const uint32_t ob = ok ? (uint32_t)(GATHER ? tok[j] : row) * b_rb + b_c + c16 : OOB;
+      dma16(ra, sa + (wave * 8 + j) * 1024, oa, 0);
+      dma16(rb, sb + (wave * 8 + j) * 1024, ob, 0);
+    }
+  }
+};
+
+// ------------------------------------------------------------ the K loop --
+// Fragments of k-step KK for a wave at (wm, wn): A from the A stage, B from
+// the B stage, each K-contiguous (KC) or M/N-contiguous (ml* give the lane
+// addresses of the latter).
+template <bool A_KC, bool B_KC, int KK>
+__device__ __forceinline__ void load_frags(bf16x8_t (&af)[4], bf16x8_t (&bf)[4], const uint8_t* sa,
+                                           const uint8_t* sb, const MncLane& mla, const MncLane& mlb, int wm,
+                                           int wn, int lane) {
+  if constexpr (A_KC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = frag_kc(sa, wm * 128 + i * 32, KK, lane);
+  } else {
+    af[0] = frag_mnc<0, KK>(sa, mla);
+    af[1] = frag_mnc<1, KK>(sa, mla);
+    af[2] = frag_mnc<2, KK>(sa, mla);
+    af[3] = frag_mnc<3, KK>(sa, mla);
+  }
+  if constexpr (B_KC) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = frag_kc(sb, wn * 128 + j * 32, KK, lane);
+  } else {
+    bf[0] = frag_mnc<0, KK>(sb, mlb);
+    bf[1] = frag_mnc<1, KK>(sb, mlb);
+    bf[2] = frag_mnc<2, KK>(sb, mlb);
+    bf[3] = frag_mnc<3, KK>(sb, mlb);
+  }
+}
+
+template <int KK>
+__device__ __forceinline__ void mma16(f32x16_t (&acc)[4][4], const bf16x8_t (&af)[4], const bf16x8_t (&bf)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+// The four k-steps of one stage, fragments double-buffered.
+template <bool A_KC, bool B_KC>
+__device__ __forceinline__ void mma_stage(f32x16_t (&acc)[4][4], const uint8_t* __restrict__ sa,
+                                          const uint8_t* __restrict__ sb, const MncLane& mla, const MncLane& mlb,
+                                          int wm, int wn, int lane) {
+  bf16x8_t f0[4], g0[4], f1[4], g1[4];
+  load_frags<A_KC, B_KC, 0>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
+  load_frags<A_KC, B_KC, 1>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
+  mma16<0>(acc, f0, g0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<A_KC, B_KC, 2>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
+  mma16<1>(acc, f1, g1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<A_KC, B_KC, 3>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
+  mma16<2>(acc, f0, g0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma16<3>(acc, f1, g1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+}
+
+__device__ __forceinline__ float acc_get(const f32x16_t& a, int e) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a[e]));
+  return v;
+}
+
+__device__ __forceinline__ void put(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+__device__ __forceinline__ void put(float* p, float v) { *p = v; }
+
+// ------------------------------------------------------------- dgrad --
+// Items (row tile, N tile) of the tile map, dealt to the XCDs in contiguous
+// runs (block b runs on XCD b % 8): XCD x takes items [x q, x q + q) of the
+// item list ordered tile-major, so the row tiles of one expert, and the
+// weight slabs they share, stay in one L2.
+//
+// SWIGLU: A = dy [P, d] (K = d), W = W2 [E, d, I] (K-rows d, N = I); the
+//         epilogue turns dh into [da | db] with the saved [a | b] of the
+//         forward and writes dab [P, 2I] (bf16).
+// else:   A = dab [P, 2I] (K = 2I), W = W13 [E, 2I, d] (N = d); out = dx [P, d].
+template <bool SWIGLU, typename OT>
+__global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
+                                                    const int32_t* __restrict__ tile_map,
+                                                    const int32_t* __restrict__ n_tiles, int Kd, int Nd,
+                                                    uint32_t a_bytes, const uint16_t* __restrict__ ab,
+                                                    OT* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntn = (Nd + BT - 1) / BT;
+  const long long items = (long long)(*n_tiles) * ntn;
+  const long long q = (items + 7) / 8;
+  const long long slot = blockIdx.x >> 3;
+  if (slot >= q) return;
+  const long long item = (blockIdx.x & 7) * q + slot;
+  if (item >= items) return;
+  const int tile = (int)(item / ntn), n = (int)(item % ntn);
+  const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * tile);
+  const int seg = tm.x, row0 = tm.y, rows = tm.w;
+  const int w_wave = __builtin_amdgcn_readfirstlane(wave);
+
+  KcRows A;
+  A.init(a, a_bytes, row0, rows, (uint32_t)Kd * 2u, w_wave, lane);
+  MncRows B;
+  const long long w_expert = (long long)Kd * Nd * 2;
+  B.init(w + (long long)seg * Kd * Nd, (uint32_t)w_expert, (uint32_t)Nd * 2u, n * BT, w_wave, lane);
+
+  MncLane mlb;
+  mlb.init(wn, lane);
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+  // Kd % 128 == 0, so the stage count is even and the loop body, two stages
+  // that name their buffers, has no branch: a branch lets the compiler sink
+  // MFMAs past the next barrier and costs registers.  The final issue loads
+  // zeros (out of range) into a buffer nobody reads.
+  const int nk = Kd / BKS;
+  A.issue(st0, w_wave, 0, 0u);
+  B.issue(st0 + BOP, w_wave, 0, 0u);
+  for (int s = 0; s < nk; s += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    A.issue(st1, w_wave, s + 1, 0u);
+    B.issue(st1 + BOP, w_wave, s + 1, 0u);
+    mma_stage<true, false>(acc, st0, st0 + BOP, mlb, mlb, wm, wn, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t oob = s + 2 < nk ? 0u : OOB;
+    A.issue(st0, w_wave, s + 2, oob);
+    B.issue(st0 + BOP, w_wave, s + 2, oob);
+    mma_stage<true, false>(acc, st1, st1 + BOP, mlb, mlb, wm, wn, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue, straight from the accumulators: column c of the tile is
+  // output column n * 256 + c; rows past the tile's token rows and columns
+  // past Nd are not written.
+  const int lcol = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = wm * 128 + i * 32 + acc_row(e, lane);
+      if (r >= rows) continue;
+      const long long orow = (long long)row0 + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n * BT + wn * 128 + j * 32 + lcol;
+        if (col >= Nd) continue;
+        const float g = acc_get(acc[i][j], e);
+        if constexpr (SWIGLU) {
+          // da = dh * b * SiLU'(a), db = dh * SiLU(a); SiLU'(a) = sg (1 + a (1 - sg))
+          const float av = bf16_to_f32(ab[orow * 2 * Nd + col]);
+          const float bv = bf16_to_f32(ab[orow * 2 * Nd + Nd + col]);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(av * -1.4426950408889634f));
+          put(out + orow * 2 * Nd + col, g * bv * sg * (1.0f + av * (1.0f - sg)));
+          put(out + orow * 2 * Nd + Nd + col, g * av * sg);
+        } else {
+          put(out + orow * Nd + col, g);
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------- wgrad --
+// dW_e [M, N] = A_e^T B_e over the K-rows of segment e.  Items (expert, M
+// tile, N tile), the shared experts first (their segments are the longest),
+// dealt to the blocks in order (block b runs on XCD b % 8).
+// DOWN:  A = dy [P, d] (M = d), B = h [P, I] (N = I)   -> dW2 [E, d, I]
+// !DOWN: A = dab [P, 2I] (M = 2I), B = x [T, d] gathered by row_token (N = d)
+//        -> dW13 [E, 2I, d]
+template <bool GATHER, typename OT>
+__global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+                                                    const int32_t* __restrict__ seg_offset,
+                                                    const int32_t* __restrict__ row_token, int P_rows, int E, int Nr,
+                                                    int Md, int Nd, uint32_t a_bytes, uint32_t b_bytes,
+                                                    OT* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntm = (Md + BT - 1) / BT, ntn = (Nd + BT - 1) / BT;
+  const int per_e = ntm * ntn;
+  const int item = blockIdx.x;
+  if (item >= E * per_e) return;
+  const int eo = item / per_e, rem = item % per_e;
+  const int e = eo < E - Nr ? Nr + eo : eo - (E - Nr);  // shared experts first
+  const int m = rem / ntn, n = rem % ntn;
+  const int w_wave = __builtin_amdgcn_readfirstlane(wave);
+
+  SegRows<GATHER> S;
+  S.ra = rsrc(a, a_bytes);
+  S.rb = rsrc(b, b_bytes);
+  S.rt = rsrc(row_token, (uint32_t)P_rows * 4u);
+  S.seg0 = seg_offset[e];
+  S.seglen = seg_offset[e + 1] - S.seg0;
+  S.a_rb = (uint32_t)Md * 2u;
+  S.b_rb = (uint32_t)Nd * 2u;
+  S.a_c = (uint32_t)m * BT * 2u;
+  S.b_c = (uint32_t)n * BT * 2u;
+
+  MncLane mla, mlb;
+  mla.init(wm, lane);
+  mlb.init(wn, lane);
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+  // Stages rounded up to an even count (the extra stage loads zeros), so the
+  // two-stage loop body has no branch.
+  const int nk = (S.seglen + 2 * BKS - 1) / (2 * BKS) * 2;
+  if (nk > 0) {
+    S.fetch(0, w_wave, lane);
+    S.issue(st0, st0 + BOP, w_wave, lane, 0, true);
+    S.fetch(1, w_wave, lane);
+    for (int s = 0; s < nk; s += 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      S.issue(st1, st1 + BOP, w_wave, lane, s + 1, true);
+      S.fetch(s + 2, w_wave, lane);
+      mma_stage<false, false>(acc, st0, st0 + BOP, mla, mlb, wm, wn, lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      S.issue(st0, st0 + BOP, w_wave, lane, s + 2, s + 2 < nk);
+      S.fetch(s + 3, w_wave, lane);
+      mma_stage<false, false>(acc, st1, st1 + BOP, mla, mlb, wm, wn, lane);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  OT* ob = out + (long long)e * Md * Nd;
+  const int lcol = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int el = 0; el < 16; ++el) {
+      const int r = m * BT + wm * 128 + i * 32 + acc_row(el, lane);
+      if (r >= Md) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n * BT + wn * 128 + j * 32 + lcol;
+        if (col < Nd) put(ob + (long long)r * Nd + col, acc_get(acc[i][j], el));
+      }
+    }
+}
+
+}  // namespace
+
+// d % 256 and I % 128: full M tiles, even stage counts (Kd % 128 == 0).
+bool ffn_bwd_ok(int d, int I) { return d % 256 == 0 && I % 128 == 0; }
+
+// dy [P, d], ab [P, 2I], h [P, I] (bf16, the forward's), x [T, d]; dab is
+// scratch [P, 2I]; dx [P, d] bf16; dW13 [E, 2I, d], dW2 [E, d, I] in dw_f32 ?
+// fp32 : bf16.
+void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const uint16_t* h,
+                         const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset, const int32_t* row_token,
+                         const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d,
+                         int I, int Nr, int Ns, uint16_t* dab, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                         hipStream_t st) {
+  const int E = Nr + Ns;
+  const uint32_t dy_bytes = (uint32_t)(P * d * 2), dab_bytes = (uint32_t)(P * 2 * I * 2);
+  const uint32_t h_bytes = (uint32_t)(P * I * 2), x_bytes = (uint32_t)((long long)T * d * 2);
+  // dgrad, down + SwiGLU: N = I
+  {
+    const long long items = (long long)tiles_max * ((I + BT - 1) / BT);
+    const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
+    hipLaunchKernelGGL((k_dgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, w2, tile_map, n_tiles, d, I,
+                       dy_bytes, ab, dab);
+  }
+  // dgrad, gate/up: N = d
+  {
+    const long long items = (long long)tiles_max * (d / BT);
+    const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
+    hipLaunchKernelGGL((k_dgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, w13, tile_map, n_tiles,
+                       2 * I, d, dab_bytes, nullptr, dx);
+  }
+  // wgrad, down: dW2 [E, d, I]
+  {
+    const unsigned grid = (unsigned)(E * (d / BT) * ((I + BT - 1) / BT));
+    if (dw_f32)
+      hipLaunchKernelGGL((k_wgrad<false, float>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token, (int)P, E,
+                         Nr, d, I, dy_bytes, h_bytes, static_cast<float*>(dw2));
+    else
+      hipLaunchKernelGGL((k_wgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
+                         (int)P, E, Nr, d, I, dy_bytes, h_bytes, static_cast<uint16_t*>(dw2));
+  }
+  // wgrad, gate/up: dW13 [E, 2I, d]
+  {
+    const unsigned grid = (unsigned)(E * (2 * I / BT) * (d / BT));
+    if (dw_f32)
+      hipLaunchKernelGGL((k_wgrad<true, float>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token, (int)P, E,
+                         Nr, 2 * I, d, dab_bytes, x_bytes, static_cast<float*>(dw13));
+    else
+      hipLaunchKernelGGL((k_wgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
+                         (int)P, E, Nr, 2 * I, d, dab_bytes, x_bytes, static_cast<uint16_t*>(dw13));
+  }
+}
+
+}  // namespace moe

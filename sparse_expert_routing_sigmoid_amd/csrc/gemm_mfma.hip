@@ -259,7 +259,7 @@ __device__ __forceinline__ float absmax8(float4 a, float4 b) {
 template <bool PHASE_A, bool H_FP8, int MT, int MA, typename OT>
 __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Item& it, uint8_t* st0, uint8_t* st1,
                                          int wm, int wn, int tid, OT* __restrict__ out, float* __restrict__ out_scale,
-                                         int Nd, int n) {
+                                         uint16_t* __restrict__ ab, int Nd, int n) {
   constexpr int NC = PHASE_A ? P_TN / 2 : P_TN;  // output columns of the tile
   constexpr int LSTR = P_TN * 4;
   const int lcol = it.lane & 31;
@@ -316,6 +316,11 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
       if (PHASE_A) {  // h = SiLU(gate) * up
         const float4 u0 = *reinterpret_cast<const float4*>(er + 512 + ch * 32);
         const float4 u1 = *reinterpret_cast<const float4*>(er + 512 + ch * 32 + 16);
+        if (!H_FP8 && ab) {  // training: keep the pre-activations [a | b] for the backward pass
+          uint16_t* abr = ab + (it.row0 + pass * 128 + r) * 2LL * Nd + col0 + ch * 8;
+          store8(abr, v0, v1);
+          store8(abr + Nd, u0, u1);
+        }
         v0 = make_float4(silu(v0.x) * u0.x, silu(v0.y) * u0.y, silu(v0.z) * u0.z, silu(v0.w) * u0.w);
         v1 = make_float4(silu(v1.x) * u1.x, silu(v1.y) * u1.y, silu(v1.z) * u1.z, silu(v1.w) * u1.w);
       }
@@ -345,7 +350,8 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
 // instantiation.
 template <bool FP8, bool PHASE_A, int MT, typename OT>
 __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* st1, int wm, int wn, int tid,
-                                         OT* __restrict__ out, float* __restrict__ out_scale, int Nd, int n) {
+                                         OT* __restrict__ out, float* __restrict__ out_scale,
+                                         uint16_t* __restrict__ ab, int Nd, int n) {
   constexpr int MA = MT > 0 ? MT : 1;
   f32x16_v acc[MA][4];
 #pragma unroll
@@ -364,7 +370,7 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
     pipe_step<FP8, MT>(acc, it, st0, st1, s + 1, s + 2 < it.nk, (uint32_t)(s + 2) * P_ROWB);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's zero loads land before LDS is reused
-  epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT>(acc, it, st0, st1, wm, wn, tid, out, out_scale, Nd, n);
+  epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT>(acc, it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n);
 }
 
 // PHASE_A: x = tokens [T, Kd] gathered by row_token, w = W13 [E, 2*Nd, Kd],
@@ -373,6 +379,8 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
 // FP8: x, w are E4M3 codes; x_scale [rows of x, Kd/128] and
 //      w_scale [E, rows of w / 128, Kd/128] are power-of-two fp32 scales;
 //      phase A writes h as E4M3 codes with scales out_scale [P, Nd/128].
+// ab (bf16 phase A only, may be NULL): [P, 2 Nd] gets the pre-activations
+//      a (columns 0..Nd-1) and b (Nd..2Nd-1) of every token row.
 template <bool FP8, bool PHASE_A, typename OT>
 __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __restrict__ x,
                                                             const uint8_t* __restrict__ w,
@@ -386,7 +394,8 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
                                                             const int* __restrict__ totals,
                                                             const int* __restrict__ offsets,
                                                             const int* __restrict__ items,
-                                                            OT* __restrict__ out, float* __restrict__ out_scale) {
+                                                            OT* __restrict__ out, float* __restrict__ out_scale,
+                                                            uint16_t* __restrict__ ab) {
   constexpr int EB = Fmt<FP8>::EB;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[Fmt<FP8>::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[Fmt<FP8>::STAGE];
@@ -471,11 +480,11 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
     int mt_live = (it.rows - it.mrow0 + 31) >> 5;  // 32-row MFMA tiles of this wave that hold rows
     mt_live = __builtin_amdgcn_readfirstlane(mt_live < 0 ? 0 : (mt_live > 4 ? 4 : mt_live));
     switch (mt_live) {
-      case 4: run_tile<FP8, PHASE_A, 4, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
-      case 3: run_tile<FP8, PHASE_A, 3, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
-      case 2: run_tile<FP8, PHASE_A, 2, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
-      case 1: run_tile<FP8, PHASE_A, 1, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
-      default: run_tile<FP8, PHASE_A, 0, OT>(it, st0, st1, wm, wn, tid, out, out_scale, Nd, n); break;
+      case 4: run_tile<FP8, PHASE_A, 4, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
+      case 3: run_tile<FP8, PHASE_A, 3, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
+      case 2: run_tile<FP8, PHASE_A, 2, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
+      case 1: run_tile<FP8, PHASE_A, 1, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
+      default: run_tile<FP8, PHASE_A, 0, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
     }
   }
 }
@@ -661,7 +670,8 @@ PhaseSched phase_sched(int* sched, int phase, int cap, int ntA) {
 // cap >= the tile count (at most ffn_schedule_max_tiles()).
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                                 const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
-                                int Nr, int cap, uint16_t* h, void* y, bool y_f32, int* sched, hipStream_t st) {
+                                int Nr, int cap, uint16_t* h, uint16_t* ab, void* y, bool y_f32, int* sched,
+                                hipStream_t st) {
   const int nb = persistent_blocks();
   const uint32_t x_bytes = (uint32_t)((long long)T * d * 2);
   const uint32_t h_bytes = (uint32_t)(P * I * 2);
@@ -671,16 +681,16 @@ void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const ui
   const PhaseSched a = phase_sched(sched, 0, cap, ntA), b = phase_sched(sched, 1, cap, ntA);
   hipLaunchKernelGGL((k_ffn_persistent<false, true, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, xb,
                      reinterpret_cast<const uint8_t*>(w13), nullptr, nullptr, row_token, tile_map, n_tiles, d, I,
-                     x_bytes, 0u, a.cnt, a.tot, a.off, a.items, h, nullptr);
+                     x_bytes, 0u, a.cnt, a.tot, a.off, a.items, h, nullptr, ab);
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<false, false, float>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
-                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr);
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr, nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<false, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
-                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<uint16_t*>(y), nullptr);
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<uint16_t*>(y), nullptr, nullptr);
 }
 
 // E4M3 x E4M3: x codes [T, d] with x_scale [T, d/128]; W13 / W2 codes with
@@ -700,15 +710,15 @@ void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uin
   const PhaseSched a = phase_sched(sched, 0, cap, ntA), b = phase_sched(sched, 1, cap, ntA);
   hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t>), dim3(nb), dim3(P_THREADS), 0, st, x, w13, x_scale,
                      w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, xs_bytes, a.cnt, a.tot, a.off, a.items,
-                     h, h_scale);
+                     h, h_scale, nullptr);
   if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<true, false, float>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
                        w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
-                       static_cast<float*>(y), nullptr);
+                       static_cast<float*>(y), nullptr, nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<true, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
                        w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
-                       static_cast<uint16_t*>(y), nullptr);
+                       static_cast<uint16_t*>(y), nullptr, nullptr);
 }
 
 }  // namespace moe

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = M.lib()
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert L.moe_status_str(0) == b"MOE_OK"
     assert L.moe_status_str(3) == b"MOE_EWORKSPACE"
 
@@ -134,3 +134,41 @@ def test_python_binding_raises_with_message():
     import torch
     with pytest.raises(M.MoeError, match="MOE_EINVAL"):
         M._check(M.lib().moe_bias_update(None, 4, 8, 0.001, FAKE, None))
+
+
+def test_backward_entry_points_reject_bad_arguments():
+    L = M.lib()
+    F = FAKE
+    T, K, Nr, Ns, d, I, tm = 64, 4, 16, 1, 512, 256, 32
+    big = 1 << 34
+    gb = lambda **kw: _status(L.moe_expert_gemm_backward, *[kw.get(k, v) for k, v in dict(
+        x=F, w13=F, w2=F, h=F, ab=F, dy=F, T=T, K=K, Nr=Nr, Ns=Ns, d=d, I=I, tm=tm, so=F, rt=F, tmap=F, nt=F,
+        ws=F, wsb=big, dx=F, dw13=F, dw2=F, dwt=M.MOE_F32, st=None).items()])
+    assert gb(I=192)[0] == M.MOE_EUNSUPPORTED           # I % 128 != 0
+    assert gb(d=384)[0] == M.MOE_EUNSUPPORTED           # d % 256 != 0
+    assert gb(dwt=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    assert gb(K=17)[0] == M.MOE_EINVAL
+    assert gb(dw13=None)[0] == M.MOE_EINVAL
+    assert gb(dy=ctypes.c_void_p(0x1002))[0] == M.MOE_EINVAL   # misaligned
+    assert gb(wsb=16)[0] == M.MOE_EWORKSPACE
+    need = M.moe_gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tm)
+    assert need == M.moe_permute_rows(T, K, Nr, Ns, tm) * 2 * I * 2
+    gt = lambda **kw: _status(L.moe_expert_gemm_train, *[kw.get(k, v) for k, v in dict(
+        x=F, w13=F, w2=F, T=T, K=K, Nr=Nr, Ns=Ns, d=d, I=I, tm=tm, so=F, rt=F, tmap=F, nt=F, ws=F, wsb=big,
+        h=F, ab=F, y=F, yt=M.MOE_BF16, st=None).items()])
+    assert gt(d=640)[0] == M.MOE_EUNSUPPORTED
+    assert gt(ab=None)[0] == M.MOE_EINVAL
+    assert gt(yt=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    assert gt(wsb=0)[0] == M.MOE_EWORKSPACE
+    cb = lambda **kw: _status(L.moe_combine_backward, *[kw.get(k, v) for k, v in dict(
+        g=F, gt=M.MOE_BF16, y=F, yt=M.MOE_BF16, inv=F, gate=F, score=F, so=F, T=T, d=d, K=K, Nr=Nr, Ns=Ns,
+        dy=F, dg=F, dz=F, dzr=F, st=None).items()])
+    assert cb(d=12)[0] == M.MOE_EINVAL
+    assert cb(score=None)[0] == M.MOE_EINVAL
+    assert cb(gt=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    rb = lambda **kw: _status(L.moe_route_backward, *[kw.get(k, v) for k, v in dict(
+        g=F, gt=M.MOE_BF16, dx=F, u=F, ut=M.MOE_BF16, e=F, idx=F, inv=F, dz=F, dzr=F, so=F, rt=F, T=T, d=d, K=K,
+        Nr=Nr, Ns=Ns, du=F, dut=M.MOE_F32, de=F, st=None).items()])
+    assert rb(de=None)[0] == M.MOE_EINVAL
+    assert rb(dut=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    assert rb(K=Nr + 1)[0] == M.MOE_EINVAL
