@@ -17,6 +17,11 @@ The roofline object describes the expert GEMM call (gate/up + SwiGLU, then
 down), the dominant cost of the step, timed with HIP events on the stream it
 is launched on.  The cpu_baseline object times the fp64 CPU oracle on a
 bounded sample of the same workload.
+
+--train times the training step instead (bf16 workloads): the forward with
+its activations kept, the backward (combine/gate, expert GEMM dgrad and
+wgrad, input and centroid gradients) for a seeded output gradient, and the
+bias rule; its roofline object describes the expert GEMM backward call.
 """
 from __future__ import annotations
 
@@ -45,6 +50,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target length of the oracle's timed CPU work (the sample is sized for it)")
+    p.add_argument("--train", action="store_true",
+                   help="time the training step instead: training forward + backward (bf16 workloads)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (calibrates HBM byte counters) and exit")
     return p.parse_args()
@@ -107,6 +114,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.train:
+        train_main(args, cfg, dev, stream)
+        return
 
     # ---- inputs, resident in HBM before timing
     e = W.make_centroids(cfg, dev)
@@ -279,6 +289,145 @@ def cpu_baseline(cfg, layer, u, e, b, weights, sample_tokens, seconds):
             "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 routing over all {cfg.Nr} experts, "
                       f"{cfg.K} routed + {cfg.Ns} shared SwiGLU experts per token, combine; "
                       f"{len(need)} experts touched; weight conversion to fp64 not timed",
+            "seconds": total, "host_cpus": os.cpu_count()}
+
+
+TRAIN_METRIC = "MoE-layer training step (forward + backward) tokens/s at 256e/top-8 d7168"
+
+
+def train_main(args, cfg, dev, stream):
+    """One training step = the forward of main() with the activations kept
+    (moe_expert_gemm_train) + moe_combine_backward -> moe_expert_gemm_backward
+    -> moe_route_backward for a seeded bf16 dL/dh' + the bias rule.  The
+    roofline object describes the moe_expert_gemm_backward call (dgrad and
+    wgrad of both expert projections, 12 d I flops per row)."""
+    import numpy as np
+    import torch
+
+    import sparse_expert_routing_sigmoid_amd as M
+    import workloads as W
+
+    if cfg.weights != "bf16" or cfg.act != "bf16" or cfg.x_fp8:
+        print(f"--train needs a bf16 workload (got {cfg.name})", file=sys.stderr)
+        sys.exit(2)
+    e = W.make_centroids(cfg, dev)
+    bias0 = W.make_bias(cfg, dev)
+    n_u = min(max(args.steps, 1), 4)
+    us = [W.make_tokens(cfg, s, dev) for s in range(n_u)]
+    gs = [W.make_free((cfg.T, cfg.d), 1.0, 100 + s, dev, torch.bfloat16) for s in range(n_u)]
+    w13, w2 = W.make_expert_weights(cfg, dev)
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16,
+                       M.ExpertWeights(M.MOE_BF16, w13, w2), tile_m=args.tile_m, device=dev, train=True,
+                       grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    bias = bias0.clone()
+    bwd_events = []
+
+    def step(s, timed):
+        u, G = us[s % n_u], gs[s % n_u]
+        layer.forward(u, e, bias)
+        M.moe_combine_backward(G, layer.y, layer.inv_row, layer.topk_gate, layer.topk_score, layer.seg_offset,
+                               cfg.Nr, cfg.Ns, layer.dy, layer.dgate, layer.dz, layer.dz_row)
+        if timed:
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+        M.moe_expert_gemm_backward(u, w13, w2, layer.h, layer.ab, layer.dy, cfg.T, cfg.K, cfg.Nr, cfg.Ns, cfg.d,
+                                   cfg.I, args.tile_m, layer.seg_offset, layer.row_token, layer.tile_map,
+                                   layer.n_tiles, layer.bwd_ws, layer.dx, layer.dw13, layer.dw2)
+        if timed:
+            ev1.record(stream)
+            bwd_events.append((ev0, ev1))
+        M.moe_route_backward(G, layer.dx, u, e, layer.topk_idx, layer.inv_row, layer.dz, layer.dz_row,
+                             layer.seg_offset, layer.row_token, cfg.Nr, cfg.Ns, layer.du, layer.de)
+        layer.update_bias(bias, cfg.gamma)
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / max(args.steps, 1)
+    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd_events]))
+    rows = int(cfg.T * cfg.K + cfg.T * cfg.Ns)
+    bwd_flops = 12.0 * cfg.d * cfg.I * rows
+    step_flops = 18.0 * cfg.d * cfg.I * rows
+    loads = layer.expert_load.cpu().numpy().astype(np.int64)
+    achieved = bwd_flops / (bwd_ms * 1e-3)
+    roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK["bf16"] / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / PEAK["bf16"], "traffic": None,
+            "kernel": "moe_expert_gemm_backward call: k_dgrad (down + SwiGLU backward), k_dgrad (gate/up), "
+                      "k_wgrad (down), k_wgrad (gate/up)",
+            "units_per_launch": {"rows": rows, "flops": bwd_flops}, "avg_launch_ms": bwd_ms}
+    out = {
+        "metric": TRAIN_METRIC,
+        "value": cfg.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init expert weights and centroids, seeded bf16 output gradients)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "Nr": cfg.Nr, "Ns": cfg.Ns, "I": cfg.I,
+                   "K": cfg.K, "routing": cfg.routing, "weights": cfg.weights, "tile_m": args.tile_m,
+                   "step": "training forward + backward + bias rule", "grad_dtype": "bf16",
+                   "parallelism": "single GPU"},
+        "layer": {"tflops": step_flops / (ms_step * 1e-3) / 1e12,
+                  "mfma_frac": step_flops / (ms_step * 1e-3) / PEAK["bf16"],
+                  "max_load": int(loads.max()), "mean_load": float(loads.mean())},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_train(cfg, us[0], gs[0], e, bias0, w13, w2, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds):
+    """Time the fp64 backward oracle's expert FFN backward (oracle/backward.py
+    ffn_backward, the dominant part of the layer backward) on the first S
+    tokens: for every expert their rows select, dx, dW13, dW2 of those rows.
+    S is sized for about `seconds` of work; weight conversion not timed."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import backward as OB
+    from oracle import moe as O
+
+    a = np.ones((256, cfg.d))
+    w = np.ones((cfg.d, cfg.I))
+    t1 = time.perf_counter()
+    a @ w
+    rate = 2.0 * 256 * cfg.d * cfg.I / max(time.perf_counter() - t1, 1e-6)
+    per_token = 18.0 * cfg.d * cfg.I * (cfg.K + cfg.Ns)
+    S = max(16, min(int(seconds * rate / per_token), cfg.T))
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    u_s, G_s = f64(u[:S]), f64(G[:S])
+    r = O.route(u_s, f64(e), f64(b), cfg.K)
+    need = sorted(set(r.idx.ravel().tolist()) | set(range(cfg.Nr, cfg.Nr + cfg.Ns)))
+    total = 0.0
+    for i in need:
+        w13_i, w2_i = f64(w13[i]), f64(w2[i])
+        if i >= cfg.Nr:
+            x, dy = u_s, G_s
+        else:
+            ts, ks = np.nonzero(r.idx == i)
+            x, dy = u_s[ts], r.gate[ts, ks][:, None] * G_s[ts]
+        t1 = time.perf_counter()
+        OB.ffn_backward(x, w13_i, w2_i, dy)
+        total += time.perf_counter() - t1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": S / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 SwiGLU FFN backward (forward recomputed, "
+                      f"dx, dW13, dW2) of the {cfg.K} routed + {cfg.Ns} shared experts of each token, "
+                      f"{len(need)} experts touched; routing, gate and centroid gradients not timed",
             "seconds": total, "host_cpus": os.cpu_count()}
 
 

@@ -15,7 +15,8 @@
 //   ds_{t,k} = (dg_{t,k} - sum_j g_{t,j} dg_{t,j}) / S_t,   S_t = sum_j s_{t,j}
 //   dz_{t,k} = ds_{t,k} s_{t,k} (1 - s_{t,k})               (z = u . e)
 //   du_t = G_t + sum of dx over the token's rows + sum_k dz_{t,k} e_{idx(t,k)}
-//   de_i = sum over the rows of segment i of dz . u_t
+//   de_i = sum over the rows of segment i of dz . u_t (the rows of segment i
+//          are the tokens that selected expert i, each once)
 #include "common.h"
 
 namespace moe {
@@ -181,28 +182,68 @@ __global__ __launch_bounds__(IG_THREADS) void k_input_grad(const GT* __restrict_
 }
 
 // ------------------------------------------------------ centroid gradient --
-// de_i = sum over the token rows r of segment i, in row order, of
-// dz_row[r] u[row_token[r]]; a block per (expert, 1024 columns).
+// de_i = sum over the token rows r of segment i of dz_row[r] u[row_token[r]].
+// A block per (expert, 512 columns): 4 waves over the same columns, wave w
+// taking rows w, w + 4, ... of the segment, eight rows at a time with the
+// next eight tokens fetched ahead; the 4 partial sums are added in wave
+// order, so the result is the same on every run.
+constexpr int CG_THREADS = 256;
+constexpr int CG_COLS = 512;
+
 template <typename UT>
-__global__ __launch_bounds__(IG_THREADS) void k_centroid_grad(const UT* __restrict__ u,
+__global__ __launch_bounds__(CG_THREADS) void k_centroid_grad(const UT* __restrict__ u,
                                                               const int32_t* __restrict__ seg_offset,
                                                               const int32_t* __restrict__ row_token,
                                                               const float* __restrict__ dz_row, int d,
                                                               float* __restrict__ de) {
-  const int i = blockIdx.x;
-  const int c = blockIdx.y * IG_COLS + threadIdx.x * 8;
-  if (c >= d) return;
+  __shared__ float4 s_part[3][64][2];
+  const int i = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.y * CG_COLS + lane * 8;
+  const bool col_ok = c < d;
   const int r0 = seg_offset[i], r1 = seg_offset[i + 1];
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8];
-  for (int r = r0; r < r1; ++r) {
-    const int tok = row_token[r];
-    if (tok < 0) continue;
-    const float z = dz_row[r];
-    ld8(u + (long long)tok * d + c, v);
+  int tok[8];
+  float z[8];
+  auto fetch = [&](int base) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(z, v[q], acc[q]);
+    for (int q = 0; q < 8; ++q) {
+      const int r = base + 4 * q;
+      tok[q] = r < r1 ? row_token[r] : -1;
+      z[q] = r < r1 ? dz_row[r] : 0.f;
+    }
+  };
+  fetch(r0 + wave);
+  for (int base = r0 + wave; base < r1; base += 32) {
+    int tk[8];
+    float zz[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      tk[q] = tok[q];
+      zz[q] = z[q];
+    }
+    fetch(base + 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (tk[q] < 0 || !col_ok) continue;
+      ld8(u + (long long)tk[q] * d + c, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = fmaf(zz[q], v[k], acc[k]);
+    }
   }
-  st8(de + (long long)i * d + c, acc);
+  if (wave > 0) {
+    s_part[wave - 1][lane][0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    s_part[wave - 1][lane][1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  __syncthreads();
+  if (wave == 0 && col_ok) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      const float4 p = s_part[w][lane][0], q = s_part[w][lane][1];
+      acc[0] += p.x; acc[1] += p.y; acc[2] += p.z; acc[3] += p.w;
+      acc[4] += q.x; acc[5] += q.y; acc[6] += q.z; acc[7] += q.w;
+    }
+    st8(de + (long long)i * d + c, acc);
+  }
 }
 
 bool fits31(unsigned long long bytes) { return bytes < (1ull << 31); }
@@ -338,12 +379,12 @@ moe_status route_backward(const void* grad_out, moe_dtype g_t, const void* dx, c
                   aligned16(de),
               MOE_EINVAL, "grad_out, dx, u, centroids, du and de must be 16-byte aligned");
   hipStream_t st = as_stream(stream);
-  const dim3 gi((unsigned)Nr, (unsigned)ceil_div(d, IG_COLS));
+  const dim3 gi((unsigned)Nr, (unsigned)ceil_div(d, CG_COLS));
   if (u_t == MOE_BF16)
-    hipLaunchKernelGGL((k_centroid_grad<uint16_t>), gi, dim3(IG_THREADS), 0, st, cp<uint16_t>(u), seg_offset,
+    hipLaunchKernelGGL((k_centroid_grad<uint16_t>), gi, dim3(CG_THREADS), 0, st, cp<uint16_t>(u), seg_offset,
                        row_token, dz_row, d, de);
   else
-    hipLaunchKernelGGL((k_centroid_grad<float>), gi, dim3(IG_THREADS), 0, st, cp<float>(u), seg_offset, row_token,
+    hipLaunchKernelGGL((k_centroid_grad<float>), gi, dim3(CG_THREADS), 0, st, cp<float>(u), seg_offset, row_token,
                        dz_row, d, de);
   if (T > 0) {
     const dim3 gt((unsigned)T, (unsigned)ceil_div(d, IG_COLS));

@@ -25,8 +25,7 @@
 // global -> LDS by the direct 16-byte buffer-to-LDS load, two stages.  LDS
 // tiles are XOR-swizzled at 16-byte granularity so that fragment reads hit
 // distinct banks: K-contiguous tiles as in the forward, M/N-contiguous tiles
-// with chunk ^= 2 * (K-row & 3), which spreads the four K-rows of one
-// transposing read over the 128 bytes of one bank cycle.
+// by a XOR of the chunk index that depends on K-row % 4 (mnc_sw).
 #include "common.h"
 
 namespace moe {
@@ -54,9 +53,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-// Row (within the 32 x 32 MFMA tile) of accumulator element e of a lane.
-__device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
-
 // K-contiguous tile (256 rows x 128 bytes): fragment of rows r0 .. r0 + 31
 // (r0 % 32 == 0) for k-step kk (16 K values): lane l gets row r0 + l % 32,
 // K values 8 (l / 32) .. + 7 of the step.
@@ -66,30 +62,35 @@ __device__ __forceinline__ bf16x8_t frag_kc(const uint8_t* t, int r0, int kk, in
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(t + (r0 + (lane & 31)) * 128 + ((c ^ sw) << 4)));
 }
 
-// M/N-contiguous tile (64 K-rows x 512 bytes): the same fragment shape (column
-// c0 + l % 32, K values 8 (l / 32) .. + 7 of k-step kk) by two transposing
-// reads of four K-rows each.  In a group of 16 lanes, lane j names K-row
+// M/N-contiguous tile (64 K-rows x 512 bytes), 16-byte chunk c of K-row kr
+// stored at chunk c ^ mnc_sw(kr % 4).  The four K-rows that one transposing
+// read touches then fall on distinct banks whether the LDS serves 16 lanes
+// over 128 bytes or 32 lanes over 256 bytes per cycle.
+__host__ __device__ constexpr int mnc_sw(int y) { return 4 * y + 2 * ((y ^ (y >> 1)) & 1); }
+
+// Fragment reads: the same fragment shape as frag_kc (column c0 + l % 32,
+// K values 8 (l / 32) .. + 7 of k-step kk) by two transposing reads of four
+// K-rows each.  In a group of 16 lanes, lane j names K-row
 // kk * 16 + 8 (group / 2) + j / 4 (+ 4 for the second read) and columns
 // c0 + 16 (group % 2) + 4 (j % 4) .. + 3, i.e. logical chunk c0 / 8 + x with
-// x = 2 (group % 2) + (j % 4) / 2, stored at chunk (c0 / 8 + x) ^ 2 (j / 4).
-// With c0 = 128 wm + 32 i that address splits into a lane part that depends
-// only on i % 2 (MncLane) and a constant, so the reads take immediate offsets.
+// x = 2 (group % 2) + (j % 4) / 2.  With c0 = 128 wm + 32 i the address splits
+// into a lane part per i (MncLane) and a constant, so the reads take
+// immediate offsets.
 struct MncLane {
-  int base[2];  // byte address of the lane's first read for i % 2 == 0, 1 (wm folded in)
+  int base[4];  // byte address of the lane's first read for i = 0..3 (wm folded in)
   __device__ void init(int wmn, int lane) {
     const int g = lane >> 4, j = lane & 15;
     const int kr = 8 * (g >> 1) + (j >> 2);
-    const int z = (2 * (g & 1) + ((j & 3) >> 1)) ^ (2 * (j >> 2));
-    const int b = kr * 512 + wmn * 256 + (j & 1) * 8;
-    base[0] = b + (z << 4);
-    base[1] = b + ((z ^ 4) << 4);
+    const int x = 2 * (g & 1) + ((j & 3) >> 1);
+    const int sw = mnc_sw(j >> 2);  // kr % 4 == j / 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i) base[i] = kr * 512 + wmn * 256 + ((((4 * i + x) ^ sw)) << 4) + (j & 1) * 8;
   }
 };
 
 template <int I, int KK>
 __device__ __forceinline__ bf16x8_t frag_mnc(const uint8_t* t, const MncLane& ml) {
-  constexpr int c = KK * 8192 + (I >> 1) * 128;
-  const uint8_t* p = t + ml.base[I & 1] + c;
+  const uint8_t* p = t + ml.base[I] + KK * 8192;
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 512));
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
@@ -125,7 +126,7 @@ struct KcRows {
 
 // M/N-contiguous, K-rows consecutive from the start of the matrix (a weight
 // matrix [K, N] of one expert): block g holds K-rows 2 g, 2 g + 1, lane l
-// K-row 2 g + l / 32, physical chunk l % 32 = logical chunk ^ 2 (K-row % 4).
+// K-row 2 g + l / 32, physical chunk l % 32 = logical chunk ^ mnc_sw(K-row % 4).
 struct MncRows {
   __amdgpu_buffer_rsrc_t r;
   uint32_t off[8];
@@ -136,7 +137,7 @@ struct MncRows {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kr = 2 * (wave * 8 + j) + (lane >> 5);
-      const uint32_t c = (uint32_t)((lane & 31) ^ (2 * (kr & 3)));
+      const uint32_t c = (uint32_t)((lane & 31) ^ mnc_sw(kr & 3));
       off[j] = (uint32_t)kr * row_bytes + (uint32_t)col0 * 2u + c * 16u;
     }
   }
@@ -156,7 +157,7 @@ template <bool GATHER>
 struct SegRows {
   __amdgpu_buffer_rsrc_t ra, rb, rt;  // A, B, row_token
   int seg0, seglen;
-  uint32_t a_rb, b_rb, a_c, b_c;  // row bytes and tile column byte offsets
+  uint32_t a_rb, b_rb, a_c;  // row bytes, A tile column byte offset
   int tok[8];
   __device__ void fetch(int s, int wave, int lane) {
 #pragma unroll
@@ -166,11 +167,11 @@ struct SegRows {
       tok[j] = k < seglen ? v : -1;
     }
   }
-  __device__ void issue(uint8_t* sa, uint8_t* sb, int wave, int lane, int s, bool live) const {
+  __device__ void issue(uint8_t* sa, uint8_t* sb, int wave, int lane, int s, uint32_t b_c, bool live) const {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kr = 2 * (wave * 8 + j) + (lane >> 5);
-      const uint32_t c16 = (uint32_t)((lane & 31) ^ (2 * (kr & 3))) * 16u;
+      const uint32_t c16 = (uint32_t)((lane & 31) ^ mnc_sw(kr & 3)) * 16u;
       const int row = seg0 + s * BKS + kr;
       const bool ok = live && tok[j] >= 0;
       const uint32_t oa = ok ? (uint32_t)row * a_rb + a_c + c16 : OOB;
@@ -209,12 +210,18 @@ __device__ __forceinline__ void load_frags(bf16x8_t (&af)[4], bf16x8_t (&bf)[4],
   }
 }
 
+// The operands go in swapped (B fragment as the matrix instruction's first
+// operand), so the instruction computes the tile transposed: lane l holds
+// output column-major pieces, element e of acc[i][j] at tile row
+// i * 32 + l % 32 and tile column j * 32 + 8 (e / 4) + 4 (l / 32) + e % 4.  Elements 4q ..
+// 4q + 3 are then four consecutive output columns of one row, stored with a
+// single 8-byte (bf16) or 16-byte (fp32) write.
 template <int KK>
 __device__ __forceinline__ void mma16(f32x16_t (&acc)[4][4], const bf16x8_t (&af)[4], const bf16x8_t (&bf)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
 }
 
 // The four k-steps of one stage, fragments double-buffered.
@@ -246,14 +253,35 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-__device__ __forceinline__ float acc_get(const f32x16_t& a, int e) {
-  float v;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a[e]));
-  return v;
+// Elements 4q .. 4q + 3 of an accumulator, read one by one from the
+// accumulator registers (left to itself the compiler copies whole
+// accumulators to VGPRs first and spills).
+__device__ __forceinline__ float4 acc_get4(const f32x16_t& a, int q) {
+  float v0, v1, v2, v3;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v0) : "a"(a[4 * q]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v1) : "a"(a[4 * q + 1]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v2) : "a"(a[4 * q + 2]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v3) : "a"(a[4 * q + 3]));
+  return make_float4(v0, v1, v2, v3);
 }
 
-__device__ __forceinline__ void put(uint16_t* p, float v) { *p = f32_to_bf16(v); }
-__device__ __forceinline__ void put(float* p, float v) { *p = v; }
+__device__ __forceinline__ void put4(uint16_t* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+__device__ __forceinline__ void put4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ float4 get4(const uint16_t* p) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u), __uint_as_float(q.y << 16),
+                     __uint_as_float(q.y & 0xFFFF0000u));
+}
+
+// da = dh * b * SiLU'(a), db = dh * SiLU(a), SiLU'(a) = sg (1 + a (1 - sg)),
+// sg = sigmoid(a) (hardware exp2 and reciprocal, as the forward's SiLU).
+__device__ __forceinline__ void swiglu_bwd(float g, float a, float b, float& da, float& db) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+  da = g * b * sg * (1.0f + a * (1.0f - sg));
+  db = g * a * sg;
+}
 
 // ------------------------------------------------------------- dgrad --
 // Items (row tile, N tile) of the tile map, dealt to the XCDs in contiguous
@@ -319,40 +347,47 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Epilogue, straight from the accumulators: column c of the tile is
-  // output column n * 256 + c; rows past the tile's token rows and columns
-  // past Nd are not written.
-  const int lcol = lane & 31;
+  // Epilogue, straight from the accumulators (see mma16): column c of the
+  // tile is output column n * 256 + c; rows past the tile's token rows and
+  // columns past Nd are not written.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * 128 + i * 32 + (lane & 31);
+    const bool live = r < rows;
+    const long long orow = (long long)row0 + r;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = wm * 128 + i * 32 + acc_row(e, lane);
-      if (r >= rows) continue;
-      const long long orow = (long long)row0 + r;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n * BT + wn * 128 + j * 32 + lcol;
-        if (col >= Nd) continue;
-        const float g = acc_get(acc[i][j], e);
+      for (int q = 0; q < 4; ++q) {
+        const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (!live || col >= Nd) continue;
+        const float4 g = acc_get4(acc[i][j], q);
         if constexpr (SWIGLU) {
-          // da = dh * b * SiLU'(a), db = dh * SiLU(a); SiLU'(a) = sg (1 + a (1 - sg))
-          const float av = bf16_to_f32(ab[orow * 2 * Nd + col]);
-          const float bv = bf16_to_f32(ab[orow * 2 * Nd + Nd + col]);
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(av * -1.4426950408889634f));
-          put(out + orow * 2 * Nd + col, g * bv * sg * (1.0f + av * (1.0f - sg)));
-          put(out + orow * 2 * Nd + Nd + col, g * av * sg);
+          const float4 av = get4(ab + orow * 2 * Nd + col);
+          const float4 bv = get4(ab + orow * 2 * Nd + Nd + col);
+          float4 da, db;
+          swiglu_bwd(g.x, av.x, bv.x, da.x, db.x);
+          swiglu_bwd(g.y, av.y, bv.y, da.y, db.y);
+          swiglu_bwd(g.z, av.z, bv.z, da.z, db.z);
+          swiglu_bwd(g.w, av.w, bv.w, da.w, db.w);
+          put4(out + orow * 2 * Nd + col, da);
+          put4(out + orow * 2 * Nd + Nd + col, db);
         } else {
-          put(out + orow * Nd + col, g);
+          put4(out + orow * Nd + col, g);
         }
       }
-    }
+  }
 }
 
 // ------------------------------------------------------------- wgrad --
-// dW_e [M, N] = A_e^T B_e over the K-rows of segment e.  Items (expert, M
-// tile, N tile), the shared experts first (their segments are the longest),
-// dealt to the blocks in order (block b runs on XCD b % 8).
+// dW_e [M, N] = A_e^T B_e over the K-rows of segment e.  An item is (expert,
+// M tile, run of N tiles): one block computes the N tiles of the run one
+// after the other with the same K-rows (the tokens are fetched once per
+// stage index, the A tile is re-read from L2), and the first stage of the
+// next N tile is loaded while the last stage of the current one is
+// multiplied and its results stored, so the pipeline stays full across the
+// run.  Routed experts (a few rows each) take runs of `nch` N tiles; shared
+// experts (every token) one N tile per item, and go first.
 // DOWN:  A = dy [P, d] (M = d), B = h [P, I] (N = I)   -> dW2 [E, d, I]
 // !DOWN: A = dab [P, 2I] (M = 2I), B = x [T, d] gathered by row_token (N = d)
 //        -> dW13 [E, 2I, d]
@@ -360,19 +395,37 @@ template <bool GATHER, typename OT>
 __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
                                                     const int32_t* __restrict__ seg_offset,
                                                     const int32_t* __restrict__ row_token, int P_rows, int E, int Nr,
-                                                    int Md, int Nd, uint32_t a_bytes, uint32_t b_bytes,
+                                                    int Md, int Nd, int nch, uint32_t a_bytes, uint32_t b_bytes,
                                                     OT* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ntm = (Md + BT - 1) / BT, ntn = (Nd + BT - 1) / BT;
-  const int per_e = ntm * ntn;
-  const int item = blockIdx.x;
-  if (item >= E * per_e) return;
-  const int eo = item / per_e, rem = item % per_e;
-  const int e = eo < E - Nr ? Nr + eo : eo - (E - Nr);  // shared experts first
-  const int m = rem / ntn, n = rem % ntn;
+  const int runs = (ntn + nch - 1) / nch;  // runs of a routed expert's M tile
+  // Block b runs on XCD b % 8.  XCD x takes every 8th shared item (from x),
+  // then all items of the routed experts x, x + 8, ..., so the blocks that
+  // share an expert's rows run together in one L2.
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int shared_items = (E - Nr) * ntm * ntn;
+  const int my_shared = shared_items > x ? (shared_items - x + 7) / 8 : 0;
+  int e, m, n0, n1;
+  if (slot < my_shared) {
+    const int item = x + 8 * slot;
+    e = Nr + item / (ntm * ntn);
+    const int rem = item % (ntm * ntn);
+    m = rem / ntn;
+    n0 = rem % ntn;
+    n1 = n0 + 1;
+  } else {
+    const int r = slot - my_shared;
+    e = x + 8 * (r / (ntm * runs));
+    if (e >= Nr) return;
+    const int rem = r % (ntm * runs);
+    m = rem / runs;
+    n0 = (rem % runs) * nch;
+    n1 = min(n0 + nch, ntn);
+  }
   const int w_wave = __builtin_amdgcn_readfirstlane(wave);
 
   SegRows<GATHER> S;
@@ -384,49 +437,55 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
   S.a_rb = (uint32_t)Md * 2u;
   S.b_rb = (uint32_t)Nd * 2u;
   S.a_c = (uint32_t)m * BT * 2u;
-  S.b_c = (uint32_t)n * BT * 2u;
 
   MncLane mla, mlb;
   mla.init(wm, lane);
   mlb.init(wn, lane);
-  f32x16_t acc[4][4];
-  zero_acc(acc);
+  OT* ob = out + (long long)e * Md * Nd;
   // Stages rounded up to an even count (the extra stage loads zeros), so the
-  // two-stage loop body has no branch.
+  // two-stage loop body has no branch.  No rows: nk = 0 and zeros are stored.
   const int nk = (S.seglen + 2 * BKS - 1) / (2 * BKS) * 2;
-  if (nk > 0) {
-    S.fetch(0, w_wave, lane);
-    S.issue(st0, st0 + BOP, w_wave, lane, 0, true);
-    S.fetch(1, w_wave, lane);
+  S.fetch(0, w_wave, lane);
+  S.issue(st0, st0 + BOP, w_wave, lane, 0, (uint32_t)n0 * BT * 2u, nk > 0);
+  S.fetch(1, w_wave, lane);
+  for (int n = n0; n < n1; ++n) {
+    f32x16_t acc[4][4];
+    zero_acc(acc);
+    const uint32_t bc = (uint32_t)n * BT * 2u;
     for (int s = 0; s < nk; s += 2) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      S.issue(st1, st1 + BOP, w_wave, lane, s + 1, true);
-      S.fetch(s + 2, w_wave, lane);
+      S.issue(st1, st1 + BOP, w_wave, lane, s + 1, bc, true);
+      const bool wrap = s + 2 == nk;  // next: stage 0 of the next N tile of the run
+      S.fetch(wrap ? 0 : s + 2, w_wave, lane);
       mma_stage<false, false>(acc, st0, st0 + BOP, mla, mlb, wm, wn, lane);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      S.issue(st0, st0 + BOP, w_wave, lane, s + 2, s + 2 < nk);
-      S.fetch(s + 3, w_wave, lane);
+      S.issue(st0, st0 + BOP, w_wave, lane, wrap ? 0 : s + 2, wrap ? bc + BT * 2u : bc, !wrap || n + 1 < n1);
+      S.fetch(wrap ? 1 : s + 3, w_wave, lane);
       mma_stage<false, false>(acc, st1, st1 + BOP, mla, mlb, wm, wn, lane);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-
-  OT* ob = out + (long long)e * Md * Nd;
-  const int lcol = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int el = 0; el < 16; ++el) {
-      const int r = m * BT + wm * 128 + i * 32 + acc_row(el, lane);
+    for (int i = 0; i < 4; ++i) {
+      const int r = m * BT + wm * 128 + i * 32 + (lane & 31);
       if (r >= Md) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n * BT + wn * 128 + j * 32 + lcol;
-        if (col < Nd) put(ob + (long long)r * Nd + col, acc_get(acc[i][j], el));
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
+        }
     }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Blocks of k_wgrad: 8 XCDs x (a share of the shared items + the items of
+// ceil(Nr / 8) routed experts).
+unsigned wgrad_grid(int Nr, int Ns, int ntm, int ntn, int nch) {
+  const long long per_xcd = ceil_div((long long)Ns * ntm * ntn, 8) + ceil_div(Nr, 8) * (long long)ntm * ceil_div(ntn, nch);
+  return (unsigned)(8 * per_xcd);
 }
 
 }  // namespace
@@ -459,25 +518,27 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
     hipLaunchKernelGGL((k_dgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, w13, tile_map, n_tiles,
                        2 * I, d, dab_bytes, nullptr, dx);
   }
-  // wgrad, down: dW2 [E, d, I]
+  // wgrad, down: dW2 [E, d, I]; routed runs of 4 N tiles (of I / 256)
   {
-    const unsigned grid = (unsigned)(E * (d / BT) * ((I + BT - 1) / BT));
+    const int ntm = d / BT, ntn = (I + BT - 1) / BT, nch = 4;
+    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
     if (dw_f32)
-      hipLaunchKernelGGL((k_wgrad<false, float>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token, (int)P, E,
-                         Nr, d, I, dy_bytes, h_bytes, static_cast<float*>(dw2));
+      hipLaunchKernelGGL((k_wgrad<false, float>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
+                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<float*>(dw2));
     else
       hipLaunchKernelGGL((k_wgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
-                         (int)P, E, Nr, d, I, dy_bytes, h_bytes, static_cast<uint16_t*>(dw2));
+                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<uint16_t*>(dw2));
   }
-  // wgrad, gate/up: dW13 [E, 2I, d]
+  // wgrad, gate/up: dW13 [E, 2I, d]; routed runs of 7 N tiles (of d / 256)
   {
-    const unsigned grid = (unsigned)(E * (2 * I / BT) * (d / BT));
+    const int ntm = 2 * I / BT, ntn = d / BT, nch = 7;
+    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
     if (dw_f32)
-      hipLaunchKernelGGL((k_wgrad<true, float>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token, (int)P, E,
-                         Nr, 2 * I, d, dab_bytes, x_bytes, static_cast<float*>(dw13));
+      hipLaunchKernelGGL((k_wgrad<true, float>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
+                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<float*>(dw13));
     else
       hipLaunchKernelGGL((k_wgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
-                         (int)P, E, Nr, 2 * I, d, dab_bytes, x_bytes, static_cast<uint16_t*>(dw13));
+                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<uint16_t*>(dw13));
   }
 }
 
