@@ -283,6 +283,46 @@ __device__ __forceinline__ void swiglu_bwd(float g, float a, float b, float& da,
   db = g * a * sg;
 }
 
+// A 256 x 256 bf16 result tile leaves through a free 64 KB stage buffer in
+// two halves of 128 rows: the waves of the half write their accumulators as
+// bf16 (16-byte chunk c of row r at chunk c ^ (r % 32), so the 32 rows one
+// write instruction touches fall on different banks), then every thread
+// copies 16-byte chunks out, two full 512-byte rows per wave instruction.
+// Rows >= rows_valid and columns >= cols_valid are not written.
+__device__ __forceinline__ void store_tile_bf16(const f32x16_t (&acc)[4][4], uint8_t* __restrict__ stg,
+                                                uint16_t* __restrict__ out, long long ld, int rows_valid,
+                                                int cols_valid, int wm, int wn, int tid, int lane) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i * 32 + (lane & 31);
+        uint8_t* rp = stg + row * 512 + 8 * (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int chunk = wn * 16 + j * 4 + q;
+            const float4 v = acc_get4(acc[i][j], q);
+            *reinterpret_cast<uint2*>(rp + ((chunk ^ (row & 31)) << 4)) =
+                make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+          }
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int rr = 0; rr < 16; ++rr) {
+      const int idx = rr * BTHREADS + tid, row = idx >> 5, chunk = idx & 31;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 512 + ((chunk ^ (row & 31)) << 4));
+      const int grow = half * 128 + row;
+      if (grow < rows_valid && chunk * 8 < cols_valid)
+        *reinterpret_cast<uint4*>(out + grow * ld + chunk * 8) = v;
+    }
+  }
+}
+
 // ------------------------------------------------------------- dgrad --
 // Items (row tile, N tile) of the tile map, dealt to the XCDs in contiguous
 // runs (block b runs on XCD b % 8): XCD x takes items [x q, x q + q) of the
@@ -347,9 +387,16 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Epilogue, straight from the accumulators (see mma16): column c of the
-  // tile is output column n * 256 + c; rows past the tile's token rows and
-  // columns past Nd are not written.
+  // Epilogue (see mma16 for the accumulator layout): column c of the tile is
+  // output column n * 256 + c; rows past the tile's token rows and columns
+  // past Nd are not written.  dx goes out through LDS (st1 is free: the last
+  // loads went to st0); the SwiGLU backward reads [a | b] and writes
+  // [da | db] straight from the accumulators.
+  if constexpr (!SWIGLU) {
+    store_tile_bf16(acc, st1, reinterpret_cast<uint16_t*>(out) + (long long)row0 * Nd + n * BT, Nd, rows,
+                    Nd - n * BT, wm, wn, tid, lane);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wm * 128 + i * 32 + (lane & 31);
@@ -362,7 +409,7 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
         const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
         if (!live || col >= Nd) continue;
         const float4 g = acc_get4(acc[i][j], q);
-        if constexpr (SWIGLU) {
+        {
           const float4 av = get4(ab + orow * 2 * Nd + col);
           const float4 bv = get4(ab + orow * 2 * Nd + Nd + col);
           float4 da, db;
@@ -372,8 +419,6 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
           swiglu_bwd(g.w, av.w, bv.w, da.w, db.w);
           put4(out + orow * 2 * Nd + col, da);
           put4(out + orow * 2 * Nd + Nd + col, db);
-        } else {
-          put4(out + orow * Nd + col, g);
         }
       }
   }
@@ -465,17 +510,24 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
       S.fetch(wrap ? 1 : s + 3, w_wave, lane);
       mma_stage<false, false>(acc, st1, st1 + BOP, mla, mlb, wm, wn, lane);
     }
+    // (see mma16 for the accumulator layout); bf16 results leave through
+    // st1, free here (the last loads went to st0)
+    if constexpr (sizeof(OT) == 2) {
+      store_tile_bf16(acc, st1, reinterpret_cast<uint16_t*>(ob) + (long long)m * BT * Nd + n * BT, Nd, Md - m * BT,
+                      Nd - n * BT, wm, wn, tid, lane);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m * BT + wm * 128 + i * 32 + (lane & 31);
-      if (r >= Md) continue;
+      for (int i = 0; i < 4; ++i) {
+        const int r = m * BT + wm * 128 + i * 32 + (lane & 31);
+        if (r >= Md) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
-          if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+            if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
+          }
+      }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
