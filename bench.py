@@ -62,9 +62,9 @@ def parse():
 # factor the same counters give for a plain copy of known size).  Valid only
 # for the kernel sources they were taken on: a changed source gives null.
 TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 35962216714, "write_bytes": 1359584277, "digest": "a8b2f4af82fd3bd8"},
-    "v3_prefill_fp8": {"fetch_bytes": 29870453029, "write_bytes": 2471189483, "digest": "a8b2f4af82fd3bd8"},
-    "v3_decode_fp8w": {"fetch_bytes": 11332985484, "write_bytes": 21533323, "digest": "49fef2d0e1c3eb96"},
+    "v3_prefill_bf16": {"fetch_bytes": 35666813324, "write_bytes": 1359584213, "digest": "9bae060818f18d3a"},
+    "v3_prefill_fp8": {"fetch_bytes": 29678604450, "write_bytes": 2470215456, "digest": "9bae060818f18d3a"},
+    "v3_decode_fp8w": {"fetch_bytes": 11331067267, "write_bytes": 21524512, "digest": "49fef2d0e1c3eb96"},
 }
 
 # Source files of the kernels each workload's expert GEMM runs.
