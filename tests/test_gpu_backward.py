@@ -144,3 +144,52 @@ def test_no_tokens():
     assert du.shape[0] == 0
     for t in (de, dw13, dw2):
         assert torch.count_nonzero(t).item() == 0
+
+
+def oracle_grads(cfg, u, e, b, w13, w2, G):
+    return OB.layer_backward(*map(f64_of, (u, e, b, w13, w2)), cfg.Nr, cfg.Ns, cfg.K, f64_of(G))
+
+
+@pytest.mark.parametrize("shape", [dict(T=1), dict(T=96, Nr=8, K=8), dict(T=200, Nr=1, K=1)],
+                         ids=["single_token", "every_expert_selected", "single_routed_expert"])
+def test_backward_degenerate_routings(shape):
+    """One token; K = N_r (every token selects every routed expert); N_r =
+    K = 1 (every gate is 1, so no gradient reaches the centroid)."""
+    cfg = CASES["small"].with_(**shape)
+    layer, w13, w2, u, e, b = build(cfg)
+    layer.forward(u, e, b)
+    G = grad_out(cfg, 3)
+    du, de, dw13, dw2 = layer.backward(G, u, e)
+    torch.cuda.synchronize()
+    gr = oracle_grads(cfg, u, e, b, w13, w2, G)
+    for name, got, want in (("du", du, gr.du), ("dw13", dw13, gr.dw13), ("dw2", dw2, gr.dw2)):
+        assert rel_l2(f64_of(got), want) <= TOL, name
+    if cfg.Nr == cfg.K == 1:
+        # g = s / s = 1 whatever s: the centroid and gate-score gradients are 0
+        assert np.all(np.abs(f64_of(layer.dz)) <= 1e-6)
+        assert np.all(np.abs(f64_of(de)) <= 1e-5)
+    else:
+        assert rel_l2(f64_of(de), gr.de) <= TOL
+
+
+def test_backward_fp32_gradient_tensors():
+    """dL/dh' given in fp32 and du requested in fp32 through the C ABI; the
+    expert-row gradient dy stays bf16 (the GEMMs' operand type)."""
+    cfg = CASES["small"]
+    layer, w13, w2, u, e, b = build(cfg)
+    layer.forward(u, e, b)
+    G = grad_out(cfg, 4).float() * 0.5 + 1e-3      # values no bf16 tensor holds
+    M.moe_combine_backward(G, layer.y, layer.inv_row, layer.topk_gate, layer.topk_score, layer.seg_offset,
+                           cfg.Nr, cfg.Ns, layer.dy, layer.dgate, layer.dz, layer.dz_row)
+    M.moe_expert_gemm_backward(u, w13, w2, layer.h, layer.ab, layer.dy, cfg.T, cfg.K, cfg.Nr, cfg.Ns, cfg.d, cfg.I,
+                               32, layer.seg_offset, layer.row_token, layer.tile_map, layer.n_tiles, layer.bwd_ws,
+                               layer.dx, layer.dw13, layer.dw2)
+    du = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    M.moe_route_backward(G, layer.dx, u, e, layer.topk_idx, layer.inv_row, layer.dz, layer.dz_row,
+                         layer.seg_offset, layer.row_token, cfg.Nr, cfg.Ns, du, layer.de)
+    torch.cuda.synchronize()
+    gr = oracle_grads(cfg, u, e, b, w13, w2, G)
+    assert rel_l2(f64_of(du), gr.du) <= TOL
+    assert rel_l2(f64_of(du) - f64_of(G), gr.du - f64_of(G)) <= TOL
+    assert rel_l2(f64_of(layer.de), gr.de) <= TOL
+    assert rel_l2(f64_of(layer.dgate), gr.dgate) <= TOL
