@@ -186,14 +186,15 @@ struct SegRows {
 // Fragments of k-step KK for a wave at (wm, wn): A from the A stage, B from
 // the B stage, each K-contiguous (KC) or M/N-contiguous (ml* give the lane
 // addresses of the latter).
-template <bool A_KC, bool B_KC, int KK>
+template <bool A_KC, bool B_KC, int KK, int MT>
 __device__ __forceinline__ void load_frags(bf16x8_t (&af)[4], bf16x8_t (&bf)[4], const uint8_t* sa,
                                            const uint8_t* sb, const MncLane& mla, const MncLane& mlb, int wm,
                                            int wn, int lane) {
   if constexpr (A_KC) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = frag_kc(sa, wm * 128 + i * 32, KK, lane);
+    for (int i = 0; i < MT; ++i) af[i] = frag_kc(sa, wm * 128 + i * 32, KK, lane);
   } else {
+    static_assert(MT == 4, "M/N-contiguous A tiles are always full");
     af[0] = frag_mnc<0, KK>(sa, mla);
     af[1] = frag_mnc<1, KK>(sa, mla);
     af[2] = frag_mnc<2, KK>(sa, mla);
@@ -216,31 +217,33 @@ __device__ __forceinline__ void load_frags(bf16x8_t (&af)[4], bf16x8_t (&bf)[4],
 // i * 32 + l % 32 and tile column j * 32 + 8 (e / 4) + 4 (l / 32) + e % 4.  Elements 4q ..
 // 4q + 3 are then four consecutive output columns of one row, stored with a
 // single 8-byte (bf16) or 16-byte (fp32) write.
-template <int KK>
+template <int KK, int MT>
 __device__ __forceinline__ void mma16(f32x16_t (&acc)[4][4], const bf16x8_t (&af)[4], const bf16x8_t (&bf)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
 }
 
-// The four k-steps of one stage, fragments double-buffered.
-template <bool A_KC, bool B_KC>
+// The four k-steps of one stage, fragments double-buffered.  MT: the 32-row
+// groups of the wave's A rows that hold rows (the others are neither read
+// nor multiplied; their accumulators stay zero).
+template <bool A_KC, bool B_KC, int MT = 4>
 __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[4][4], const uint8_t* __restrict__ sa,
                                           const uint8_t* __restrict__ sb, const MncLane& mla, const MncLane& mlb,
                                           int wm, int wn, int lane) {
   bf16x8_t f0[4], g0[4], f1[4], g1[4];
-  load_frags<A_KC, B_KC, 0>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
-  load_frags<A_KC, B_KC, 1>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
-  mma16<0>(acc, f0, g0);
+  load_frags<A_KC, B_KC, 0, MT>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
+  load_frags<A_KC, B_KC, 1, MT>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
+  mma16<0, MT>(acc, f0, g0);
   __builtin_amdgcn_sched_barrier(0);
-  load_frags<A_KC, B_KC, 2>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
-  mma16<1>(acc, f1, g1);
+  load_frags<A_KC, B_KC, 2, MT>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
+  mma16<1, MT>(acc, f1, g1);
   __builtin_amdgcn_sched_barrier(0);
-  load_frags<A_KC, B_KC, 3>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
-  mma16<2>(acc, f0, g0);
+  load_frags<A_KC, B_KC, 3, MT>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
+  mma16<2, MT>(acc, f0, g0);
   __builtin_amdgcn_sched_barrier(0);
-  mma16<3>(acc, f1, g1);
+  mma16<3, MT>(acc, f1, g1);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -334,6 +337,76 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16_t (&acc)[4][4], uin
 }
 
 // ------------------------------------------------------------- dgrad --
+// K loop and epilogue of one dgrad item for a wave with MT live 32-row
+// groups (all instantiations run the same barriers).
+template <bool SWIGLU, typename OT, int MT>
+__device__ __forceinline__ void dgrad_run(const KcRows& A, const MncRows& B, uint8_t* __restrict__ st0,
+                                          uint8_t* __restrict__ st1, const MncLane& mlb, int wm, int wn, int tid,
+                                          int lane, int w_wave, int Kd, int Nd, int n, int row0, int rows,
+                                          const uint16_t* __restrict__ ab, OT* __restrict__ out) {
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+  // Kd % 128 == 0, so the stage count is even and the loop body, two stages
+  // that name their buffers, has no branch: a branch lets the compiler sink
+  // MFMAs past the next barrier and costs registers.  The final issue loads
+  // zeros (out of range) into a buffer nobody reads.
+  const int nk = Kd / BKS;
+  A.issue(st0, w_wave, 0, 0u);
+  B.issue(st0 + BOP, w_wave, 0, 0u);
+  for (int s = 0; s < nk; s += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    A.issue(st1, w_wave, s + 1, 0u);
+    B.issue(st1 + BOP, w_wave, s + 1, 0u);
+    mma_stage<true, false, MT>(acc, st0, st0 + BOP, mlb, mlb, wm, wn, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t oob = s + 2 < nk ? 0u : OOB;
+    A.issue(st0, w_wave, s + 2, oob);
+    B.issue(st0 + BOP, w_wave, s + 2, oob);
+    mma_stage<true, false, MT>(acc, st1, st1 + BOP, mlb, mlb, wm, wn, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue (see mma16 for the accumulator layout): column c of the tile is
+  // output column n * 256 + c; rows past the tile's token rows and columns
+  // past Nd are not written.  dx goes out through LDS (st1 is free: the last
+  // loads went to st0); the SwiGLU backward reads [a | b] and writes
+  // [da | db] straight from the accumulators.
+  if constexpr (!SWIGLU) {
+    store_tile_bf16(acc, st1, reinterpret_cast<uint16_t*>(out) + (long long)row0 * Nd + n * BT, Nd, rows,
+                    Nd - n * BT, wm, wn, tid, lane);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * 128 + i * 32 + (lane & 31);
+    const bool live = r < rows;
+    const long long orow = (long long)row0 + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (!live || col >= Nd) continue;
+        const float4 g = acc_get4(acc[i][j], q);
+        {
+          const float4 av = get4(ab + orow * 2 * Nd + col);
+          const float4 bv = get4(ab + orow * 2 * Nd + Nd + col);
+          float4 da, db;
+          swiglu_bwd(g.x, av.x, bv.x, da.x, db.x);
+          swiglu_bwd(g.y, av.y, bv.y, da.y, db.y);
+          swiglu_bwd(g.z, av.z, bv.z, da.z, db.z);
+          swiglu_bwd(g.w, av.w, bv.w, da.w, db.w);
+          put4(out + orow * 2 * Nd + col, da);
+          put4(out + orow * 2 * Nd + Nd + col, db);
+        }
+      }
+  }
+}
+
+
+
 // Items (row tile, N tile) of the tile map, dealt to the XCDs in contiguous
 // runs (block b runs on XCD b % 8): XCD x takes items [x q, x q + q) of the
 // item list ordered tile-major, so the row tiles of one expert, and the
@@ -373,64 +446,15 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
 
   MncLane mlb;
   mlb.init(wn, lane);
-  f32x16_t acc[4][4];
-  zero_acc(acc);
-  // Kd % 128 == 0, so the stage count is even and the loop body, two stages
-  // that name their buffers, has no branch: a branch lets the compiler sink
-  // MFMAs past the next barrier and costs registers.  The final issue loads
-  // zeros (out of range) into a buffer nobody reads.
-  const int nk = Kd / BKS;
-  A.issue(st0, w_wave, 0, 0u);
-  B.issue(st0 + BOP, w_wave, 0, 0u);
-  for (int s = 0; s < nk; s += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    A.issue(st1, w_wave, s + 1, 0u);
-    B.issue(st1 + BOP, w_wave, s + 1, 0u);
-    mma_stage<true, false>(acc, st0, st0 + BOP, mlb, mlb, wm, wn, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint32_t oob = s + 2 < nk ? 0u : OOB;
-    A.issue(st0, w_wave, s + 2, oob);
-    B.issue(st0 + BOP, w_wave, s + 2, oob);
-    mma_stage<true, false>(acc, st1, st1 + BOP, mlb, mlb, wm, wn, lane);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // Epilogue (see mma16 for the accumulator layout): column c of the tile is
-  // output column n * 256 + c; rows past the tile's token rows and columns
-  // past Nd are not written.  dx goes out through LDS (st1 is free: the last
-  // loads went to st0); the SwiGLU backward reads [a | b] and writes
-  // [da | db] straight from the accumulators.
-  if constexpr (!SWIGLU) {
-    store_tile_bf16(acc, st1, reinterpret_cast<uint16_t*>(out) + (long long)row0 * Nd + n * BT, Nd, rows,
-                    Nd - n * BT, wm, wn, tid, lane);
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wm * 128 + i * 32 + (lane & 31);
-    const bool live = r < rows;
-    const long long orow = (long long)row0 + r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (!live || col >= Nd) continue;
-        const float4 g = acc_get4(acc[i][j], q);
-        {
-          const float4 av = get4(ab + orow * 2 * Nd + col);
-          const float4 bv = get4(ab + orow * 2 * Nd + Nd + col);
-          float4 da, db;
-          swiglu_bwd(g.x, av.x, bv.x, da.x, db.x);
-          swiglu_bwd(g.y, av.y, bv.y, da.y, db.y);
-          swiglu_bwd(g.z, av.z, bv.z, da.z, db.z);
-          swiglu_bwd(g.w, av.w, bv.w, da.w, db.w);
-          put4(out + orow * 2 * Nd + col, da);
-          put4(out + orow * 2 * Nd + Nd + col, db);
-        }
-      }
+  // 32-row groups of this wave's rows that hold token rows
+  int mt = (rows - wm * 128 + 31) >> 5;
+  mt = __builtin_amdgcn_readfirstlane(mt < 0 ? 0 : (mt > 4 ? 4 : mt));
+  switch (mt) {
+    case 4: dgrad_run<SWIGLU, OT, 4>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 3: dgrad_run<SWIGLU, OT, 3>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 2: dgrad_run<SWIGLU, OT, 2>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 1: dgrad_run<SWIGLU, OT, 1>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    default: dgrad_run<SWIGLU, OT, 0>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
   }
 }
 
@@ -591,9 +615,9 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
       hipLaunchKernelGGL((k_wgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
                          (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<uint16_t*>(dw2));
   }
-  // wgrad, gate/up: dW13 [E, 2I, d]; routed runs of 7 N tiles (of d / 256)
+  // wgrad, gate/up: dW13 [E, 2I, d]; routed runs of 4 N tiles (of d / 256)
   {
-    const int ntm = 2 * I / BT, ntn = d / BT, nch = 7;
+    const int ntm = 2 * I / BT, ntn = d / BT, nch = 4;
     const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
     if (dw_f32)
       hipLaunchKernelGGL((k_wgrad<true, float>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
