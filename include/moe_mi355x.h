@@ -22,11 +22,17 @@
  * ---------------------------------------
  *  - Pointers named as device pointers must point to device memory (HBM) of
  *    the current HIP device; the caller owns every buffer.  The library
- *    allocates and frees nothing, keeps no pointer after a call returns and
- *    holds no mutable global state.
- *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
- *    enqueues kernels on it and returns without synchronising; calls on
- *    distinct streams may run concurrently from different threads.
+ *    allocates and frees no memory and keeps no pointer after a call
+ *    returns.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call
+ *    enqueues its kernels on it and returns without synchronising; calls on
+ *    distinct streams may run concurrently from different threads.  One
+ *    exception: moe_expert_gemm on the (BF16, E4M3) path forks half of its
+ *    down-projection kernels onto a side stream of the library's own (one
+ *    per device, created with two events on first use and kept until the
+ *    process ends) and joins it back into `stream` with an event before it
+ *    returns, so to the caller all its work is still ordered on `stream`
+ *    (a mutex serialises the fork between threads).
  *  - Tensors are row-major and contiguous, element offsets are 64-bit.
  *    Data tensors (u, centroids, x, weights, y, out, q and the workspaces)
  *    must be 16-byte aligned (hipMalloc and torch allocations are 256-byte
