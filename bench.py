@@ -135,9 +135,13 @@ def main():
 
     bias = bias0.clone()
     gemm_events = []
+    step_events = []
 
     def step(s, timed):
         u = us[s % n_u]
+        if timed:
+            sv0 = torch.cuda.Event(enable_timing=True)
+            sv0.record(stream)
         layer.route(u, e, bias)
         layer.permute()
         if timed:
@@ -150,6 +154,10 @@ def main():
             gemm_events.append((ev0, ev1))
         layer.combine(u)
         layer.update_bias(bias, cfg.gamma)
+        if timed:
+            sv1 = torch.cuda.Event(enable_timing=True)
+            sv1.record(stream)
+            step_events.append((sv0, sv1))
 
     for s in range(args.warmup):
         step(s, False)
@@ -161,6 +169,7 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / max(args.steps, 1)
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in gemm_events])) if gemm_events else float("nan")
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_events])
 
     # ---- algorithmic work of one step
     loads = layer.expert_load.cpu().numpy().astype(np.int64)
@@ -221,13 +230,46 @@ def main():
                   "mfma_frac": gemm_flops / layer_time / (PEAK["fp8"] if cfg.x_fp8 else PEAK["bf16"]),
                   "hbm_gbs": layer_bytes / layer_time / 1e9, "hbm_frac": layer_bytes / layer_time / PEAK["hbm"],
                   "experts_touched": touched, "max_load": int(loads.max()), "mean_load": float(loads.mean()),
+                  "last_step_load_slope": load_fit_exponent(loads),
                   "padded_rows": int(layer.seg_offset[-1].item())},
+        "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
+                    "p90": float(np.percentile(step_ms, 90)), "timer": "HIP events per step on the stream"},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, layer, us[0], e, bias0, weights, args.cpu_sample_tokens,
                                            args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def load_fit_exponent(loads):
+    """Least-squares slope of log(load) against log(rank) over the experts
+    with a nonzero load, sorted by load (a Zipf law of exponent s gives -s).
+    Reported for the last timed step: the bias rule, applied after every
+    step, flattens the skew of the first step (slope -1.1 at T = 8192 with
+    b = 0) as the steps go on."""
+    import numpy as np
+    x = np.sort(loads[loads > 0])[::-1].astype(np.float64)
+    if x.size < 2:
+        return None
+    return float(np.polyfit(np.log(np.arange(1, x.size + 1)), np.log(x), 1)[0])
+
+
+def host_info():
+    """CPU model and the BLAS NumPy uses, for the oracle timing."""
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{p.get('internal_api')} ({p.get('num_threads')} threads)" for p in threadpool_info()
+            if p.get("user_api") == "blas"]
+    return {"cpu_model": model, "blas": ", ".join(blas) or None}
 
 
 def cpu_baseline(cfg, layer, u, e, b, weights, sample_tokens, seconds):
@@ -290,7 +332,7 @@ def cpu_baseline(cfg, layer, u, e, b, weights, sample_tokens, seconds):
             "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 routing over all {cfg.Nr} experts, "
                       f"{cfg.K} routed + {cfg.Ns} shared SwiGLU experts per token, combine; "
                       f"{len(need)} experts touched; weight conversion to fp64 not timed",
-            "seconds": total, "host_cpus": os.cpu_count()}
+            "seconds": total, "host_cpus": os.cpu_count(), **host_info()}
 
 
 TRAIN_METRIC = "MoE-layer training step (forward + backward) tokens/s at 256e/top-8 d7168"
@@ -429,7 +471,7 @@ def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds):
             "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 SwiGLU FFN backward (forward recomputed, "
                       f"dx, dW13, dW2) of the {cfg.K} routed + {cfg.Ns} shared experts of each token, "
                       f"{len(need)} experts touched; routing, gate and centroid gradients not timed",
-            "seconds": total, "host_cpus": os.cpu_count()}
+            "seconds": total, "host_cpus": os.cpu_count(), **host_info()}
 
 
 if __name__ == "__main__":
