@@ -193,3 +193,37 @@ def test_backward_fp32_gradient_tensors():
     assert rel_l2(f64_of(du) - f64_of(G), gr.du - f64_of(G)) <= TOL
     assert rel_l2(f64_of(layer.de), gr.de) <= TOL
     assert rel_l2(f64_of(layer.dgate), gr.dgate) <= TOL
+
+
+@pytest.mark.parametrize("tile_m", [1, 256])
+def test_backward_segment_padding(tile_m):
+    """Segments padded to 1 row (no padding) and to 256 rows (every segment
+    a whole tile): padding rows must neither contribute nor be read."""
+    cfg = CASES["small"].with_(T=200, K=5)
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16,
+                       M.ExpertWeights(M.MOE_BF16, w13, w2), tile_m=tile_m, train=True)
+    u, e, b = W.make_tokens(cfg, 0, "cuda"), W.make_centroids(cfg, "cuda"), W.make_bias(cfg, "cuda")
+    layer.dy.fill_(float("nan"))          # padding rows of the row buffers hold NaN
+    layer.dx.fill_(float("nan"))
+    layer.forward(u, e, b)
+    G = grad_out(cfg, 5)
+    du, de, dw13, dw2 = layer.backward(G, u, e)
+    torch.cuda.synchronize()
+    gr = oracle_grads(cfg, u, e, b, w13, w2, G)
+    for name, got, want in (("du", du, gr.du), ("de", de, gr.de), ("dw13", dw13, gr.dw13), ("dw2", dw2, gr.dw2)):
+        assert rel_l2(f64_of(got), want) <= TOL, name
+
+
+def test_backward_top16():
+    """K = 16, the largest K the library takes."""
+    cfg = CASES["small"].with_(T=128, Nr=32, K=16)
+    layer, w13, w2, u, e, b = build(cfg)
+    layer.forward(u, e, b)
+    G = grad_out(cfg, 6)
+    du, de, dw13, dw2 = layer.backward(G, u, e)
+    torch.cuda.synchronize()
+    gr = oracle_grads(cfg, u, e, b, w13, w2, G)
+    for name, got, want in (("du", du, gr.du), ("de", de, gr.de), ("dw13", dw13, gr.dw13), ("dw2", dw2, gr.dw2),
+                            ("dz", layer.dz, gr.dz)):
+        assert rel_l2(f64_of(got), want) <= TOL, name
