@@ -49,12 +49,25 @@ __device__ __forceinline__ void ld8(const uint16_t* p, float (&v)[8]) {
     v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
 }
+// The same with the non-temporal hint, for rows read once (G, y, dx):
+// 426 -> 410 us for the combine backward at T = 8192.  The centroid
+// gradient re-reads token rows once per selected expert and keeps ld8.
+__device__ __forceinline__ void ld8_once(const uint16_t* p, float (&v)[8]) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(q[i] << 16);
+    v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+  }
+}
 __device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
+__device__ __forceinline__ void ld8_once(const float* p, float (&v)[8]) { ld8(p, v); }
 __device__ __forceinline__ void st8(uint16_t* p, const float (&v)[8]) {
   uint4 q;
   q.x = pack_bf16x2(v[0], v[1]);
@@ -99,11 +112,11 @@ __global__ __launch_bounds__(CBB_THREADS) void k_combine_bwd(const GT* __restric
   }
   for (int c = tid * 8; c < d; c += CBB_THREADS * 8) {
     float gv[8], yv[8], o[8];
-    ld8(G + (long long)t * d + c, gv);
+    ld8_once(G + (long long)t * d + c, gv);
 #pragma unroll
     for (int k = 0; k < MOE_MAX_K; ++k) {
       if (k >= K) break;
-      ld8(y + rows[k] * d + c, yv);
+      ld8_once(y + rows[k] * d + c, yv);
       float p = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) p = fmaf(gv[i], yv[i], p);
@@ -161,14 +174,14 @@ __global__ __launch_bounds__(IG_THREADS) void k_input_grad(const GT* __restrict_
   const int c = blockIdx.y * IG_COLS + threadIdx.x * 8;
   if (c >= d) return;
   float acc[8], v[8];
-  ld8(G + (long long)t * d + c, acc);
+  ld8_once(G + (long long)t * d + c, acc);
   for (int j = 0; j < Ns; ++j) {
-    ld8(dx + ((long long)seg_offset[Nr + j] + t) * d + c, v);
+    ld8_once(dx + ((long long)seg_offset[Nr + j] + t) * d + c, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
   for (int k = 0; k < K; ++k) {
-    ld8(dx + (long long)inv_row[(long long)t * K + k] * d + c, v);
+    ld8_once(dx + (long long)inv_row[(long long)t * K + k] * d + c, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
