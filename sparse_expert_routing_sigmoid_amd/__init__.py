@@ -368,3 +368,24 @@ class MoeLayer:
 
     def update_bias(self, bias, gamma=0.001, stream=None):
         moe_bias_update(self.expert_load, self.T * self.K, gamma, bias, stream)
+
+
+def moe_forward(u, centroids, bias, weights: ExpertWeights, K, Ns, update_bias=False, gamma=0.001, x_fp8=False,
+                tile_m=32, out_dtype=None, stream=None):
+    """One DeepSeekMoE layer forward in a single call: route, permute,
+    [quantise u], expert GEMMs, combine, and optionally the end-of-step bias
+    rule (the bias tensor is updated in place).  Allocates the layer's
+    buffers on every call (MoeLayer keeps them across steps).  Returns
+    (out, layer): the layer holds the routing, loads and layout of the call.
+
+    u [T, d] (fp32/bf16), centroids [N_r, d] fp32, bias [N_r] fp32,
+    weights: ExpertWeights of the N_r routed + Ns shared experts."""
+    T, d = u.shape
+    Nr = centroids.shape[0]
+    I = weights.w2.shape[2]
+    layer = MoeLayer(T, d, Nr, Ns, I, K, u.dtype, weights, x_fp8=x_fp8, tile_m=tile_m, out_dtype=out_dtype,
+                     device=u.device)
+    out = layer.forward(u, centroids, bias, stream)
+    if update_bias:
+        layer.update_bias(bias, gamma, stream)
+    return out, layer

@@ -151,33 +151,36 @@ struct MncRows {
 // seglen - 1), for both operands of a weight gradient.  A K-row is live if it
 // lies in the segment and holds a token (row_token >= 0); dead K-rows load
 // zeros on both sides.  Operand A reads permuted row seg0 + k; operand B the
-// same row, or (GATHER) the token's row of x.  The tokens of the next stage
-// are fetched one stage ahead.
-template <bool GATHER>
+// same row, or (GATHER) the token's row of x.  The loading waves (lw = 0 ..
+// 32 / NB - 1) issue NB 1 KB blocks of each operand apiece per stage; the
+// tokens of the next stage are fetched one stage ahead.
+template <bool GATHER, int NB>
 struct SegRows {
   __amdgpu_buffer_rsrc_t ra, rb, rt;  // A, B, row_token
   int seg0, seglen;
   uint32_t a_rb, b_rb, a_c;  // row bytes, A tile column byte offset
-  int tok[8];
-  __device__ void fetch(int s, int wave, int lane) {
+  int tok[NB];
+  __device__ void fetch(int s, int lw, int lane) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = s * BKS + 2 * (wave * 8 + j) + (lane >> 5);
-      const int v = __builtin_amdgcn_raw_buffer_load_b32(rt, k < seglen ? (uint32_t)(seg0 + k) * 4u : OOB, 0, 0);
-      tok[j] = k < seglen ? v : -1;
+    for (int j = 0; j < NB; ++j) {
+      const int k = s * BKS + 2 * (lw * NB + j) + (lane >> 5);
+      // K-rows past the segment load 0 (out of range); issue() masks them,
+      // so nothing here waits for the load
+      tok[j] = __builtin_amdgcn_raw_buffer_load_b32(rt, k < seglen ? (uint32_t)(seg0 + k) * 4u : OOB, 0, 0);
     }
   }
-  __device__ void issue(uint8_t* sa, uint8_t* sb, int wave, int lane, int s, uint32_t b_c, bool live) const {
+  __device__ void issue(uint8_t* sa, uint8_t* sb, int lw, int lane, int s, uint32_t b_c, bool live) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kr = 2 * (wave * 8 + j) + (lane >> 5);
+    for (int j = 0; j < NB; ++j) {
+      const int g = lw * NB + j;
+      const int kr = 2 * g + (lane >> 5);
       const uint32_t c16 = (uint32_t)((lane & 31) ^ mnc_sw(kr & 3)) * 16u;
       const int row = seg0 + s * BKS + kr;
-      const bool ok = live && tok[j] >= 0;
+      const bool ok = live && s * BKS + kr < seglen && tok[j] >= 0;
       const uint32_t oa = ok ? (uint32_t)row * a_rb + a_c + c16 : OOB;
       const uint32_t ob = ok ? (uint32_t)(GATHER ? tok[j] : row) * b_rb + b_c + c16 : OOB;
-      dma16(ra, sa + (wave * 8 + j) * 1024, oa, 0);
-      dma16(rb, sb + (wave * 8 + j) * 1024, ob, 0);
+      dma16(ra, sa + g * 1024, oa, 0);
+      dma16(rb, sb + g * 1024, ob, 0);
     }
   }
 };
@@ -294,6 +297,32 @@ __device__ __forceinline__ void nt_store16(uint16_t* p, uint4 v) {
   const u32x4_t q = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t*>(p));
 }
+
+// 8-byte LDS store written as an instruction of its own: the compiler cannot
+// tell that no direct-to-LDS load is still writing the address and would
+// otherwise wait for every global access in flight, stores included, first.
+// Callers make sure no such load targets the buffer.
+__device__ __forceinline__ void lds_st64(uint8_t* p, uint32_t lo, uint32_t hi) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)p;
+  const unsigned long long v = ((unsigned long long)hi << 32) | lo;
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
+// Wait until at most N global accesses of this wave are in flight (they
+// complete in issue order).  The builtin, unlike an asm statement, tells the
+// compiler what has completed, so it adds no stricter wait of its own for
+// registers loaded before.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits only for this wave's LDS accesses.
+// __syncthreads() also waits for every global load and store the wave has in
+// flight, which would hold a wave's next stage behind its result stores.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // A 256 x 256 bf16 result tile leaves through a free 64 KB stage buffer in
 // two halves of 128 rows: the waves of the half write their accumulators as
@@ -459,14 +488,136 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
 }
 
 // ------------------------------------------------------------- wgrad --
+constexpr int WG_STORES = 32;  // buffer stores per wave for one bf16 result tile
+
+// One pair of stages of a wgrad K loop.  On entry st0 holds stage s
+// (complete and visible) and the loads of stage s + 1 into st1 are in
+// flight, issued before the last `pending` global accesses of this wave;
+// `tok` holds the tokens of stage (s + 2) % nk.  Each buffer is refilled as
+// soon as every wave has read it: with the stage after next of this N tile,
+// or past its last stage the first stages of the next N tile of the run
+// (zeros after the last).
+template <int PENDING, bool GATHER>
+__device__ __forceinline__ void wgrad_pair(f32x16_t (&acc)[4][4], SegRows<GATHER, 8>& S, uint8_t* __restrict__ st0,
+                                           uint8_t* __restrict__ st1, const MncLane& mla, const MncLane& mlb, int wm,
+                                           int wn, int lane, int w_wave, int s, int nk, uint32_t bc, bool more) {
+  const bool wrap = s + 2 == nk;
+  const uint32_t bn = wrap ? bc + BT * 2u : bc;
+  const bool live = !wrap || more;
+  mma_stage<false, false>(acc, st0, st0 + BOP, mla, mlb, wm, wn, lane);
+  vm_wait<PENDING>();
+  lds_barrier();
+  S.issue(st0, st0 + BOP, w_wave, lane, wrap ? 0 : s + 2, bn, live);
+  S.fetch(wrap ? 1 : s + 3, w_wave, lane);
+  mma_stage<false, false>(acc, st1, st1 + BOP, mla, mlb, wm, wn, lane);
+  vm_wait<0>();
+  lds_barrier();
+  S.issue(st1, st1 + BOP, w_wave, lane, wrap ? 1 : s + 3, bn, live);
+  S.fetch(wrap ? (2 < nk ? 2 : 0) : (s + 4 < nk ? s + 4 : 0), w_wave, lane);
+}
+
+// The K loops and result tiles of one wgrad item (see k_wgrad).  bf16 result
+// tiles leave through a third LDS buffer (stq, 32 KB) in four quarters of 64
+// rows, so both stage buffers keep loading meanwhile: the tile's stores are
+// issued after the loads of the next tile's first two stages and only the
+// wait for the second of those (vmcnt counts in issue order) lets them
+// drain, a whole stage of MFMAs later.
+template <bool GATHER, typename OT>
+__device__ __forceinline__ void wgrad_run(SegRows<GATHER, 8>& S, uint8_t* __restrict__ st0, uint8_t* __restrict__ st1,
+                                          uint8_t* __restrict__ stq, const MncLane& mla, const MncLane& mlb, int wm,
+                                          int wn, int tid, int lane, int w_wave, int m, int n0, int n1, int nk, int Md,
+                                          int Nd, OT* __restrict__ ob) {
+  constexpr bool BF16 = sizeof(OT) == 2;
+  S.fetch(0, w_wave, lane);
+  S.issue(st0, st0 + BOP, w_wave, lane, 0, (uint32_t)n0 * BT * 2u, nk > 0);
+  S.fetch(1, w_wave, lane);
+  S.issue(st1, st1 + BOP, w_wave, lane, 1, (uint32_t)n0 * BT * 2u, nk > 0);
+  S.fetch(2 < nk ? 2 : 0, w_wave, lane);
+  // The token loads may be moved freely (row_token is read-only); pin them
+  // here, so the first pair does not see them as still in flight.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(S.tok[j]));
+  vm_wait<0>();
+  lds_barrier();
+  for (int n = n0; n < n1; ++n) {
+    f32x16_t acc[4][4];
+    zero_acc(acc);
+    const uint32_t bc = (uint32_t)n * BT * 2u;
+    const bool more = n + 1 < n1;
+    // The first pair runs with the previous tile's stores still in flight.
+    // Its stage index is hidden from the compiler: as a constant it would
+    // hoist that pair's load addresses out of the N loop and spill them,
+    // and a reload from scratch would wait for the stores.
+    int s0 = 0;
+    asm volatile("" : "+s"(s0));
+    if (nk > 0)
+      wgrad_pair<BF16 ? WG_STORES : 0>(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s0, nk, bc, more);
+    for (int s = 2; s < nk; s += 2)
+      wgrad_pair<0>(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s, nk, bc, more);
+    // (see mma16 for the accumulator layout)
+    if constexpr (BF16) {
+      // quarter qq: rows 64 qq .. 64 qq + 63 of the tile, held by the waves
+      // with wm = qq / 2 as their 32-row groups i = 2 (qq % 2), + 1; 16-byte
+      // chunk c of row r at chunk c ^ (r % 32); every thread then copies 8
+      // chunks out of full 512-byte rows with non-temporal buffer stores
+      // (columns past Nd are out of range and dropped).
+      const __amdgpu_buffer_rsrc_t ro = rsrc(ob, (uint32_t)Md * (uint32_t)Nd * 2u);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        lds_barrier();
+        if (wm == qq / 2) {
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * (qq % 2) + ii;
+            const int row = ii * 32 + (lane & 31);
+            uint8_t* rp = stq + row * 512 + 8 * (lane >> 5);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int chunk = wn * 16 + j * 4 + q;
+                const float4 v = acc_get4(acc[i][j], q);
+                lds_st64(rp + ((chunk ^ (row & 31)) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+              }
+          }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int rr = 0; rr < WG_STORES / 4; ++rr) {
+          const int idx = rr * BTHREADS + tid, row = idx >> 5, chunk = idx & 31;
+          const uint4 v = *reinterpret_cast<const uint4*>(stq + row * 512 + ((chunk ^ (row & 31)) << 4));
+          const int grow = m * BT + qq * 64 + row, gcol = n * BT + chunk * 8;
+          const uint32_t off = grow < Md && gcol < Nd ? ((uint32_t)grow * (uint32_t)Nd + (uint32_t)gcol) * 2u : OOB;
+          typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+          const u32x4_t q = {v.x, v.y, v.z, v.w};
+          __builtin_amdgcn_raw_buffer_store_b128(q, ro, off, 0, 2);  // 2: non-temporal
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m * BT + wm * 128 + i * 32 + (lane & 31);
+        if (r >= Md) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+            if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
+          }
+      }
+    }
+  }
+}
+
 // dW_e [M, N] = A_e^T B_e over the K-rows of segment e.  An item is (expert,
 // M tile, run of N tiles): one block computes the N tiles of the run one
 // after the other with the same K-rows (the tokens are fetched once per
-// stage index, the A tile is re-read from L2), and the first stage of the
-// next N tile is loaded while the last stage of the current one is
-// multiplied and its results stored, so the pipeline stays full across the
-// run.  Routed experts (a few rows each) take runs of `nch` N tiles; shared
-// experts (every token) one N tile per item, and go first.
+// stage index, the A tile is re-read from L2); the first stage of the next
+// N tile is loaded while the last stage of the current one is multiplied,
+// and a tile's results are stored while the next one is multiplied
+// (wgrad_run).  Routed experts (a few rows each) take runs of `nch` N tiles;
+// shared experts (every token) one N tile per item, and go first.
 // DOWN:  A = dy [P, d] (M = d), B = h [P, I] (N = I)   -> dW2 [E, d, I]
 // !DOWN: A = dab [P, 2I] (M = 2I), B = x [T, d] gathered by row_token (N = d)
 //        -> dW13 [E, 2I, d]
@@ -478,6 +629,7 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
                                                     OT* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP];
+  __shared__ __attribute__((aligned(1024))) uint8_t stq[BOP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ntm = (Md + BT - 1) / BT, ntn = (Nd + BT - 1) / BT;
@@ -507,7 +659,7 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
   }
   const int w_wave = __builtin_amdgcn_readfirstlane(wave);
 
-  SegRows<GATHER> S;
+  SegRows<GATHER, 8> S;
   S.ra = rsrc(a, a_bytes);
   S.rb = rsrc(b, b_bytes);
   S.rt = rsrc(row_token, (uint32_t)P_rows * 4u);
@@ -522,49 +674,10 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
   mlb.init(wn, lane);
   OT* ob = out + (long long)e * Md * Nd;
   // Stages rounded up to an even count (the extra stage loads zeros), so the
-  // two-stage loop body has no branch.  No rows: nk = 0 and zeros are stored.
+  // two-stage loop body has no branch on the stage.  No rows: nk = 0 and
+  // zeros are stored.
   const int nk = (S.seglen + 2 * BKS - 1) / (2 * BKS) * 2;
-  S.fetch(0, w_wave, lane);
-  S.issue(st0, st0 + BOP, w_wave, lane, 0, (uint32_t)n0 * BT * 2u, nk > 0);
-  S.fetch(1, w_wave, lane);
-  for (int n = n0; n < n1; ++n) {
-    f32x16_t acc[4][4];
-    zero_acc(acc);
-    const uint32_t bc = (uint32_t)n * BT * 2u;
-    for (int s = 0; s < nk; s += 2) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      S.issue(st1, st1 + BOP, w_wave, lane, s + 1, bc, true);
-      const bool wrap = s + 2 == nk;  // next: stage 0 of the next N tile of the run
-      S.fetch(wrap ? 0 : s + 2, w_wave, lane);
-      mma_stage<false, false>(acc, st0, st0 + BOP, mla, mlb, wm, wn, lane);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      S.issue(st0, st0 + BOP, w_wave, lane, wrap ? 0 : s + 2, wrap ? bc + BT * 2u : bc, !wrap || n + 1 < n1);
-      S.fetch(wrap ? 1 : s + 3, w_wave, lane);
-      mma_stage<false, false>(acc, st1, st1 + BOP, mla, mlb, wm, wn, lane);
-    }
-    // (see mma16 for the accumulator layout); bf16 results leave through
-    // st1, free here (the last loads went to st0)
-    if constexpr (sizeof(OT) == 2) {
-      store_tile_bf16(acc, st1, reinterpret_cast<uint16_t*>(ob) + (long long)m * BT * Nd + n * BT, Nd, Md - m * BT,
-                      Nd - n * BT, wm, wn, tid, lane);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m * BT + wm * 128 + i * 32 + (lane & 31);
-        if (r >= Md) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
-            if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
-          }
-      }
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wgrad_run(S, st0, st1, stq, mla, mlb, wm, wn, tid, lane, w_wave, m, n0, n1, nk, Md, Nd, ob);
 }
 
 // Blocks of k_wgrad: 8 XCDs x (a share of the shared items + the items of

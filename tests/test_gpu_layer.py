@@ -134,3 +134,22 @@ def test_w8a16_layer_forward():
     assert np.all(np.isfinite(got))
     assert rel_l2(got[ok], o.out[ok]) <= 1e-2
     assert rel_l2(got[ok] - f64_of(u)[ok], (o.out - f64_of(u))[ok]) <= 1e-2
+
+
+def test_moe_forward_one_call_matches_layer():
+    """The one-call moe_forward gives the same output and bias step as
+    MoeLayer on the same inputs (bit for bit: the same kernels)."""
+    cfg = W.CONFIGS["mid_bf16"].with_(T=256, d=512, Nr=16, Ns=1, I=256, K=4)
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    weights = M.ExpertWeights(M.MOE_BF16, w13, w2)
+    u, e, b = W.make_tokens(cfg, 0, "cuda"), W.make_centroids(cfg, "cuda"), W.make_bias(cfg, "cuda")
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, weights, tile_m=32)
+    ref = layer.forward(u, e, b).clone()
+    b_ref = b.clone()
+    layer.update_bias(b_ref, cfg.gamma)
+    b_one = b.clone()
+    out, one = M.moe_forward(u, e, b_one, weights, cfg.K, cfg.Ns, update_bias=True, gamma=cfg.gamma)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(b_one, b_ref)
+    assert torch.equal(one.topk_idx, layer.topk_idx)
