@@ -20,6 +20,16 @@ Reading B1: the selection (top-K of s + b) is piecewise constant, so it gets
 no derivative: gradients flow through the gates of the selected experts
 only, and the bias b gets none.  This holds everywhere except on the
 measure-zero set of exact ties, where the layer is not differentiable.
+
+FP8 variant (ffn_backward_fp8): the same page's "Key ideas" FP8 bullet puts
+every tensor in E4M3 with 1x128 tiles for activations and 128x128 blocks for
+weights.  Reading B2: the two input-gradient products (dh = dy W2 and
+dx = [da | db] W13) take the activation gradient in 1x128 tiles along their
+K axis and the weights in the forward's 128x128 blocks, each tile with its
+power-of-two scale (R10 of oracle/moe.py); the activation gradient is
+rounded to fp32 before it is quantised.  The weight-gradient products stay
+unquantised: their K axis is the token axis, along which the pages give no
+tiling.
 """
 from __future__ import annotations
 
@@ -27,6 +37,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from .e4m3 import dequantize_tiles, quantize_tiles
 from .moe import route, sigmoid
 
 
@@ -76,12 +87,44 @@ def ffn_backward(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray)
     return dx, dw13, dw2, y
 
 
-def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out) -> LayerGrads:
+def fp8_tile_matmul(g: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """g [n, K] @ w [K, N] with both operands in E4M3 (reading B2): g in
+    1x128 tiles along K (rounded to fp32 first), w in 128x128 blocks of its
+    stored layout; the dequantised values (code x power-of-two scale, exact)
+    are multiplied in fp64."""
+    gq, gs = quantize_tiles(np.asarray(g, dtype=np.float64).astype(np.float32), 1, 128)
+    wq, ws = quantize_tiles(np.asarray(w, dtype=np.float64).astype(np.float32), 128, 128)
+    return dequantize_tiles(gq, gs, 1, 128) @ dequantize_tiles(wq, ws, 128, 128)
+
+
+def ffn_backward_fp8(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray):
+    """ffn_backward with the input-gradient products in E4M3 (reading B2):
+    dh = Q(dy) Q(W2), dx = Q([da | db]) Q(W13); the weight gradients use the
+    unquantised dy and [da | db].  Returns (dx, dw13, dw2, y)."""
+    x, w13, w2, dy = _f64(x), _f64(w13), _f64(w2), _f64(dy)
+    I = w2.shape[1]
+    ab = x @ w13.T
+    a, b = ab[:, :I], ab[:, I:]
+    h = silu(a) * b
+    y = h @ w2.T
+    dw2 = dy.T @ h
+    dh = fp8_tile_matmul(dy, w2)
+    da = dh * b * silu_grad(a)
+    db = dh * silu(a)
+    dab = np.concatenate([da, db], axis=1)
+    dw13 = dab.T @ x
+    dx = fp8_tile_matmul(dab, w13)
+    return dx, dw13, dw2, y
+
+
+def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out, fp8_dgrad: bool = False) -> LayerGrads:
     """Gradients of L = sum(grad_out * out) for the layer of
     oracle.moe.layer_forward (bf16 / fp32 path, no FP8 quantisation).
 
     u [T, d], e [N_r, d], b [N_r], w13 [N_r+N_s, 2I, d], w2 [N_r+N_s, d, I],
-    grad_out [T, d] = dL/dout."""
+    grad_out [T, d] = dL/dout.  fp8_dgrad: every expert's backward is
+    ffn_backward_fp8 instead of ffn_backward."""
+    ffn_bwd = ffn_backward_fp8 if fp8_dgrad else ffn_backward
     u, e, G = _f64(u), _f64(e), _f64(grad_out)
     w13, w2 = _f64(w13), _f64(w2)
     T, d = u.shape
@@ -93,7 +136,7 @@ def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out) -> Laye
 
     # shared experts: gate 1 (R7), every token
     for j in range(Ns):
-        dx, dw13[Nr + j], dw2[Nr + j], _ = ffn_backward(u, w13[Nr + j], w2[Nr + j], G)
+        dx, dw13[Nr + j], dw2[Nr + j], _ = ffn_bwd(u, w13[Nr + j], w2[Nr + j], G)
         du_ffn += dx
 
     # routed experts: the output gradient reaches FFN_i scaled by the gate;
@@ -103,7 +146,7 @@ def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out) -> Laye
         if t_sel.size == 0:
             continue
         dy = r.gate[t_sel, k_sel][:, None] * G[t_sel]
-        dx, dw13[i], dw2[i], y = ffn_backward(u[t_sel], w13[i], w2[i], dy)
+        dx, dw13[i], dw2[i], y = ffn_bwd(u[t_sel], w13[i], w2[i], dy)
         np.add.at(du_ffn, t_sel, dx)
         dgate[t_sel, k_sel] = np.sum(G[t_sel] * y, axis=1)
 

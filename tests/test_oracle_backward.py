@@ -122,3 +122,103 @@ def test_gate_gradient_sums_to_zero_over_a_token():
     gr = B.layer_backward(p["u"], p["e"], p["b"], p["w13"], p["w2"], c["Nr"], c["Ns"], c["K"], p["G"])
     ds = gr.dz / (r.score * (1 - r.score))
     np.testing.assert_allclose(np.sum(r.score * ds, axis=1), 0.0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ FP8 --
+# fp8_tile_matmul (reading B2) against what the E4M3 format and the tile
+# scaling fix, without calling the oracle's quantiser from the test.
+
+def _e4m3_grid_values(rng, shape):
+    """Random finite E4M3FN values, decoded from the format's fields here:
+    sign, 4-bit exponent (bias 7), 3-bit mantissa; exponent 15 with mantissa
+    7 is NaN and left out, exponent 0 is subnormal."""
+    e = rng.integers(0, 16, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    m = np.where((e == 15) & (m == 7), 6, m)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.where(rng.integers(0, 2, size=shape) == 1, -mag, mag)
+
+
+def _on_grid(rng, rows, cols, tile_rows, tile_cols, kmin=-4, kmax=4):
+    """A matrix whose every tile holds E4M3 values times its own 2^k, with one
+    entry of magnitude 448 * 2^k, so that the tile's scale is 2^k and every
+    entry is a code times the scale."""
+    x = _e4m3_grid_values(rng, (rows, cols))
+    for r0 in range(0, rows, tile_rows):
+        for c0 in range(0, cols, tile_cols):
+            k = int(rng.integers(kmin, kmax + 1))
+            t = x[r0:r0 + tile_rows, c0:c0 + tile_cols]
+            t[rng.integers(0, t.shape[0]), rng.integers(0, t.shape[1])] = 448.0 * (1 if rng.random() < .5 else -1)
+            x[r0:r0 + tile_rows, c0:c0 + tile_cols] = t * 2.0 ** k
+    return x
+
+
+def test_fp8_tile_matmul_is_exact_on_the_grid():
+    """Operands that the tile quantisation represents exactly give exactly
+    the fp64 product.  Each 1x128 tile of g and each 128x128 block of w has
+    its own exponent, so tiles taken along the wrong axis, or of the wrong
+    size, would mix exponents and round the smaller entries."""
+    rng = np.random.default_rng(5)
+    g = _on_grid(rng, 48, 384, 1, 128)
+    w = _on_grid(rng, 384, 256, 128, 128)
+    assert np.array_equal(B.fp8_tile_matmul(g, w), g @ w)
+    # the identity is exact in 128x128 blocks, so g comes back unchanged
+    assert np.array_equal(B.fp8_tile_matmul(g, np.eye(384)), g)
+    # tiles whose scale changes inside a 128x128 block are not exact
+    w_bad = w.copy()
+    w_bad[:, :128] = _on_grid(rng, 384, 128, 1, 128)  # scales vary inside a 128x128 block
+    assert not np.array_equal(B.fp8_tile_matmul(g, w_bad), g @ w_bad)
+
+
+def test_fp8_tile_matmul_error_within_the_rounding_bound():
+    """Random operands: every entry is off by at most half an E4M3 step of
+    its tile (relative 2^-4 for normal codes, 2^-10 of the scale below
+    2^-6), so each product entry is within sum |g| e_w + e_g |w| + e_g e_w."""
+    rng = np.random.default_rng(6)
+    g = rng.standard_normal((40, 256)) * np.exp(rng.standard_normal((40, 1)))
+    w = rng.standard_normal((256, 384)) / 16
+    got = B.fp8_tile_matmul(g, w)
+    want = g @ w
+
+    def step_bound(x, tile_rows, tile_cols):
+        rows, cols = x.shape
+        t = np.abs(x).reshape(rows // tile_rows, tile_rows, cols // tile_cols, tile_cols).max(axis=(1, 3))
+        s = 2.0 ** np.ceil(np.log2(t / 448.0))          # the smallest 2^k with amax <= 448 * 2^k
+        s = np.repeat(np.repeat(s, tile_rows, 0), tile_cols, 1)
+        return np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10)
+
+    eg, ew = step_bound(g.astype(np.float32).astype(np.float64), 1, 128), step_bound(w, 128, 128)
+    bound = np.abs(g) @ ew + eg @ np.abs(w) + eg @ ew
+    assert np.all(np.abs(got - want) <= bound * (1 + 1e-12) + 1e-300)
+    assert np.linalg.norm(got - want) / np.linalg.norm(want) < 0.05
+
+
+def test_fp8_ffn_backward_weight_gradients_and_closeness():
+    """ffn_backward_fp8 keeps the weight gradient of W2 unquantised (equal to
+    ffn_backward's), and its input gradient stays within the E4M3 error of
+    the exact one."""
+    rng = np.random.default_rng(7)
+    n, d, I = 64, 256, 128
+    x = rng.standard_normal((n, d))
+    w13 = rng.standard_normal((2 * I, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((d, I)) / np.sqrt(I)
+    dy = rng.standard_normal((n, d))
+    dx8, dw13_8, dw2_8, y8 = B.ffn_backward_fp8(x, w13, w2, dy)
+    dx, dw13, dw2, y = B.ffn_backward(x, w13, w2, dy)
+    assert np.array_equal(dw2_8, dw2) and np.array_equal(y8, y)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel(dx8, dx) < 0.06 and rel(dw13_8, dw13) < 0.06
+    assert rel(dx8, dx) > 1e-4  # the quantisation did happen
+
+
+def test_fp8_layer_backward_switch():
+    """layer_backward(fp8_dgrad=True) changes only what flows through the
+    expert input gradients: the gate and score gradients and dW2 are those of
+    the exact backward."""
+    p = tiny_inputs(3, T=6, d=256, Nr=4, Ns=1, I=128, K=2)
+    g = B.layer_backward(p["u"], p["e"], p["b"], p["w13"], p["w2"], 4, 1, 2, p["G"])
+    g8 = B.layer_backward(p["u"], p["e"], p["b"], p["w13"], p["w2"], 4, 1, 2, p["G"], fp8_dgrad=True)
+    assert np.array_equal(g8.dgate, g.dgate) and np.array_equal(g8.dz, g.dz) and np.array_equal(g8.dw2, g.dw2)
+    assert np.array_equal(g8.du_router, g.du_router) and np.array_equal(g8.de, g.de)
+    assert not np.array_equal(g8.du_ffn, g.du_ffn)
+    assert np.linalg.norm(g8.du - g.du) / np.linalg.norm(g.du) < 0.05
