@@ -52,6 +52,9 @@ def parse():
                    help="target length of the oracle's timed CPU work (the sample is sized for it)")
     p.add_argument("--train", action="store_true",
                    help="time the training step instead: training forward + backward (bf16 workloads)")
+    p.add_argument("--dgrad-fp8", action="store_true",
+                   help="with --train: the backward's input-gradient products on E4M3 operands "
+                        "(moe_expert_gemm_backward_w8; E4M3 weights prepared once at set-up)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (calibrates HBM byte counters) and exit")
     return p.parse_args()
@@ -359,9 +362,10 @@ def train_main(args, cfg, dev, stream):
     us = [W.make_tokens(cfg, s, dev) for s in range(n_u)]
     gs = [W.make_free((cfg.T, cfg.d), 1.0, 100 + s, dev, torch.bfloat16) for s in range(n_u)]
     w13, w2 = W.make_expert_weights(cfg, dev)
+    w8 = M.quantize_weights(w13, w2) if args.dgrad_fp8 else None
     layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16,
                        M.ExpertWeights(M.MOE_BF16, w13, w2), tile_m=args.tile_m, device=dev, train=True,
-                       grad_dtype=torch.bfloat16)
+                       grad_dtype=torch.bfloat16, dgrad_weights=w8)
     torch.cuda.synchronize()
     bias = bias0.clone()
     bwd_events = []
@@ -375,9 +379,14 @@ def train_main(args, cfg, dev, stream):
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
             ev0.record(stream)
-        M.moe_expert_gemm_backward(u, w13, w2, layer.h, layer.ab, layer.dy, cfg.T, cfg.K, cfg.Nr, cfg.Ns, cfg.d,
-                                   cfg.I, args.tile_m, layer.seg_offset, layer.row_token, layer.tile_map,
-                                   layer.n_tiles, layer.bwd_ws, layer.dx, layer.dw13, layer.dw2)
+        if w8 is None:
+            M.moe_expert_gemm_backward(u, w13, w2, layer.h, layer.ab, layer.dy, cfg.T, cfg.K, cfg.Nr, cfg.Ns, cfg.d,
+                                       cfg.I, args.tile_m, layer.seg_offset, layer.row_token, layer.tile_map,
+                                       layer.n_tiles, layer.bwd_ws, layer.dx, layer.dw13, layer.dw2)
+        else:
+            M.moe_expert_gemm_backward_w8(u, w8, layer.h, layer.ab, layer.dy, cfg.T, cfg.K, cfg.Nr, cfg.Ns, cfg.d,
+                                          cfg.I, args.tile_m, layer.seg_offset, layer.row_token, layer.tile_map,
+                                          layer.n_tiles, layer.bwd_ws, layer.dx, layer.dw13, layer.dw2)
         if timed:
             ev1.record(stream)
             bwd_events.append((ev0, ev1))
@@ -400,10 +409,20 @@ def train_main(args, cfg, dev, stream):
     step_flops = 18.0 * cfg.d * cfg.I * rows
     loads = layer.expert_load.cpu().numpy().astype(np.int64)
     achieved = bwd_flops / (bwd_ms * 1e-3)
-    roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK["bf16"] / 1e12, "unit": "TFLOP/s",
-            "frac": achieved / PEAK["bf16"], "traffic": None,
-            "kernel": "moe_expert_gemm_backward call: k_dgrad (down + SwiGLU backward), k_dgrad (gate/up), "
-                      "k_wgrad (down), k_wgrad (gate/up)",
+    if w8 is None:
+        peak = PEAK["bf16"]
+        kernels = ("moe_expert_gemm_backward call: k_dgrad (down + SwiGLU backward), k_dgrad (gate/up), "
+                   "k_wgrad (down), k_wgrad (gate/up)")
+    else:
+        # half the flops (the input-gradient products) at the E4M3 peak, half
+        # (the weight gradients) at the bf16 peak: the call's time at peak
+        # gives its effective peak rate
+        peak = bwd_flops / (0.5 * bwd_flops / PEAK["fp8"] + 0.5 * bwd_flops / PEAK["bf16"])
+        kernels = ("moe_expert_gemm_backward_w8 call: k_quant_1x128 (dy), k_dgrad8 (down + SwiGLU backward), "
+                   "k_quant_1x128 ([da|db]), k_dgrad8 (gate/up), k_wgrad (down), k_wgrad (gate/up); peak = the "
+                   "call's flops over their time at the E4M3 (dgrad) and bf16 (wgrad) peaks")
+    roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": None, "kernel": kernels,
             "units_per_launch": {"rows": rows, "flops": bwd_flops}, "avg_launch_ms": bwd_ms}
     out = {
         "metric": TRAIN_METRIC,
@@ -416,11 +435,13 @@ def train_main(args, cfg, dev, stream):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w8 is None else "bf16 + e4m3 dgrad",
         "data": "synthetic (seeded; random-init expert weights and centroids, seeded bf16 output gradients)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "Nr": cfg.Nr, "Ns": cfg.Ns, "I": cfg.I,
                    "K": cfg.K, "routing": cfg.routing, "weights": cfg.weights, "tile_m": args.tile_m,
-                   "step": "training forward + backward + bias rule", "grad_dtype": "bf16",
+                   "step": "training forward + backward + bias rule" + (
+                       "; backward input-gradient products on E4M3 (weights quantised once at set-up, "
+                       "not in the step)" if w8 is not None else ""), "grad_dtype": "bf16",
                    "parallelism": "single GPU"},
         "layer": {"tflops": step_flops / (ms_step * 1e-3) / 1e12,
                   "mfma_frac": step_flops / (ms_step * 1e-3) / PEAK["bf16"],
@@ -428,11 +449,12 @@ def train_main(args, cfg, dev, stream):
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_train(cfg, us[0], gs[0], e, bias0, w13, w2, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_train(cfg, us[0], gs[0], e, bias0, w13, w2, args.cpu_seconds,
+                                                 fp8=w8 is not None)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds):
+def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds, fp8=False):
     """Time the fp64 backward oracle's expert FFN backward (oracle/backward.py
     ffn_backward, the dominant part of the layer backward) on the first S
     tokens: for every expert their rows select, dx, dW13, dW2 of those rows.
@@ -464,11 +486,12 @@ def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds):
             ts, ks = np.nonzero(r.idx == i)
             x, dy = u_s[ts], r.gate[ts, ks][:, None] * G_s[ts]
         t1 = time.perf_counter()
-        OB.ffn_backward(x, w13_i, w2_i, dy)
+        (OB.ffn_backward_fp8 if fp8 else OB.ffn_backward)(x, w13_i, w2_i, dy)
         total += time.perf_counter() - t1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": S / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 SwiGLU FFN backward (forward recomputed, "
+            "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 SwiGLU FFN backward"
+                      f"{' with E4M3 input-gradient products' if fp8 else ''} (forward recomputed, "
                       f"dx, dW13, dW2) of the {cfg.K} routed + {cfg.Ns} shared experts of each token, "
                       f"{len(need)} experts touched; routing, gate and centroid gradients not timed",
             "seconds": total, "host_cpus": os.cpu_count(), **host_info()}

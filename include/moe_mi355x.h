@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Limits of this implementation. */
 #define MOE_MAX_EXPERTS 1024   /* routed + shared experts */
@@ -334,6 +334,36 @@ moe_status moe_expert_gemm_backward(const void* x, const void* w13, const void* 
                                     const int32_t* tile_map, const int32_t* n_tiles,
                                     void* ws, size_t ws_bytes, void* dx,
                                     void* dw13, void* dw2, moe_dtype dw_t, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_expert_gemm_backward_w8: moe_expert_gemm_backward with the two
+ * input-gradient products on E4M3 operands, after [RG-FP8] (E4M3
+ * everywhere, 1x128 tiles for activations, 128x128 blocks for weights):
+ * dy and then [da | db] are quantised in 1x128
+ * tiles along their K axis (d, 2I) with power-of-two scales, and multiply
+ * the E4M3 weights of the forward, block-scaled E8M0 on the matrix cores:
+ *   dh = Q(dy) Q(W2),  dx = Q([da | db]) Q(W13)
+ * The weight gradients are those of moe_expert_gemm_backward (bf16 dy,
+ * [da | db], h, x): their K axis is the token axis, for which the pages give
+ * no tiling.
+ *   w13, w13_scale device E4M3 [Nr+Ns, 2I, d] with fp32 [Nr+Ns, 2I/128,
+ *                  d/128] block scales, w2, w2_scale [Nr+Ns, d, I] with
+ *                  [Nr+Ns, d/128, I/128] (as fp8_quantize_tiles writes them
+ *                  with 128x128 tiles; powers of two)
+ *   ws             device, moe_gemm_backward_w8_workspace_bytes(...) bytes
+ *   every other argument as moe_expert_gemm_backward
+ *   Errors: as moe_expert_gemm_backward; MOE_EUNSUPPORTED also for
+ *   d > 16384 or I > 8192.
+ * ---------------------------------------------------------------------- */
+size_t moe_gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status moe_expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale,
+                                       const uint8_t* w2, const float* w2_scale,
+                                       const void* h, const void* ab, const void* dy,
+                                       int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                       const int32_t* seg_offset, const int32_t* row_token,
+                                       const int32_t* tile_map, const int32_t* n_tiles,
+                                       void* ws, size_t ws_bytes, void* dx,
+                                       void* dw13, void* dw2, moe_dtype dw_t, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_route_backward: the layer's input and centroid gradients.

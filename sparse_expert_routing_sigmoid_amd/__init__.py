@@ -49,6 +49,8 @@ SIGNATURES = {
     "moe_combine_backward": (_i, [_vp, _i, _vp, _i] + [_vp] * 4 + [_i] * 5 + [_vp] * 5),
     "moe_gemm_backward_workspace_bytes": (_sz, [_i] * 7),
     "moe_expert_gemm_backward": (_i, [_vp] * 6 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
+    "moe_gemm_backward_w8_workspace_bytes": (_sz, [_i] * 7),
+    "moe_expert_gemm_backward_w8": (_i, [_vp] * 8 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
     "moe_route_backward": (_i, [_vp, _i, _vp, _vp, _i] + [_vp] * 7 + [_i] * 5 + [_vp, _i, _vp, _vp]),
 }
 
@@ -195,6 +197,23 @@ def moe_expert_gemm_backward(x, w13, w2, h, ab, dy, T, K, Nr, Ns, d, I, tile_m, 
                                           dtype_code(dw13), _stream(stream)))
 
 
+def moe_gemm_backward_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m):
+    return lib().moe_gemm_backward_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m)
+
+
+def moe_expert_gemm_backward_w8(x, w8: "ExpertWeights", h, ab, dy, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token,
+                                tile_map, n_tiles, ws, dx, dw13, dw2, stream=None):
+    """moe_expert_gemm_backward with the input-gradient products on E4M3
+    operands; w8: the E4M3 expert weights (quantize_weights)."""
+    if w8.w_t != MOE_E4M3:
+        raise ValueError("moe_expert_gemm_backward_w8 needs E4M3 weights")
+    _check(lib().moe_expert_gemm_backward_w8(_ptr(x), _ptr(w8.w13), _ptr(w8.w13_scale), _ptr(w8.w2),
+                                             _ptr(w8.w2_scale), _ptr(h), _ptr(ab), _ptr(dy), T, K, Nr, Ns, d, I,
+                                             tile_m, _ptr(seg_offset), _ptr(row_token), _ptr(tile_map),
+                                             _ptr(n_tiles), _ptr(ws), _nbytes(ws), _ptr(dx), _ptr(dw13), _ptr(dw2),
+                                             dtype_code(dw13), _stream(stream)))
+
+
 def moe_route_backward(grad_out, dx, u, centroids, topk_idx, inv_row, dz, dz_row, seg_offset, row_token, Nr, Ns,
                        du, de, stream=None):
     T, d = u.shape
@@ -260,7 +279,7 @@ class MoeLayer:
     synchronisation happens inside forward()."""
 
     def __init__(self, T, d, Nr, Ns, I, K, act_dtype, weights: ExpertWeights, x_fp8=False,
-                 tile_m=32, out_dtype=None, device="cuda", train=False, grad_dtype=None):
+                 tile_m=32, out_dtype=None, device="cuda", train=False, grad_dtype=None, dgrad_weights=None):
         self.T, self.d, self.Nr, self.Ns, self.I, self.K = T, d, Nr, Ns, I, K
         self.tile_m, self.x_fp8, self.w = tile_m, x_fp8, weights
         dev = torch.device(device)
@@ -309,8 +328,13 @@ class MoeLayer:
             self.dgate = torch.empty((T, K), **f32)
             self.dz = torch.empty((T, K), **f32)
             self.dz_row = torch.empty((P,), **f32)
-            self.bwd_ws = torch.empty((max(moe_gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tile_m), 1),),
-                                      dtype=torch.uint8, device=dev)
+            # dgrad_weights: E4M3 copies of the weights (quantize_weights); the
+            # backward then runs its input-gradient products on E4M3 operands
+            self.dgrad_w = dgrad_weights
+            if dgrad_weights is not None and dgrad_weights.w_t != MOE_E4M3:
+                raise ValueError("dgrad_weights must be E4M3 weights")
+            ws_fn = moe_gemm_backward_workspace_bytes if dgrad_weights is None else moe_gemm_backward_w8_workspace_bytes
+            self.bwd_ws = torch.empty((max(ws_fn(T, K, Nr, Ns, d, I, tile_m), 1),), dtype=torch.uint8, device=dev)
             self.dw13 = torch.empty((E, 2 * I, d), dtype=gd, device=dev)
             self.dw2 = torch.empty((E, d, I), dtype=gd, device=dev)
             self.du = torch.empty((T, d), dtype=act_dtype, device=dev)
@@ -359,9 +383,14 @@ class MoeLayer:
         w = self.w
         moe_combine_backward(grad_out, self.y, self.inv_row, self.topk_gate, self.topk_score, self.seg_offset,
                              self.Nr, self.Ns, self.dy, self.dgate, self.dz, self.dz_row, stream)
-        moe_expert_gemm_backward(u, w.w13, w.w2, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns, self.d,
-                                 self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map, self.n_tiles,
-                                 self.bwd_ws, self.dx, self.dw13, self.dw2, stream)
+        if self.dgrad_w is None:
+            moe_expert_gemm_backward(u, w.w13, w.w2, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns,
+                                     self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map,
+                                     self.n_tiles, self.bwd_ws, self.dx, self.dw13, self.dw2, stream)
+        else:
+            moe_expert_gemm_backward_w8(u, self.dgrad_w, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns,
+                                        self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map,
+                                        self.n_tiles, self.bwd_ws, self.dx, self.dw13, self.dw2, stream)
         moe_route_backward(grad_out, self.dx, u, centroids, self.topk_idx, self.inv_row, self.dz, self.dz_row,
                            self.seg_offset, self.row_token, self.Nr, self.Ns, self.du, self.de, stream)
         return self.du, self.de, self.dw13, self.dw2

@@ -45,6 +45,13 @@ moe_status expert_gemm_backward(const void* x, const void* w13, const void* w2, 
                                 const int32_t* seg_offset, const int32_t* row_token, const int32_t* tile_map,
                                 const int32_t* n_tiles, void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2,
                                 moe_dtype dw_t, void* stream);
+size_t gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                   const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
+                                   int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                   const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                   void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
+                                   void* stream);
 moe_status route_backward(const void* grad_out, moe_dtype g_t, const void* dx, const void* u, moe_dtype u_t,
                           const float* centroids, const int32_t* topk_idx, const int32_t* inv_row, const float* dz,
                           const float* dz_row, const int32_t* seg_offset, const int32_t* row_token, int T, int d,
@@ -179,6 +186,22 @@ moe_status moe_expert_gemm_backward(const void* x, const void* w13, const void* 
   moe::clear_error();
   return moe::expert_gemm_backward(x, w13, w2, h, ab, dy, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token, tile_map,
                                    n_tiles, ws, ws_bytes, dx, dw13, dw2, dw_t, stream);
+}
+
+size_t moe_gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  return moe::gemm_backward_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m);
+}
+
+moe_status moe_expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                       const float* w2_scale, const void* h, const void* ab, const void* dy, int T,
+                                       int K, int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                       void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
+                                       void* stream) {
+  moe::clear_error();
+  return moe::expert_gemm_backward_w8(x, w13, w13_scale, w2, w2_scale, h, ab, dy, T, K, Nr, Ns, d, I, tile_m,
+                                      seg_offset, row_token, tile_map, n_tiles, ws, ws_bytes, dx, dw13, dw2, dw_t,
+                                      stream);
 }
 
 moe_status moe_route_backward(const void* grad_out, moe_dtype g_t, const void* dx, const void* u, moe_dtype u_t,

@@ -31,6 +31,12 @@ void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const ui
                                 int Nr, int cap, uint16_t* h, uint16_t* ab, void* y, bool y_f32, int* sched,
                                 hipStream_t st);
 bool ffn_bwd_ok(int d, int I);
+bool ffn_bwd_w8_ok(int d, int I);
+void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
+                       const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
+                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
+                       int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
+                       uint8_t* dabq, float* dabs, uint16_t* dx, void* dw13, void* dw2, bool dw_f32, hipStream_t st);
 void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const uint16_t* h,
                          const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset, const int32_t* row_token,
                          const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d,
@@ -373,6 +379,60 @@ moe_status expert_gemm_backward(const void* x, const void* w13, const void* w2, 
                       Ns, static_cast<uint16_t*>(ws), static_cast<uint16_t*>(dx), dw13, dw2, dw_t == MOE_F32,
                       as_stream(stream));
   return launch_status("moe_expert_gemm_backward");
+}
+
+// Workspace of the E4M3-dgrad backward: [da | db] bf16, its E4M3 codes, the
+// codes of dy, then the fp32 1x128 scales of both, each part 256-byte aligned.
+struct W8Ws {
+  size_t dab, dabq, dyq, dabs, dys, total;
+  W8Ws(size_t P, int d, int I) {
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    dab = 0;
+    dabq = dab + up(P * 2 * I * 2);
+    dyq = dabq + up(P * 2 * I);
+    dabs = dyq + up(P * d);
+    dys = dabs + up(P * (2 * I / 128) * 4);
+    total = dys + up(P * (d / 128) * 4);
+  }
+};
+
+size_t gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  if (T < 0 || d < 128 || I < 64 || Nr < 1 || Ns < 0 || K < 1 || tile_m < 1) return 0;
+  return W8Ws(permute_rows(T, K, Nr, Ns, tile_m), d, I).total;
+}
+
+moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                   const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
+                                   int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                   const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                   void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
+                                   void* stream) {
+  const moe_status cs = check_layer(T, K, Nr, Ns, d, I, tile_m);
+  if (cs != MOE_OK) return cs;
+  MOE_REQUIRE(dw_t == MOE_F32 || dw_t == MOE_BF16, MOE_EINVAL, "dw_t must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(w13 && w13_scale && w2 && w2_scale && seg_offset && row_token && tile_map && n_tiles && dw13 && dw2,
+              MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(T == 0 || (x && h && ab && dy && dx), MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(w13) && aligned16(w2) && aligned16(h) && aligned16(ab) && aligned16(dy) &&
+                  aligned16(ws) && aligned16(dx) && aligned16(dw13) && aligned16(dw2),
+              MOE_EINVAL, "data tensors and ws must be 16-byte aligned");
+  MOE_REQUIRE(ffn_bwd_w8_ok(d, I), MOE_EUNSUPPORTED,
+              "E4M3 backward needs d % 256 == 0, I % 128 == 0, d <= 16384 and I <= 8192");
+  const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
+  MOE_REQUIRE(fits31((unsigned long long)T * d * 2) && fits31((unsigned long long)P * d * 2) &&
+                  fits31((unsigned long long)P * 2 * I * 2) && fits31((unsigned long long)2 * I * d * 2),
+              MOE_EUNSUPPORTED, "backward: operand of 2 GiB or more");
+  const W8Ws L(P, d, I);
+  MOE_REQUIRE(ws && ws_bytes >= L.total, MOE_EWORKSPACE, "workspace smaller than moe_gemm_backward_w8_workspace_bytes");
+  if (T == 0) return MOE_OK;
+  const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
+  uint8_t* wb = static_cast<uint8_t*>(ws);
+  launch_ffn_bwd_w8(cp<uint16_t>(x), w13, w13_scale, w2, w2_scale, cp<uint16_t>(h), cp<uint16_t>(ab),
+                    cp<uint16_t>(dy), seg_offset, row_token, tile_map, n_tiles, tiles_max, T, (long long)P, d, I, Nr,
+                    Ns, reinterpret_cast<uint16_t*>(wb + L.dab), wb + L.dyq, reinterpret_cast<float*>(wb + L.dys),
+                    wb + L.dabq, reinterpret_cast<float*>(wb + L.dabs), static_cast<uint16_t*>(dx), dw13, dw2,
+                    dw_t == MOE_F32, as_stream(stream));
+  return launch_status("moe_expert_gemm_backward_w8");
 }
 
 moe_status route_backward(const void* grad_out, moe_dtype g_t, const void* dx, const void* u, moe_dtype u_t,

@@ -30,6 +30,9 @@
 
 namespace moe {
 
+moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long long cols, int tile_rows, int tile_cols,
+                          uint8_t* q, float* scale, void* stream);
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -366,37 +369,11 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16_t (&acc)[4][4], uin
 }
 
 // ------------------------------------------------------------- dgrad --
-// K loop and epilogue of one dgrad item for a wave with MT live 32-row
-// groups (all instantiations run the same barriers).
-template <bool SWIGLU, typename OT, int MT>
-__device__ __forceinline__ void dgrad_run(const KcRows& A, const MncRows& B, uint8_t* __restrict__ st0,
-                                          uint8_t* __restrict__ st1, const MncLane& mlb, int wm, int wn, int tid,
-                                          int lane, int w_wave, int Kd, int Nd, int n, int row0, int rows,
-                                          const uint16_t* __restrict__ ab, OT* __restrict__ out) {
-  f32x16_t acc[4][4];
-  zero_acc(acc);
-  // Kd % 128 == 0, so the stage count is even and the loop body, two stages
-  // that name their buffers, has no branch: a branch lets the compiler sink
-  // MFMAs past the next barrier and costs registers.  The final issue loads
-  // zeros (out of range) into a buffer nobody reads.
-  const int nk = Kd / BKS;
-  A.issue(st0, w_wave, 0, 0u);
-  B.issue(st0 + BOP, w_wave, 0, 0u);
-  for (int s = 0; s < nk; s += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    A.issue(st1, w_wave, s + 1, 0u);
-    B.issue(st1 + BOP, w_wave, s + 1, 0u);
-    mma_stage<true, false, MT>(acc, st0, st0 + BOP, mlb, mlb, wm, wn, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint32_t oob = s + 2 < nk ? 0u : OOB;
-    A.issue(st0, w_wave, s + 2, oob);
-    B.issue(st0 + BOP, w_wave, s + 2, oob);
-    mma_stage<true, false, MT>(acc, st1, st1 + BOP, mlb, mlb, wm, wn, lane);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
+// Epilogue of a dgrad item, shared by the bf16 and E4M3 kernels.
+template <bool SWIGLU, typename OT>
+__device__ __forceinline__ void dgrad_epilogue(const f32x16_t (&acc)[4][4], uint8_t* __restrict__ st1, int wm, int wn,
+                                               int tid, int lane, int Nd, int n, int row0, int rows,
+                                               const uint16_t* __restrict__ ab, OT* __restrict__ out) {
   // Epilogue (see mma16 for the accumulator layout): column c of the tile is
   // output column n * 256 + c; rows past the tile's token rows and columns
   // past Nd are not written.  dx goes out through LDS (st1 is free: the last
@@ -435,6 +412,280 @@ __device__ __forceinline__ void dgrad_run(const KcRows& A, const MncRows& B, uin
 }
 
 
+// K loop and epilogue of one dgrad item for a wave with MT live 32-row
+// groups (all instantiations run the same barriers).
+template <bool SWIGLU, typename OT, int MT>
+__device__ __forceinline__ void dgrad_run(const KcRows& A, const MncRows& B, uint8_t* __restrict__ st0,
+                                          uint8_t* __restrict__ st1, const MncLane& mlb, int wm, int wn, int tid,
+                                          int lane, int w_wave, int Kd, int Nd, int n, int row0, int rows,
+                                          const uint16_t* __restrict__ ab, OT* __restrict__ out) {
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+  // Kd % 128 == 0, so the stage count is even and the loop body, two stages
+  // that name their buffers, has no branch: a branch lets the compiler sink
+  // MFMAs past the next barrier and costs registers.  The final issue loads
+  // zeros (out of range) into a buffer nobody reads.
+  const int nk = Kd / BKS;
+  A.issue(st0, w_wave, 0, 0u);
+  B.issue(st0 + BOP, w_wave, 0, 0u);
+  for (int s = 0; s < nk; s += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    A.issue(st1, w_wave, s + 1, 0u);
+    B.issue(st1 + BOP, w_wave, s + 1, 0u);
+    mma_stage<true, false, MT>(acc, st0, st0 + BOP, mlb, mlb, wm, wn, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t oob = s + 2 < nk ? 0u : OOB;
+    A.issue(st0, w_wave, s + 2, oob);
+    B.issue(st0 + BOP, w_wave, s + 2, oob);
+    mma_stage<true, false, MT>(acc, st1, st1 + BOP, mlb, mlb, wm, wn, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  dgrad_epilogue<SWIGLU, OT>(acc, st1, wm, wn, tid, lane, Nd, n, row0, rows, ab, out);
+}
+
+// ------------------------------------------------------------ E4M3 dgrad --
+// The dgrad products with E4M3 operands: the activation gradient in 1x128
+// tiles along K (a power-of-two scale per row and 128 K), the weights in
+// 128x128 blocks (one power-of-two scale per block), as the forward's FP8
+// path.  A stage is one scale block of K: 128 K values, so a K-contiguous
+// row is 128 bytes as in the bf16 kernels (KcRows serves unchanged) and an
+// M/N-contiguous weight tile is 128 K-rows of 256 bytes.  The
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes, per lane, 32 bytes of K and the
+// E8M0 exponent of their scale: the weight block's for the first operand,
+// the row's for the second, so the scaling is exact and free.
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
+
+constexpr int BSC = 1024;  // bytes of the 256 row scales (fp32) of an E4M3 stage
+
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xFF); }
+
+// M/N-contiguous E4M3 tiles (128 K-rows x 256 bytes): 16-byte chunk c of
+// K-row kr is stored at chunk c ^ f8_sw(kr % 8).  A transposing 8-bit read
+// takes 16 bytes from each of 8 K-rows (16 lanes); with f8_sw the 8 pieces
+// fall on distinct banks, and the pieces of two neighbouring lane groups
+// (columns +16) on the other 8 chunk positions of a 256-byte row, so the
+// read is conflict-free whether the LDS serves 16 lanes over 128 bytes or
+// 32 lanes over 256 bytes per cycle.
+__host__ __device__ constexpr int f8_sw(int y) { return 2 * y + (y >> 2); }
+
+// Weight loads: block g (1 KB) of the stage holds K-rows 4 g .. 4 g + 3;
+// lane l writes K-row 4 g + l / 16, physical chunk l % 16.
+struct MncRows8 {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off[8];
+  uint32_t kstride;  // bytes per stage (128 K-rows)
+  __device__ void init(const void* base, uint32_t bytes, uint32_t row_bytes, int col0, int wave, int lane) {
+    r = rsrc(base, bytes);
+    kstride = row_bytes * 128u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kr = 4 * (wave * 8 + j) + (lane >> 4);
+      const uint32_t c = (uint32_t)((lane & 15) ^ f8_sw(kr & 7));
+      off[j] = (uint32_t)kr * row_bytes + (uint32_t)col0 + c * 16u;
+    }
+  }
+  __device__ void issue(uint8_t* st, int wave, int s, uint32_t oob) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(r, st + (wave * 8 + j) * 1024, off[j] | oob, (uint32_t)s * kstride);
+  }
+};
+
+// Fragment of the weight tile for MFMA tile jt (columns 32 jt .. + 31 of the
+// wave's 128) and k-step kk (64 K): lane l gets column l % 32 and K values
+// 32 (l / 32) .. + 31 of the step, in K order, by four transposing reads of
+// 8 K-rows.  In a 16-lane group g, lane t names K-row 32 (g / 2) + t / 2
+// (+ 8 per read) and 8 bytes at column 16 (g % 2) + 8 (t % 2) of the
+// fragment's 32; lane t receives column t of the group's 16, one byte per
+// K-row.  The column chunk 8 wn + 2 jt + g % 2 has disjoint bit fields, so
+// the swizzled chunk splits into a lane part and 2 jt.
+struct MncLane8 {
+  int base[4];
+  __device__ void init(int wn, int lane) {
+    const int g = lane >> 4, t = lane & 15;
+    const int kr = 32 * (g >> 1) + (t >> 1);
+    const int lx = (wn * 8 + (g & 1)) ^ f8_sw(t >> 1);
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) base[jt] = kr * 256 + (((2 * jt) ^ lx) << 4) + 8 * (t & 1);
+  }
+};
+
+template <int JT, int KK>
+__device__ __forceinline__ i32x8_t frag_mnc8(const uint8_t* t, const MncLane8& ml) {
+  const uint8_t* p = t + ml.base[JT] + KK * 64 * 256;
+  const i32x2_t r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+  const i32x2_t r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 8 * 256));
+  const i32x2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 16 * 256));
+  const i32x2_t r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 24 * 256));
+  const i32x8_t v = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  return v;
+}
+
+// K-contiguous E4M3 rows (the KcRows layout): lane l gets row r0 + l % 32,
+// K bytes 32 (l / 32) .. + 31 of k-step kk, the same K order as frag_mnc8.
+__device__ __forceinline__ i32x8_t frag_kc8(const uint8_t* t, int r0, int kk, int lane) {
+  const int c0 = kk * 4 + 2 * (lane >> 5);
+  const int sw = (lane & 7) ^ ((lane >> 3) & 1);
+  const uint8_t* row = t + (r0 + (lane & 31)) * 128;
+  const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c0 ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c0 + 1) ^ sw) << 4));
+  const i32x8_t v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  return v;
+}
+
+// Row scales of the activation tiles: the 256 fp32 scales of a stage's K
+// block, 4-byte direct-to-LDS loads, wave w rows 64 w .. 64 w + 63; rows
+// past the tile's rows load zeros.
+struct RowScales {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off;
+  __device__ void init(const float* scales, uint32_t bytes, long long row0, int rows, int nkb, int wave, int lane) {
+    r = rsrc(scales, bytes);
+    const int tr = wave * 64 + lane;
+    off = tr < rows ? (uint32_t)((row0 + tr) * nkb) * 4u : OOB;
+  }
+  __device__ void issue(uint8_t* sc, int wave, int s, uint32_t oob) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(sc + wave * 256), 4, off | oob, (uint32_t)s * 4u, 0, 0);
+  }
+};
+
+// The two k-steps of one E4M3 stage.  sb: E8M0 exponent of the wave's weight
+// block; the row exponents come from the stage's scale block.
+template <int MT>
+__device__ __forceinline__ void mma_stage8(f32x16_t (&acc)[4][4], const uint8_t* __restrict__ st, int sb,
+                                           const MncLane8& mlb, int wm, int lane) {
+  const uint8_t* sa_t = st;
+  const uint8_t* sb_t = st + BOP;
+  const float* scl = reinterpret_cast<const float*>(st + 2 * BOP);
+  int sa[4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) sa[i] = e8m0_of(scl[wm * 128 + i * 32 + (lane & 31)]);
+  i32x8_t a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) a0[i] = frag_kc8(sa_t, wm * 128 + i * 32, 0, lane);
+  b0[0] = frag_mnc8<0, 0>(sb_t, mlb);
+  b0[1] = frag_mnc8<1, 0>(sb_t, mlb);
+  b0[2] = frag_mnc8<2, 0>(sb_t, mlb);
+  b0[3] = frag_mnc8<3, 0>(sb_t, mlb);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) a1[i] = frag_kc8(sa_t, wm * 128 + i * 32, 1, lane);
+  b1[0] = frag_mnc8<0, 1>(sb_t, mlb);
+  b1[1] = frag_mnc8<1, 1>(sb_t, mlb);
+  b1[2] = frag_mnc8<2, 1>(sb_t, mlb);
+  b1[3] = frag_mnc8<3, 1>(sb_t, mlb);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0[j], a0[i], acc[i][j], 0, 0, 0, sb, 0, sa[i]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1[j], a1[i], acc[i][j], 0, 0, 0, sb, 0, sa[i]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K loop and epilogue of one E4M3 dgrad item (see dgrad_run).  A stage
+// buffer holds the activation rows (32 KB), the weight K-rows (32 KB) and
+// the row scales (1 KB).  Lane l holds the scales of the wave's weight
+// blocks for K blocks l and l + 64 (bsc0, bsc1).
+template <bool SWIGLU, typename OT, int MT>
+__device__ __forceinline__ void dgrad8_run(const KcRows& A, const MncRows8& B, const RowScales& R, float bsc0,
+                                           float bsc1, uint8_t* __restrict__ st0, uint8_t* __restrict__ st1,
+                                           const MncLane8& mlb, int wm, int wn, int tid, int lane, int w_wave, int Kd,
+                                           int Nd, int n, int row0, int rows, const uint16_t* __restrict__ ab,
+                                           OT* __restrict__ out) {
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+  // Kd % 256 == 0: an even stage count, a loop body without branches.
+  const int nk = Kd / 128;
+  auto wscale = [&](int s) {
+    const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_uint(s < 64 ? bsc0 : bsc1),
+                                                                         s & 63));
+    return e8m0_of(v);
+  };
+  A.issue(st0, w_wave, 0, 0u);
+  B.issue(st0 + BOP, w_wave, 0, 0u);
+  R.issue(st0 + 2 * BOP, w_wave, 0, 0u);
+  for (int s = 0; s < nk; s += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    A.issue(st1, w_wave, s + 1, 0u);
+    B.issue(st1 + BOP, w_wave, s + 1, 0u);
+    R.issue(st1 + 2 * BOP, w_wave, s + 1, 0u);
+    mma_stage8<MT>(acc, st0, wscale(s), mlb, wm, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t oob = s + 2 < nk ? 0u : OOB;
+    A.issue(st0, w_wave, s + 2, oob);
+    B.issue(st0 + BOP, w_wave, s + 2, oob);
+    R.issue(st0 + 2 * BOP, w_wave, s + 2, oob);
+    mma_stage8<MT>(acc, st1, wscale(s + 1), mlb, wm, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  dgrad_epilogue<SWIGLU, OT>(acc, st1, wm, wn, tid, lane, Nd, n, row0, rows, ab, out);
+}
+
+// E4M3 dgrad items, dealt as k_dgrad's.  a [P, Kd] E4M3 codes with as
+// [P, Kd / 128] fp32 row scales; w [E, Kd, Nd] E4M3 with ws
+// [E, Kd / 128, Nd / 128] block scales; the epilogue as k_dgrad's.
+template <bool SWIGLU, typename OT>
+__global__ __launch_bounds__(BTHREADS) void k_dgrad8(const uint8_t* __restrict__ a, const float* __restrict__ as,
+                                                     const uint8_t* __restrict__ w, const float* __restrict__ ws,
+                                                     const int32_t* __restrict__ tile_map,
+                                                     const int32_t* __restrict__ n_tiles, int Kd, int Nd,
+                                                     uint32_t a_bytes, uint32_t as_bytes,
+                                                     const uint16_t* __restrict__ ab, OT* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP + BSC];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP + BSC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntn = (Nd + BT - 1) / BT;
+  const long long items = (long long)(*n_tiles) * ntn;
+  const long long q = (items + 7) / 8;
+  const long long slot = blockIdx.x >> 3;
+  if (slot >= q) return;
+  const long long item = (blockIdx.x & 7) * q + slot;
+  if (item >= items) return;
+  const int tile = (int)(item / ntn), n = (int)(item % ntn);
+  const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * tile);
+  const int seg = tm.x, row0 = tm.y, rows = tm.w;
+  const int w_wave = __builtin_amdgcn_readfirstlane(wave);
+  const int nkb = Kd / 128, nnb = Nd / 128;
+
+  KcRows A;
+  A.init(a, a_bytes, row0, rows, (uint32_t)Kd, w_wave, lane);
+  MncRows8 B;
+  const long long w_expert = (long long)Kd * Nd;
+  B.init(w + (long long)seg * w_expert, (uint32_t)w_expert, (uint32_t)Nd, n * BT, w_wave, lane);
+  RowScales R;
+  R.init(as, as_bytes, row0, rows, nkb, w_wave, lane);
+  // the wave's weight blocks: K blocks lane and lane + 64, N block 2 n + wn
+  // (past Nd: a block that only dead columns use)
+  const int nb = 2 * n + wn;
+  const float* wsb = ws + (long long)seg * nkb * nnb + (nb < nnb ? nb : 0);
+  const float bsc0 = lane < nkb ? wsb[(long long)lane * nnb] : 1.0f;
+  const float bsc1 = lane + 64 < nkb ? wsb[(long long)(lane + 64) * nnb] : 1.0f;
+
+  MncLane8 mlb;
+  mlb.init(wn, lane);
+  int mt = (rows - wm * 128 + 31) >> 5;
+  mt = __builtin_amdgcn_readfirstlane(mt < 0 ? 0 : (mt > 4 ? 4 : mt));
+  switch (mt) {
+    case 4: dgrad8_run<SWIGLU, OT, 4>(A, B, R, bsc0, bsc1, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 3: dgrad8_run<SWIGLU, OT, 3>(A, B, R, bsc0, bsc1, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 2: dgrad8_run<SWIGLU, OT, 2>(A, B, R, bsc0, bsc1, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 1: dgrad8_run<SWIGLU, OT, 1>(A, B, R, bsc0, bsc1, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    default: dgrad8_run<SWIGLU, OT, 0>(A, B, R, bsc0, bsc1, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+  }
+}
 
 // Items (row tile, N tile) of the tile map, dealt to the XCDs in contiguous
 // runs (block b runs on XCD b % 8): XCD x takes items [x q, x q + q) of the
@@ -692,6 +943,36 @@ unsigned wgrad_grid(int Nr, int Ns, int ntm, int ntn, int nch) {
 // d % 256 and I % 128: full M tiles, even stage counts (Kd % 128 == 0).
 bool ffn_bwd_ok(int d, int I) { return d % 256 == 0 && I % 128 == 0; }
 
+// Both weight gradients (bf16 operands): dW2 [E, d, I] and dW13 [E, 2I, d]
+// in dw_f32 ? fp32 : bf16, routed runs of 4 N tiles.
+static void launch_wgrads(const uint16_t* x, const uint16_t* h, const uint16_t* dy, const uint16_t* dab,
+                          const int32_t* seg_offset, const int32_t* row_token, int T, long long P, int d, int I,
+                          int Nr, int Ns, void* dw13, void* dw2, bool dw_f32, hipStream_t st) {
+  const int E = Nr + Ns;
+  const uint32_t dy_bytes = (uint32_t)(P * d * 2), dab_bytes = (uint32_t)(P * 2 * I * 2);
+  const uint32_t h_bytes = (uint32_t)(P * I * 2), x_bytes = (uint32_t)((long long)T * d * 2);
+  {
+    const int ntm = d / BT, ntn = (I + BT - 1) / BT, nch = 4;
+    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
+    if (dw_f32)
+      hipLaunchKernelGGL((k_wgrad<false, float>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
+                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<float*>(dw2));
+    else
+      hipLaunchKernelGGL((k_wgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
+                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<uint16_t*>(dw2));
+  }
+  {
+    const int ntm = 2 * I / BT, ntn = d / BT, nch = 4;
+    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
+    if (dw_f32)
+      hipLaunchKernelGGL((k_wgrad<true, float>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
+                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<float*>(dw13));
+    else
+      hipLaunchKernelGGL((k_wgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
+                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<uint16_t*>(dw13));
+  }
+}
+
 // dy [P, d], ab [P, 2I], h [P, I] (bf16, the forward's), x [T, d]; dab is
 // scratch [P, 2I]; dx [P, d] bf16; dW13 [E, 2I, d], dW2 [E, d, I] in dw_f32 ?
 // fp32 : bf16.
@@ -700,9 +981,7 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
                          const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d,
                          int I, int Nr, int Ns, uint16_t* dab, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
                          hipStream_t st) {
-  const int E = Nr + Ns;
   const uint32_t dy_bytes = (uint32_t)(P * d * 2), dab_bytes = (uint32_t)(P * 2 * I * 2);
-  const uint32_t h_bytes = (uint32_t)(P * I * 2), x_bytes = (uint32_t)((long long)T * d * 2);
   // dgrad, down + SwiGLU: N = I
   {
     const long long items = (long long)tiles_max * ((I + BT - 1) / BT);
@@ -717,28 +996,38 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
     hipLaunchKernelGGL((k_dgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, w13, tile_map, n_tiles,
                        2 * I, d, dab_bytes, nullptr, dx);
   }
-  // wgrad, down: dW2 [E, d, I]; routed runs of 4 N tiles (of I / 256)
+  launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, dw13, dw2, dw_f32, st);
+}
+
+// d <= 16384 and I <= 8192: a lane holds the block scales of two K blocks.
+bool ffn_bwd_w8_ok(int d, int I) { return ffn_bwd_ok(d, I) && d / 128 <= 128 && 2 * I / 128 <= 128; }
+
+// As launch_ffn_bwd_bf16 with the two dgrad products in E4M3: dy and then
+// [da | db] are quantised in 1x128 tiles (dyq/dys, dabq/dabs scratch), the
+// weights come as E4M3 codes with 128x128 block scales.  The wgrads stay
+// bf16 (dy and [da | db] unquantised).
+void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
+                       const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
+                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
+                       int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
+                       uint8_t* dabq, float* dabs, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                       hipStream_t st) {
+  quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
   {
-    const int ntm = d / BT, ntn = (I + BT - 1) / BT, nch = 4;
-    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
-    if (dw_f32)
-      hipLaunchKernelGGL((k_wgrad<false, float>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
-                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<float*>(dw2));
-    else
-      hipLaunchKernelGGL((k_wgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
-                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<uint16_t*>(dw2));
+    const long long items = (long long)tiles_max * ((I + BT - 1) / BT);
+    const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
+    hipLaunchKernelGGL((k_dgrad8<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dys, w2, w2s, tile_map,
+                       n_tiles, d, I, (uint32_t)(P * d), (uint32_t)(P * (d / 128) * 4), ab, dab);
   }
-  // wgrad, gate/up: dW13 [E, 2I, d]; routed runs of 4 N tiles (of d / 256)
+  quantize_tiles(dab, MOE_BF16, P, 2LL * I, 1, 128, dabq, dabs, st);
   {
-    const int ntm = 2 * I / BT, ntn = d / BT, nch = 4;
-    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
-    if (dw_f32)
-      hipLaunchKernelGGL((k_wgrad<true, float>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
-                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<float*>(dw13));
-    else
-      hipLaunchKernelGGL((k_wgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
-                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<uint16_t*>(dw13));
+    const long long items = (long long)tiles_max * (d / BT);
+    const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
+    hipLaunchKernelGGL((k_dgrad8<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dabq, dabs, w13, w13s,
+                       tile_map, n_tiles, 2 * I, d, (uint32_t)(P * 2 * I), (uint32_t)(P * (2 * I / 128) * 4), nullptr,
+                       dx);
   }
+  launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, dw13, dw2, dw_f32, st);
 }
 
 }  // namespace moe

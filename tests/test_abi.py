@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = M.lib()
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert L.moe_status_str(0) == b"MOE_OK"
     assert L.moe_status_str(3) == b"MOE_EWORKSPACE"
 
@@ -153,6 +153,19 @@ def test_backward_entry_points_reject_bad_arguments():
     assert gb(wsb=16)[0] == M.MOE_EWORKSPACE
     need = M.moe_gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tm)
     assert need == M.moe_permute_rows(T, K, Nr, Ns, tm) * 2 * I * 2
+    g8 = lambda **kw: _status(L.moe_expert_gemm_backward_w8, *[kw.get(k, v) for k, v in dict(
+        x=F, w13=F, w13s=F, w2=F, w2s=F, h=F, ab=F, dy=F, T=T, K=K, Nr=Nr, Ns=Ns, d=d, I=I, tm=tm, so=F, rt=F,
+        tmap=F, nt=F, ws=F, wsb=big, dx=F, dw13=F, dw2=F, dwt=M.MOE_BF16, st=None).items()])
+    assert g8(I=192)[0] == M.MOE_EUNSUPPORTED
+    assert g8(d=16640)[0] == M.MOE_EUNSUPPORTED         # more than 128 scale blocks along d
+    assert g8(I=8320)[0] == M.MOE_EUNSUPPORTED
+    assert g8(w2s=None)[0] == M.MOE_EINVAL
+    assert g8(dwt=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    assert g8(wsb=16)[0] == M.MOE_EWORKSPACE
+    P = M.moe_permute_rows(T, K, Nr, Ns, tm)
+    need8 = M.moe_gemm_backward_w8_workspace_bytes(T, K, Nr, Ns, d, I, tm)
+    assert need8 >= P * 2 * I * 2 + P * 2 * I + P * d + P * (2 * I + d) // 128 * 4
+    assert g8(wsb=need8 - 1)[0] == M.MOE_EWORKSPACE
     gt = lambda **kw: _status(L.moe_expert_gemm_train, *[kw.get(k, v) for k, v in dict(
         x=F, w13=F, w2=F, T=T, K=K, Nr=Nr, Ns=Ns, d=d, I=I, tm=tm, so=F, rt=F, tmap=F, nt=F, ws=F, wsb=big,
         h=F, ab=F, y=F, yt=M.MOE_BF16, st=None).items()])
