@@ -346,15 +346,18 @@ def train_main(args, cfg, dev, stream):
     (moe_expert_gemm_train) + moe_combine_backward -> moe_expert_gemm_backward
     -> moe_route_backward for a seeded bf16 dL/dh' + the bias rule.  The
     roofline object describes the moe_expert_gemm_backward call (dgrad and
-    wgrad of both expert projections, 12 d I flops per row)."""
+    wgrad of both expert projections, 12 d I flops per row).  On an E4M3
+    workload (x_fp8, E4M3 weights) the step is the FP8 one:
+    moe_expert_gemm_train_w8 and moe_expert_gemm_backward_w8."""
     import numpy as np
     import torch
 
     import sparse_expert_routing_sigmoid_amd as M
     import workloads as W
 
-    if cfg.weights != "bf16" or cfg.act != "bf16" or cfg.x_fp8:
-        print(f"--train needs a bf16 workload (got {cfg.name})", file=sys.stderr)
+    fp8_step = cfg.x_fp8 and cfg.weights == "e4m3"
+    if not fp8_step and (cfg.weights != "bf16" or cfg.act != "bf16" or cfg.x_fp8):
+        print(f"--train needs a bf16 or an E4M3 workload (got {cfg.name})", file=sys.stderr)
         sys.exit(2)
     e = W.make_centroids(cfg, dev)
     bias0 = W.make_bias(cfg, dev)
@@ -362,10 +365,15 @@ def train_main(args, cfg, dev, stream):
     us = [W.make_tokens(cfg, s, dev) for s in range(n_u)]
     gs = [W.make_free((cfg.T, cfg.d), 1.0, 100 + s, dev, torch.bfloat16) for s in range(n_u)]
     w13, w2 = W.make_expert_weights(cfg, dev)
-    w8 = M.quantize_weights(w13, w2) if args.dgrad_fp8 else None
-    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16,
-                       M.ExpertWeights(M.MOE_BF16, w13, w2), tile_m=args.tile_m, device=dev, train=True,
-                       grad_dtype=torch.bfloat16, dgrad_weights=w8)
+    # E4M3 weights: quantised once per optimizer step, outside the layer step
+    w8 = M.quantize_weights(w13, w2) if (args.dgrad_fp8 or fp8_step) else None
+    if fp8_step:
+        layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True,
+                           tile_m=args.tile_m, device=dev, train=True, grad_dtype=torch.bfloat16)
+    else:
+        layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16,
+                           M.ExpertWeights(M.MOE_BF16, w13, w2), tile_m=args.tile_m, device=dev, train=True,
+                           grad_dtype=torch.bfloat16, dgrad_weights=w8)
     torch.cuda.synchronize()
     bias = bias0.clone()
     bwd_events = []
@@ -407,6 +415,8 @@ def train_main(args, cfg, dev, stream):
     rows = int(cfg.T * cfg.K + cfg.T * cfg.Ns)
     bwd_flops = 12.0 * cfg.d * cfg.I * rows
     step_flops = 18.0 * cfg.d * cfg.I * rows
+    step_peak = PEAK["bf16"] if not fp8_step else step_flops / (12.0 / 18 * step_flops / PEAK["fp8"] +
+                                                               6.0 / 18 * step_flops / PEAK["bf16"])
     loads = layer.expert_load.cpu().numpy().astype(np.int64)
     achieved = bwd_flops / (bwd_ms * 1e-3)
     if w8 is None:
@@ -435,22 +445,24 @@ def train_main(args, cfg, dev, stream):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w8 is None else "bf16 + e4m3 dgrad",
+        "dtype": "e4m3 + bf16 wgrad" if fp8_step else ("bf16" if w8 is None else "bf16 + e4m3 dgrad"),
         "data": "synthetic (seeded; random-init expert weights and centroids, seeded bf16 output gradients)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "Nr": cfg.Nr, "Ns": cfg.Ns, "I": cfg.I,
                    "K": cfg.K, "routing": cfg.routing, "weights": cfg.weights, "tile_m": args.tile_m,
                    "step": "training forward + backward + bias rule" + (
+                       "; E4M3 forward and backward input-gradient products, bf16 weight gradients "
+                       "(weights quantised once per optimizer step, not in the step)" if fp8_step else
                        "; backward input-gradient products on E4M3 (weights quantised once at set-up, "
                        "not in the step)" if w8 is not None else ""), "grad_dtype": "bf16",
                    "parallelism": "single GPU"},
         "layer": {"tflops": step_flops / (ms_step * 1e-3) / 1e12,
-                  "mfma_frac": step_flops / (ms_step * 1e-3) / PEAK["bf16"],
+                  "mfma_frac": step_flops / (ms_step * 1e-3) / step_peak,
                   "max_load": int(loads.max()), "mean_load": float(loads.mean())},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_train(cfg, us[0], gs[0], e, bias0, w13, w2, args.cpu_seconds,
-                                                 fp8=w8 is not None)
+                                                 fp8="train" if fp8_step else w8 is not None)
     print(json.dumps(out), flush=True)
 
 
@@ -478,6 +490,10 @@ def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds, fp8=False):
     r = O.route(u_s, f64(e), f64(b), cfg.K)
     need = sorted(set(r.idx.ravel().tolist()) | set(range(cfg.Nr, cfg.Nr + cfg.Ns)))
     total = 0.0
+    # (FP8 training step: the weights go in as stored; quantising them
+    # belongs to the optimizer step, and the timed work does not depend on
+    # their values)
+    print(f"cpu baseline: {S} tokens, {len(need)} experts", file=sys.stderr, flush=True)
     for i in need:
         w13_i, w2_i = f64(w13[i]), f64(w2[i])
         if i >= cfg.Nr:
@@ -486,12 +502,14 @@ def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds, fp8=False):
             ts, ks = np.nonzero(r.idx == i)
             x, dy = u_s[ts], r.gate[ts, ks][:, None] * G_s[ts]
         t1 = time.perf_counter()
-        (OB.ffn_backward_fp8 if fp8 else OB.ffn_backward)(x, w13_i, w2_i, dy)
+        fn = OB.ffn_backward_fp8_train if fp8 == "train" else (OB.ffn_backward_fp8 if fp8 else OB.ffn_backward)
+        fn(x, w13_i, w2_i, dy)
         total += time.perf_counter() - t1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": S / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 SwiGLU FFN backward"
-                      f"{' with E4M3 input-gradient products' if fp8 else ''} (forward recomputed, "
+                      f"{' of the FP8 training step' if fp8 == 'train' else ' with E4M3 input-gradient products' if fp8 else ''}"
+                      f" (forward recomputed, "
                       f"dx, dW13, dW2) of the {cfg.K} routed + {cfg.Ns} shared experts of each token, "
                       f"{len(need)} experts touched; routing, gate and centroid gradients not timed",
             "seconds": total, "host_cpus": os.cpu_count(), **host_info()}

@@ -286,6 +286,30 @@ moe_status moe_expert_gemm_train(const void* x, const void* w13, const void* w2,
                                  void* y, moe_dtype y_t, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_expert_gemm_train_w8: moe_expert_gemm for (x_t, w_t) = (E4M3, E4M3)
+ * ([RG-FP8]: x in 1x128 tiles, weights in 128x128 blocks, h re-quantised in
+ * 1x128 tiles before the down projection) that also keeps, for
+ * moe_expert_gemm_backward_w8, ab [P_max, 2I] (bf16 pre-activations from
+ * the fp32 accumulators) and h [P_max, I] (bf16: the E4M3 h that the down
+ * projection multiplies, code x scale, exact).  y as in moe_expert_gemm.
+ *   x, x_scale     device [T, d] E4M3 codes, [T, d/128] fp32 scales
+ *   w13 .. w2_scale as moe_expert_gemm_backward_w8
+ *   ws  device, moe_gemm_train_w8_workspace_bytes(...) bytes (work schedule
+ *       and the E4M3 h)
+ *   Errors: as moe_expert_gemm_train; MOE_EUNSUPPORTED unless d % 256 == 0,
+ *   I % 256 == 0, d <= 8192 and I <= 8192.
+ * ---------------------------------------------------------------------- */
+size_t moe_gemm_train_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status moe_expert_gemm_train_w8(const uint8_t* x, const float* x_scale,
+                                    const uint8_t* w13, const float* w13_scale,
+                                    const uint8_t* w2, const float* w2_scale,
+                                    int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                    const int32_t* seg_offset, const int32_t* row_token,
+                                    const int32_t* tile_map, const int32_t* n_tiles,
+                                    void* ws, size_t ws_bytes, void* h, void* ab,
+                                    void* y, moe_dtype y_t, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_combine_backward: gradients of the [RG-MoE] combine equation and of
  * the gate equation (g = s / sum of the selected s) for one step.
  *   grad_out, g_t  device [T, d] G = dL/dh', MOE_F32 or MOE_BF16

@@ -30,6 +30,14 @@ power-of-two scale (R10 of oracle/moe.py); the activation gradient is
 rounded to fp32 before it is quantised.  The weight-gradient products stay
 unquantised: their K axis is the token axis, along which the pages give no
 tiling.
+
+FP8 training step (ffn_backward_fp8_train): the forward of the FP8 path
+(oracle/moe.py, R8: x in 1x128 tiles, h re-quantised in 1x128 tiles, the
+weights in 128x128 blocks) followed by the backward of reading B2.  Reading
+B3: every quantiser passes the gradient straight through (it is treated as
+the identity when differentiated), so dW2 uses the quantised h that the
+down projection multiplied, and dW13 uses the unquantised expert input x
+(the token rows as stored, which the weight-gradient products read).
 """
 from __future__ import annotations
 
@@ -87,14 +95,19 @@ def ffn_backward(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray)
     return dx, dw13, dw2, y
 
 
+def _q_act(g: np.ndarray) -> np.ndarray:
+    """g rounded to fp32, then through 1x128 E4M3 tiles (code x scale, fp64)."""
+    q, s = quantize_tiles(np.asarray(g, dtype=np.float64).astype(np.float32), 1, 128)
+    return dequantize_tiles(q, s, 1, 128)
+
+
 def fp8_tile_matmul(g: np.ndarray, w: np.ndarray) -> np.ndarray:
     """g [n, K] @ w [K, N] with both operands in E4M3 (reading B2): g in
     1x128 tiles along K (rounded to fp32 first), w in 128x128 blocks of its
     stored layout; the dequantised values (code x power-of-two scale, exact)
     are multiplied in fp64."""
-    gq, gs = quantize_tiles(np.asarray(g, dtype=np.float64).astype(np.float32), 1, 128)
     wq, ws = quantize_tiles(np.asarray(w, dtype=np.float64).astype(np.float32), 128, 128)
-    return dequantize_tiles(gq, gs, 1, 128) @ dequantize_tiles(wq, ws, 128, 128)
+    return _q_act(g) @ dequantize_tiles(wq, ws, 128, 128)
 
 
 def ffn_backward_fp8(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray):
@@ -117,14 +130,41 @@ def ffn_backward_fp8(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndar
     return dx, dw13, dw2, y
 
 
-def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out, fp8_dgrad: bool = False) -> LayerGrads:
+def ffn_backward_fp8_train(x: np.ndarray, w13q: np.ndarray, w2q: np.ndarray, dy: np.ndarray):
+    """Forward and backward of one expert on the FP8 training path (reading
+    B3).  x [n, d] the expert's input rows as stored; w13q [2I, d], w2q
+    [d, I] the decoded E4M3 weights (code x block scale).
+      forward:  [a; b] = W13q Q(x),  h = Q(SiLU(a) b),  y = W2q h
+      backward: dW2 = dy^T h,  dh = Q(dy) W2q,  da, db as ffn_backward,
+                dW13 = [da | db]^T x,  dx = Q([da | db]) W13q
+    Q: 1x128 E4M3 tiles along the row.  Returns (dx, dw13, dw2, y)."""
+    x, w13q, w2q, dy = _f64(x), _f64(w13q), _f64(w2q), _f64(dy)
+    I = w2q.shape[1]
+    ab = _q_act(x) @ w13q.T
+    a, b = ab[:, :I], ab[:, I:]
+    h = _q_act(silu(a) * b)
+    y = h @ w2q.T
+    dw2 = dy.T @ h
+    dh = _q_act(dy) @ w2q
+    da = dh * b * silu_grad(a)
+    db = dh * silu(a)
+    dab = np.concatenate([da, db], axis=1)
+    dw13 = dab.T @ x
+    dx = _q_act(dab) @ w13q
+    return dx, dw13, dw2, y
+
+
+def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out, fp8_dgrad: bool = False,
+                   fp8_train: bool = False) -> LayerGrads:
     """Gradients of L = sum(grad_out * out) for the layer of
     oracle.moe.layer_forward (bf16 / fp32 path, no FP8 quantisation).
 
     u [T, d], e [N_r, d], b [N_r], w13 [N_r+N_s, 2I, d], w2 [N_r+N_s, d, I],
     grad_out [T, d] = dL/dout.  fp8_dgrad: every expert's backward is
-    ffn_backward_fp8 instead of ffn_backward."""
-    ffn_bwd = ffn_backward_fp8 if fp8_dgrad else ffn_backward
+    ffn_backward_fp8 instead of ffn_backward.  fp8_train: the whole FP8
+    training step, ffn_backward_fp8_train, with w13 / w2 the decoded E4M3
+    weights; the router still sees the unquantised u (R8)."""
+    ffn_bwd = ffn_backward_fp8_train if fp8_train else (ffn_backward_fp8 if fp8_dgrad else ffn_backward)
     u, e, G = _f64(u), _f64(e), _f64(grad_out)
     w13, w2 = _f64(w13), _f64(w2)
     T, d = u.shape

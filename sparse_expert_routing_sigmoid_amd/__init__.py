@@ -49,6 +49,8 @@ SIGNATURES = {
     "moe_combine_backward": (_i, [_vp, _i, _vp, _i] + [_vp] * 4 + [_i] * 5 + [_vp] * 5),
     "moe_gemm_backward_workspace_bytes": (_sz, [_i] * 7),
     "moe_expert_gemm_backward": (_i, [_vp] * 6 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
+    "moe_gemm_train_w8_workspace_bytes": (_sz, [_i] * 7),
+    "moe_expert_gemm_train_w8": (_i, [_vp] * 6 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
     "moe_gemm_backward_w8_workspace_bytes": (_sz, [_i] * 7),
     "moe_expert_gemm_backward_w8": (_i, [_vp] * 8 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
     "moe_route_backward": (_i, [_vp, _i, _vp, _vp, _i] + [_vp] * 7 + [_i] * 5 + [_vp, _i, _vp, _vp]),
@@ -197,6 +199,22 @@ def moe_expert_gemm_backward(x, w13, w2, h, ab, dy, T, K, Nr, Ns, d, I, tile_m, 
                                           dtype_code(dw13), _stream(stream)))
 
 
+def moe_gemm_train_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m):
+    return lib().moe_gemm_train_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m)
+
+
+def moe_expert_gemm_train_w8(xq, xs, w8: "ExpertWeights", T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token,
+                             tile_map, n_tiles, ws, h, ab, y, stream=None):
+    """The E4M3 expert GEMMs keeping h and [a | b] (bf16) for the backward;
+    xq / xs: u in 1x128 E4M3 tiles (fp8_quantize_tiles)."""
+    if w8.w_t != MOE_E4M3:
+        raise ValueError("moe_expert_gemm_train_w8 needs E4M3 weights")
+    _check(lib().moe_expert_gemm_train_w8(_ptr(xq), _ptr(xs), _ptr(w8.w13), _ptr(w8.w13_scale), _ptr(w8.w2),
+                                          _ptr(w8.w2_scale), T, K, Nr, Ns, d, I, tile_m, _ptr(seg_offset),
+                                          _ptr(row_token), _ptr(tile_map), _ptr(n_tiles), _ptr(ws), _nbytes(ws),
+                                          _ptr(h), _ptr(ab), _ptr(y), dtype_code(y), _stream(stream)))
+
+
 def moe_gemm_backward_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m):
     return lib().moe_gemm_backward_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m)
 
@@ -313,16 +331,23 @@ class MoeLayer:
         self.train = train
         if train:
             # the training forward keeps h and the pre-activations [a | b]
-            # for the backward (bf16 path only)
-            if x_fp8 or weights.w_t != MOE_BF16 or act_dtype != torch.bfloat16:
-                raise ValueError("training needs bf16 activations and weights")
+            # for the backward: bf16 activations with bf16 weights, or the
+            # E4M3 path (x_fp8 with E4M3 weights, which the backward's
+            # input-gradient products then use too)
+            self.train_fp8 = x_fp8 and weights.w_t == MOE_E4M3
+            if act_dtype != torch.bfloat16 or not (self.train_fp8 or (not x_fp8 and weights.w_t == MOE_BF16)):
+                raise ValueError("training needs bf16 activations with bf16 weights, or x_fp8 with E4M3 weights")
+            if self.train_fp8:
+                if dgrad_weights is not None and dgrad_weights is not weights:
+                    raise ValueError("the E4M3 training path uses its own weights for the backward")
+                dgrad_weights = weights
             bf16 = dict(dtype=torch.bfloat16, device=dev)
             E = Nr + Ns
             self.h = torch.empty((P, I), **bf16)
             self.ab = torch.empty((P, 2 * I), **bf16)
-            self.train_ws = torch.empty((max(moe_gemm_train_workspace_bytes(T, K, Nr, Ns, d, I, tile_m), 1),),
-                                        dtype=torch.uint8, device=dev)
-            gd = weights.w13.dtype if grad_dtype is None else grad_dtype
+            tws = moe_gemm_train_w8_workspace_bytes if self.train_fp8 else moe_gemm_train_workspace_bytes
+            self.train_ws = torch.empty((max(tws(T, K, Nr, Ns, d, I, tile_m), 1),), dtype=torch.uint8, device=dev)
+            gd = (torch.bfloat16 if self.train_fp8 else weights.w13.dtype) if grad_dtype is None else grad_dtype
             self.dy = torch.empty((P, d), **bf16)
             self.dx = torch.empty((P, d), **bf16)
             self.dgate = torch.empty((T, K), **f32)
@@ -356,9 +381,14 @@ class MoeLayer:
         else:
             x, xs = u, None
         if self.train:
-            moe_expert_gemm_train(u, w.w13, w.w2, self.T, self.K, self.Nr, self.Ns, self.d, self.I, self.tile_m,
-                                  self.seg_offset, self.row_token, self.tile_map, self.n_tiles, self.train_ws,
-                                  self.h, self.ab, self.y, stream)
+            if self.train_fp8:
+                moe_expert_gemm_train_w8(x, xs, w, self.T, self.K, self.Nr, self.Ns, self.d, self.I, self.tile_m,
+                                         self.seg_offset, self.row_token, self.tile_map, self.n_tiles, self.train_ws,
+                                         self.h, self.ab, self.y, stream)
+            else:
+                moe_expert_gemm_train(u, w.w13, w.w2, self.T, self.K, self.Nr, self.Ns, self.d, self.I, self.tile_m,
+                                      self.seg_offset, self.row_token, self.tile_map, self.n_tiles, self.train_ws,
+                                      self.h, self.ab, self.y, stream)
             return
         moe_expert_gemm(x, xs, w.w_t, w.w13, w.w13_scale, w.w2, w.w2_scale, self.T, self.K, self.Nr, self.Ns,
                         self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map, self.n_tiles,

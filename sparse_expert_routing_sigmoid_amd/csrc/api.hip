@@ -45,6 +45,12 @@ moe_status expert_gemm_backward(const void* x, const void* w13, const void* w2, 
                                 const int32_t* seg_offset, const int32_t* row_token, const int32_t* tile_map,
                                 const int32_t* n_tiles, void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2,
                                 moe_dtype dw_t, void* stream);
+size_t gemm_train_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status expert_gemm_train_w8(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
+                                const uint8_t* w2, const float* w2_scale, int T, int K, int Nr, int Ns, int d, int I,
+                                int tile_m, const int32_t* seg_offset, const int32_t* row_token,
+                                const int32_t* tile_map, const int32_t* n_tiles, void* ws, size_t ws_bytes, void* h,
+                                void* ab, void* y, moe_dtype y_t, void* stream);
 size_t gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
 moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
                                    const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
@@ -186,6 +192,21 @@ moe_status moe_expert_gemm_backward(const void* x, const void* w13, const void* 
   moe::clear_error();
   return moe::expert_gemm_backward(x, w13, w2, h, ab, dy, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token, tile_map,
                                    n_tiles, ws, ws_bytes, dx, dw13, dw2, dw_t, stream);
+}
+
+size_t moe_gemm_train_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  return moe::gemm_train_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m);
+}
+
+moe_status moe_expert_gemm_train_w8(const uint8_t* x, const float* x_scale, const uint8_t* w13,
+                                    const float* w13_scale, const uint8_t* w2, const float* w2_scale, int T, int K,
+                                    int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                    const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                    void* ws, size_t ws_bytes, void* h, void* ab, void* y, moe_dtype y_t,
+                                    void* stream) {
+  moe::clear_error();
+  return moe::expert_gemm_train_w8(x, x_scale, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns, d, I, tile_m, seg_offset,
+                                   row_token, tile_map, n_tiles, ws, ws_bytes, h, ab, y, y_t, stream);
 }
 
 size_t moe_gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {

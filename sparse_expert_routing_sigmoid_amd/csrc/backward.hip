@@ -32,6 +32,12 @@ void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const ui
                                 hipStream_t st);
 bool ffn_bwd_ok(int d, int I);
 bool ffn_bwd_w8_ok(int d, int I);
+bool ffn_fp8_persistent_ok(int d, int I);
+void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
+                               const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
+                               const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
+                               int Nr, int cap, uint8_t* h, float* h_scale, void* y, bool y_f32, int* sched,
+                               hipStream_t st, uint16_t* ab, uint16_t* hb);
 void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
                        const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
                        const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
@@ -312,6 +318,53 @@ moe_status expert_gemm_train(const void* x, const void* w13, const void* w2, int
                              static_cast<uint16_t*>(ab), y, y_t == MOE_F32, static_cast<int*>(ws),
                              as_stream(stream));
   return launch_status("moe_expert_gemm_train");
+}
+
+// Workspace of the E4M3 training forward: the work schedule, then h as E4M3
+// codes [P, I] and its 1x128 scales [P, I / 128].
+static size_t train_w8_h_offset(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  return (gemm_sched_bytes(T, K, Nr, Ns, d, I, tile_m) + 255) / 256 * 256;
+}
+
+size_t gemm_train_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  if (T < 0 || d < 1 || I < 128 || Nr < 1 || Ns < 0 || K < 1 || tile_m < 1) return 0;
+  const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
+  return train_w8_h_offset(T, K, Nr, Ns, d, I, tile_m) + (P * I + 255) / 256 * 256 + P * (size_t)(I / 128) * 4;
+}
+
+moe_status expert_gemm_train_w8(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
+                                const uint8_t* w2, const float* w2_scale, int T, int K, int Nr, int Ns, int d, int I,
+                                int tile_m, const int32_t* seg_offset, const int32_t* row_token,
+                                const int32_t* tile_map, const int32_t* n_tiles, void* ws, size_t ws_bytes, void* h,
+                                void* ab, void* y, moe_dtype y_t, void* stream) {
+  const moe_status cs = check_layer(T, K, Nr, Ns, d, I, tile_m);
+  if (cs != MOE_OK) return cs;
+  MOE_REQUIRE(y_t == MOE_F32 || y_t == MOE_BF16, MOE_EINVAL, "bad y_t");
+  MOE_REQUIRE(w13 && w13_scale && w2 && w2_scale && seg_offset && row_token && tile_map && n_tiles && y && h && ab,
+              MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(T == 0 || (x && x_scale), MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(w13) && aligned16(w2) && aligned16(y) && aligned16(ws) && aligned16(h) &&
+                  aligned16(ab),
+              MOE_EINVAL, "x, w13, w2, h, ab, y and ws must be 16-byte aligned");
+  MOE_REQUIRE(ffn_fp8_persistent_ok(d, I) && ffn_bwd_w8_ok(d, I), MOE_EUNSUPPORTED,
+              "E4M3 training path needs d % 256 == 0, I % 256 == 0, d <= 8192, I <= 8192");
+  const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
+  const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
+  MOE_REQUIRE(tiles_max <= ffn_schedule_max_tiles(), MOE_EUNSUPPORTED, "more GEMM tiles than the schedule holds");
+  MOE_REQUIRE(fits31((unsigned long long)P * d * 2) && fits31((unsigned long long)P * 2 * I * 2) &&
+                  fits31((unsigned long long)2 * I * d),
+              MOE_EUNSUPPORTED, "training path: operand of 2 GiB or more");
+  MOE_REQUIRE(ws && ws_bytes >= gemm_train_w8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m), MOE_EWORKSPACE,
+              "workspace smaller than moe_gemm_train_w8_workspace_bytes");
+  if (T == 0) return MOE_OK;
+  uint8_t* wb = static_cast<uint8_t*>(ws);
+  const size_t ho = train_w8_h_offset(T, K, Nr, Ns, d, I, tile_m);
+  uint8_t* hq = wb + ho;
+  float* hs = reinterpret_cast<float*>(wb + ho + (P * I + 255) / 256 * 256);
+  launch_ffn_fp8_persistent(x, x_scale, w13, w13_scale, w2, w2_scale, row_token, tile_map, n_tiles, T, (long long)P,
+                            d, I, Nr, tiles_max, hq, hs, y, y_t == MOE_F32, reinterpret_cast<int*>(wb),
+                            as_stream(stream), static_cast<uint16_t*>(ab), static_cast<uint16_t*>(h));
+  return launch_status("moe_expert_gemm_train_w8");
 }
 
 moe_status combine_backward(const void* grad_out, moe_dtype g_t, const void* y, moe_dtype y_t,

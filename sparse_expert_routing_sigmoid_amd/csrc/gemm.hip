@@ -22,7 +22,7 @@ void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uin
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                int Nr, int cap, uint8_t* h, float* h_scale, void* y, bool y_f32, int* sched,
-                               hipStream_t st);
+                               hipStream_t st, uint16_t* ab = nullptr, uint16_t* hb = nullptr);
 bool ffn_w8a16_ok(int d, int I);
 void launch_ffn_w8a16(const uint16_t* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
                       const float* w2_scale, const int32_t* row_token, const int32_t* tile_map,

@@ -256,10 +256,10 @@ __device__ __forceinline__ float absmax8(float4 a, float4 b) {
 // are quantised as one 1x128 E4M3 tile (power-of-two scale, round to nearest
 // even): the 16 threads holding a row find its amax with lane shuffles.
 // MT == 0: the wave has no rows.
-template <bool PHASE_A, bool H_FP8, int MT, int MA, typename OT>
+template <bool PHASE_A, bool H_FP8, int MT, int MA, typename OT, bool KEEP>
 __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Item& it, uint8_t* st0, uint8_t* st1,
                                          int wm, int wn, int tid, OT* __restrict__ out, float* __restrict__ out_scale,
-                                         uint16_t* __restrict__ ab, int Nd, int n) {
+                                         uint16_t* __restrict__ ab, uint16_t* __restrict__ hb, int Nd, int n) {
   constexpr int NC = PHASE_A ? P_TN / 2 : P_TN;  // output columns of the tile
   constexpr int LSTR = P_TN * 4;
   const int lcol = it.lane & 31;
@@ -316,7 +316,7 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
       if (PHASE_A) {  // h = SiLU(gate) * up
         const float4 u0 = *reinterpret_cast<const float4*>(er + 512 + ch * 32);
         const float4 u1 = *reinterpret_cast<const float4*>(er + 512 + ch * 32 + 16);
-        if (!H_FP8 && ab) {  // training: keep the pre-activations [a | b] for the backward pass
+        if ((!H_FP8 || KEEP) && ab) {  // training: keep the pre-activations [a | b] for the backward pass
           uint16_t* abr = ab + (it.row0 + pass * 128 + r) * 2LL * Nd + col0 + ch * 8;
           store8(abr, v0, v1);
           store8(abr + Nd, u0, u1);
@@ -337,6 +337,15 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
         uint8_t* dst = reinterpret_cast<uint8_t*>(out) + orow * Nd + col0 + ch * 8;
         *reinterpret_cast<uint2*>(dst) = wv;
         if (ch == 0) out_scale[orow * (Nd / 128) + n] = exp2_int(k);
+        if (KEEP && hb) {  // training: h as phase B multiplies it, code x scale in bf16 (exact)
+          const float sc = exp2_int(k);
+          uint4 hv;
+          hv.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv.x, sc, false));
+          hv.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv.x, sc, true));
+          hv.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv.y, sc, false));
+          hv.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv.y, sc, true));
+          *reinterpret_cast<uint4*>(hb + orow * Nd + col0 + ch * 8) = hv;
+        }
       } else {
         store8(out + orow * Nd + col0 + ch * 8, v0, v1);
       }
@@ -348,10 +357,10 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
 // K loop (two-stage pipeline, unrolled by two so each step names its
 // buffers and the loop has a single exit) and epilogue, all in one
 // instantiation.
-template <bool FP8, bool PHASE_A, int MT, typename OT>
+template <bool FP8, bool PHASE_A, int MT, typename OT, bool KEEP>
 __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* st1, int wm, int wn, int tid,
                                          OT* __restrict__ out, float* __restrict__ out_scale,
-                                         uint16_t* __restrict__ ab, int Nd, int n) {
+                                         uint16_t* __restrict__ ab, uint16_t* __restrict__ hb, int Nd, int n) {
   constexpr int MA = MT > 0 ? MT : 1;
   f32x16_v acc[MA][4];
 #pragma unroll
@@ -370,7 +379,8 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
     pipe_step<FP8, MT>(acc, it, st0, st1, s + 1, s + 2 < it.nk, (uint32_t)(s + 2) * P_ROWB);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's zero loads land before LDS is reused
-  epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT>(acc, it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n);
+  epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT, KEEP>(acc, it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd,
+                                                      n);
 }
 
 // PHASE_A: x = tokens [T, Kd] gathered by row_token, w = W13 [E, 2*Nd, Kd],
@@ -381,7 +391,7 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
 //      phase A writes h as E4M3 codes with scales out_scale [P, Nd/128].
 // ab (bf16 phase A only, may be NULL): [P, 2 Nd] gets the pre-activations
 //      a (columns 0..Nd-1) and b (Nd..2Nd-1) of every token row.
-template <bool FP8, bool PHASE_A, typename OT>
+template <bool FP8, bool PHASE_A, typename OT, bool KEEP = false>
 __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __restrict__ x,
                                                             const uint8_t* __restrict__ w,
                                                             const float* __restrict__ x_scale,
@@ -395,7 +405,8 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
                                                             const int* __restrict__ offsets,
                                                             const int* __restrict__ items,
                                                             OT* __restrict__ out, float* __restrict__ out_scale,
-                                                            uint16_t* __restrict__ ab) {
+                                                            uint16_t* __restrict__ ab,
+                                                            uint16_t* __restrict__ hb) {
   constexpr int EB = Fmt<FP8>::EB;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[Fmt<FP8>::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[Fmt<FP8>::STAGE];
@@ -480,11 +491,11 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
     int mt_live = (it.rows - it.mrow0 + 31) >> 5;  // 32-row MFMA tiles of this wave that hold rows
     mt_live = __builtin_amdgcn_readfirstlane(mt_live < 0 ? 0 : (mt_live > 4 ? 4 : mt_live));
     switch (mt_live) {
-      case 4: run_tile<FP8, PHASE_A, 4, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
-      case 3: run_tile<FP8, PHASE_A, 3, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
-      case 2: run_tile<FP8, PHASE_A, 2, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
-      case 1: run_tile<FP8, PHASE_A, 1, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
-      default: run_tile<FP8, PHASE_A, 0, OT>(it, st0, st1, wm, wn, tid, out, out_scale, ab, Nd, n); break;
+      case 4: run_tile<FP8, PHASE_A, 4, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+      case 3: run_tile<FP8, PHASE_A, 3, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+      case 2: run_tile<FP8, PHASE_A, 2, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+      case 1: run_tile<FP8, PHASE_A, 1, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+      default: run_tile<FP8, PHASE_A, 0, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
     }
   }
 }
@@ -681,25 +692,28 @@ void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const ui
   const PhaseSched a = phase_sched(sched, 0, cap, ntA), b = phase_sched(sched, 1, cap, ntA);
   hipLaunchKernelGGL((k_ffn_persistent<false, true, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, xb,
                      reinterpret_cast<const uint8_t*>(w13), nullptr, nullptr, row_token, tile_map, n_tiles, d, I,
-                     x_bytes, 0u, a.cnt, a.tot, a.off, a.items, h, nullptr, ab);
+                     x_bytes, 0u, a.cnt, a.tot, a.off, a.items, h, nullptr, ab, nullptr);
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
   if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<false, false, float>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
-                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr, nullptr);
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr, nullptr, nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<false, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
-                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<uint16_t*>(y), nullptr, nullptr);
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<uint16_t*>(y), nullptr, nullptr,
+                       nullptr);
 }
 
 // E4M3 x E4M3: x codes [T, d] with x_scale [T, d/128]; W13 / W2 codes with
 // block scales; h (workspace) = codes [P, I] then scales [P, I/128].
+// Training (ab, hb not NULL): phase A also writes [a | b] [P, 2I] and h
+// [P, I] (its E4M3 value) in bf16.
 void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                int Nr, int cap, uint8_t* h, float* h_scale, void* y, bool y_f32, int* sched,
-                               hipStream_t st) {
+                               hipStream_t st, uint16_t* ab, uint16_t* hb) {
   const int nb = persistent_blocks();
   const uint32_t x_bytes = (uint32_t)((long long)T * d);
   const uint32_t xs_bytes = (uint32_t)((long long)T * (d / 128) * 4);
@@ -708,17 +722,22 @@ void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uin
   const int ntA = I / 128, ntB = d / 256;
   hipLaunchKernelGGL(k_ffn_schedule, dim3(1), dim3(1024), 0, st, tile_map, n_tiles, Nr, ntA, ntB, cap, sched);
   const PhaseSched a = phase_sched(sched, 0, cap, ntA), b = phase_sched(sched, 1, cap, ntA);
-  hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t>), dim3(nb), dim3(P_THREADS), 0, st, x, w13, x_scale,
-                     w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, xs_bytes, a.cnt, a.tot, a.off, a.items,
-                     h, h_scale, nullptr);
+  if (ab || hb)
+    hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t, true>), dim3(nb), dim3(P_THREADS), 0, st, x, w13,
+                       x_scale, w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, xs_bytes, a.cnt, a.tot, a.off,
+                       a.items, h, h_scale, ab, hb);
+  else
+    hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t>), dim3(nb), dim3(P_THREADS), 0, st, x, w13, x_scale,
+                       w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, xs_bytes, a.cnt, a.tot, a.off, a.items,
+                       h, h_scale, nullptr, nullptr);
   if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<true, false, float>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
                        w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
-                       static_cast<float*>(y), nullptr, nullptr);
+                       static_cast<float*>(y), nullptr, nullptr, nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<true, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
                        w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
-                       static_cast<uint16_t*>(y), nullptr, nullptr);
+                       static_cast<uint16_t*>(y), nullptr, nullptr, nullptr);
 }
 
 }  // namespace moe

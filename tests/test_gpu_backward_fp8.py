@@ -93,3 +93,49 @@ def test_fp8_dgrad_rejects_bf16_weights():
     with pytest.raises(ValueError):
         M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, M.ExpertWeights(M.MOE_BF16, w13, w2),
                    train=True, dgrad_weights=M.ExpertWeights(M.MOE_BF16, w13, w2))
+
+
+TRAIN_CASES = {
+    "small": CASES["small"],
+    # several row tiles per expert; the FP8 forward needs I % 256 == 0
+    "mid": BASE.with_(T=1024, d=1024, Nr=32, Ns=2, I=512, K=6),
+}
+
+
+@pytest.mark.parametrize("name", list(TRAIN_CASES))
+def test_fp8_training_step_matches_oracle(name):
+    """MoeLayer(train=True, x_fp8=True, E4M3 weights): the E4M3 training
+    forward (keeping [a|b] and the E4M3 h in bf16) and the backward with E4M3
+    input-gradient products, against layer_backward(fp8_train=True) on the
+    oracle's own 128x128 quantisation of the same bf16 weights."""
+    from oracle.e4m3 import dequantize_tiles, quantize_tiles
+    cfg = TRAIN_CASES[name]
+    print(f"fp8 training step parity {name}: {cfg}", flush=True)
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    w8 = M.quantize_weights(w13, w2)
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True, tile_m=32,
+                       train=True)
+    plain = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True, tile_m=32)
+    u, e, b = W.make_tokens(cfg, 0, "cuda"), W.make_centroids(cfg, "cuda"), W.make_bias(cfg, "cuda")
+    out = layer.forward(u, e, b).clone()
+    out_plain = plain.forward(u, e, b)
+    G = W.make_free((cfg.T, cfg.d), 1.0, 100, "cuda", torch.bfloat16)
+    du, de, dw13, dw2 = layer.backward(G, u, e)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_plain)   # the training forward computes the same layer output
+
+    u64, e64, b64, G64 = map(f64_of, (u, e, b, G))
+    r = O.route(u64, e64, b64, cfg.K)
+    ok, tied = check_routing(np_of(layer.topk_idx), np_of(layer.topk_gate), np_of(layer.expert_load), r, cfg.Nr)
+    assert not tied, "seeded inputs hold a near-tie; the gradients would not be comparable"
+    deq = lambda w: dequantize_tiles(*quantize_tiles(w.astype(np.float32), 128, 128), 128, 128)
+    w13q = np.stack([deq(x) for x in f64_of(w13)])
+    w2q = np.stack([deq(x) for x in f64_of(w2)])
+    gr = OB.layer_backward(u64, e64, b64, w13q, w2q, cfg.Nr, cfg.Ns, cfg.K, G64, fp8_train=True)
+    errs = {"du": rel_l2(f64_of(du), gr.du), "du_ffn": rel_l2(f64_of(du) - G64 - gr.du_router, gr.du_ffn),
+            "dw13": rel_l2(f64_of(dw13), gr.dw13), "dw2": rel_l2(f64_of(dw2), gr.dw2),
+            "de": rel_l2(f64_of(de), gr.de), "dgate": rel_l2(f64_of(layer.dgate), gr.dgate),
+            "dz": rel_l2(f64_of(layer.dz), gr.dz)}
+    print(errs, flush=True)
+    for k, v in errs.items():
+        assert v <= TOL8, (k, v)

@@ -222,3 +222,50 @@ def test_fp8_layer_backward_switch():
     assert np.array_equal(g8.du_router, g.du_router) and np.array_equal(g8.de, g.de)
     assert not np.array_equal(g8.du_ffn, g.du_ffn)
     assert np.linalg.norm(g8.du - g.du) / np.linalg.norm(g.du) < 0.05
+
+
+def test_fp8_train_step_forward_is_the_fp8_forward():
+    """The forward inside ffn_backward_fp8_train is the FP8 forward oracle
+    (x and h in 1x128 tiles, R8), and the layer gradients of the FP8 training
+    step use its outputs for the gate gradients."""
+    p = tiny_inputs(4, T=6, d=256, Nr=4, Ns=1, I=128, K=2)
+    w13q = np.stack([O.quantize_activations(w) for w in p["w13"]])   # any fixed weights will do here
+    w2q = np.stack([O.quantize_activations(w) for w in p["w2"]])
+    f = O.layer_forward(p["u"], p["e"], p["b"], w13q, w2q, 4, 1, 2, x_quant=True, h_quant=True)
+    g = B.layer_backward(p["u"], p["e"], p["b"], w13q, w2q, 4, 1, 2, p["G"], fp8_train=True)
+    dgate = np.einsum("td,tkd->tk", p["G"], f.y_routed)
+    assert np.allclose(g.dgate, dgate, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_train_step_straight_through_gradients():
+    """With quantisers treated as the identity (B3) the FP8 training step's
+    gradients equal the fp64 autograd gradients of the same function in which
+    each quantiser's output is a constant offset added to its input: checked
+    here by torch autograd with Q(z) = z + (Q(z) - z).detach()."""
+    rng = np.random.default_rng(8)
+    n, d, I = 16, 256, 128
+    x = rng.standard_normal((n, d))
+    w13q = O.quantize_activations(rng.standard_normal((2 * I, d)) / 16)
+    w2q = O.quantize_activations(rng.standard_normal((d, I)) / 16)
+    dy = rng.standard_normal((n, d))
+    dx, dw13, dw2, y = B.ffn_backward_fp8_train(x, w13q, w2q, dy)
+
+    def q(t):   # forward value of the oracle's quantiser, gradient of the identity
+        return t + (torch.from_numpy(O.quantize_activations(t.detach().numpy().astype(np.float32))) - t).detach()
+
+    xt = torch.tensor(x, requires_grad=True)
+    W13 = torch.tensor(w13q, requires_grad=True)
+    W2 = torch.tensor(w2q, requires_grad=True)
+    ab = q(xt) @ W13.T
+    a, b = ab[:, :I], ab[:, I:]
+    h = q(a * torch.sigmoid(a) * b)
+    yt = h @ W2.T
+    assert np.allclose(yt.detach().numpy(), y, rtol=1e-12, atol=1e-12)
+    (yt * torch.from_numpy(dy)).sum().backward()
+    # dW2 and the exact dW13 of this function (through Q(x)) vs the oracle's
+    assert np.allclose(W2.grad.numpy(), dw2, rtol=1e-10, atol=1e-10)
+    # the oracle's dW13 reads the unquantised x (B3) and its dx quantises the
+    # gradients (B2): both differ from straight-through autograd by E4M3 error only
+    rel = lambda u_, v: np.linalg.norm(u_ - v) / np.linalg.norm(v)
+    assert rel(dw13, W13.grad.numpy()) < 0.05
+    assert rel(dx, xt.grad.numpy()) < 0.08

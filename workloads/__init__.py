@@ -77,6 +77,12 @@ CONFIGS = {
     "v3_prefill_fp8": LayerConfig("v3_prefill_fp8", 4, T=16384, d=7168, Nr=256, Ns=1, I=2048, K=8,
                                   act="bf16", weights="e4m3", x_fp8=True, routing="zipf",
                                   bias_init="zero", steps=10),
+    # the v3_prefill_bf16 layer (same seeds: same tokens, centroids and weight
+    # draws) run on the E4M3 path, at the size the training step fits in
+    # 32-bit buffer offsets; a training workload only
+    "v3_train_fp8": LayerConfig("v3_train_fp8", 2, T=8192, d=7168, Nr=256, Ns=1, I=2048, K=8,
+                                act="bf16", weights="e4m3", x_fp8=True, routing="zipf",
+                                bias_init="zero", steps=10),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
