@@ -1,4 +1,5 @@
-// Backward of the grouped SwiGLU expert GEMMs on MFMA (gfx950, bf16).
+// Backward of the grouped SwiGLU expert GEMMs on MFMA (gfx950): bf16, and
+// the input-gradient products on E4M3 operands (k_dgrad8, further below).
 //
 // The forward (expert FFNs of the combine equation, "DeepSeek-V3 Technical
 // Report" reading guide, Method section 2, in SwiGLU form) computes per row
