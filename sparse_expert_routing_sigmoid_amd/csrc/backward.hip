@@ -477,7 +477,8 @@ moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const floa
               MOE_EUNSUPPORTED, "backward: operand of 2 GiB or more");
   const W8Ws L(P, d, I);
   MOE_REQUIRE(ws && ws_bytes >= L.total, MOE_EWORKSPACE, "workspace smaller than moe_gemm_backward_w8_workspace_bytes");
-  if (T == 0) return MOE_OK;
+  // T == 0 still launches: the weight-gradient kernels write the zeros of
+  // the experts without rows (every expert here)
   const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
   uint8_t* wb = static_cast<uint8_t*>(ws);
   launch_ffn_bwd_w8(cp<uint16_t>(x), w13, w13_scale, w2, w2_scale, cp<uint16_t>(h), cp<uint16_t>(ab),

@@ -1013,14 +1013,15 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
                        uint8_t* dabq, float* dabs, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
                        hipStream_t st) {
-  quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
+  // with no tokens every row is padding: nothing to quantise (and dy may be NULL)
+  if (T > 0) quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
   {
     const long long items = (long long)tiles_max * ((I + BT - 1) / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
     hipLaunchKernelGGL((k_dgrad8<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dys, w2, w2s, tile_map,
                        n_tiles, d, I, (uint32_t)(P * d), (uint32_t)(P * (d / 128) * 4), ab, dab);
   }
-  quantize_tiles(dab, MOE_BF16, P, 2LL * I, 1, 128, dabq, dabs, st);
+  if (T > 0) quantize_tiles(dab, MOE_BF16, P, 2LL * I, 1, 128, dabq, dabs, st);
   {
     const long long items = (long long)tiles_max * (d / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));

@@ -139,3 +139,54 @@ def test_fp8_training_step_matches_oracle(name):
     print(errs, flush=True)
     for k, v in errs.items():
         assert v <= TOL8, (k, v)
+
+
+def test_fp8_dgrad_experts_without_rows_and_no_tokens():
+    """Experts that receive no row get zero weight and centroid gradients on
+    the E4M3 path too, and a step without tokens writes zeros."""
+    cfg = CASES["small"].with_(T=8, Nr=64, K=2)
+    layer, w13, w2, u, e, b = build(cfg)
+    for t in (layer.dw13, layer.dw2, layer.de):
+        t.fill_(float("nan"))
+    layer.forward(u, e, b)
+    G = W.make_free((cfg.T, cfg.d), 1.0, 102, "cuda", torch.bfloat16)
+    du, de, dw13, dw2 = layer.backward(G, u, e)
+    torch.cuda.synchronize()
+    idle = np.nonzero(np_of(layer.expert_load) == 0)[0]
+    assert idle.size > 0
+    assert torch.count_nonzero(dw13[idle]).item() == 0 and torch.count_nonzero(dw2[idle]).item() == 0
+    assert torch.count_nonzero(de[idle]).item() == 0
+    gr = OB.layer_backward(*map(f64_of, (u, e, b, w13, w2)), cfg.Nr, cfg.Ns, cfg.K, f64_of(G), fp8_dgrad=True)
+    for name, got, want in (("du", du, gr.du), ("dw13", dw13, gr.dw13), ("dw2", dw2, gr.dw2)):
+        assert rel_l2(f64_of(got), want) <= TOL8, name
+
+    cfg0 = CASES["small"].with_(T=0)
+    layer, w13, w2, u, e, b = build(cfg0)
+    for t in (layer.dw13, layer.dw2, layer.de):
+        t.fill_(float("nan"))
+    layer.forward(u, e, b)
+    du, de, dw13, dw2 = layer.backward(torch.empty((0, cfg0.d), dtype=torch.bfloat16, device="cuda"), u, e)
+    torch.cuda.synchronize()
+    for t in (de, dw13, dw2):
+        assert torch.count_nonzero(t).item() == 0
+
+
+def test_fp8_training_step_single_token():
+    """One token on the E4M3 training path: one row per selected expert."""
+    from oracle.e4m3 import dequantize_tiles, quantize_tiles
+    cfg = TRAIN_CASES["small"].with_(T=1)
+    w13, w2 = W.make_expert_weights(cfg, "cuda")
+    w8 = M.quantize_weights(w13, w2)
+    layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True, tile_m=32,
+                       train=True)
+    u, e, b = W.make_tokens(cfg, 0, "cuda"), W.make_centroids(cfg, "cuda"), W.make_bias(cfg, "cuda")
+    layer.forward(u, e, b)
+    G = W.make_free((cfg.T, cfg.d), 1.0, 103, "cuda", torch.bfloat16)
+    du, de, dw13, dw2 = layer.backward(G, u, e)
+    torch.cuda.synchronize()
+    deq = lambda w: dequantize_tiles(*quantize_tiles(w.astype(np.float32), 128, 128), 128, 128)
+    w13q = np.stack([deq(x) for x in f64_of(w13)])
+    w2q = np.stack([deq(x) for x in f64_of(w2)])
+    gr = OB.layer_backward(*map(f64_of, (u, e, b)), w13q, w2q, cfg.Nr, cfg.Ns, cfg.K, f64_of(G), fp8_train=True)
+    for name, got, want in (("du", du, gr.du), ("de", de, gr.de), ("dw13", dw13, gr.dw13), ("dw2", dw2, gr.dw2)):
+        assert rel_l2(f64_of(got), want) <= TOL8, name
