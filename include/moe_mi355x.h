@@ -68,7 +68,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,        /* NULL pointer, size out of range, bad enum */
-  MOE_EUNSUPPORTED = 2,  /* a valid combination this build does not run */
+  MOE_EUNSUPPORTED = 2,  /* a valid combination the library does not run */
   MOE_EWORKSPACE = 3,    /* workspace smaller than the size helper returns */
   MOE_EHIP = 4           /* the HIP runtime reported an error at launch */
 } moe_status;
