@@ -70,15 +70,25 @@ TRAFFIC = {
     "v3_decode_fp8w": {"fetch_bytes": 11295357709, "write_bytes": 21428939, "digest": "c01919518e0da1b8"},
 }
 
+# HBM traffic of one backward expert GEMM call of the training step
+# (moe_expert_gemm_backward / _w8; the latter with its two 1x128
+# quantisation passes), taken the same way from `--train` runs.
+TRAIN_TRAFFIC = {
+    "v3_prefill_bf16": {"fetch_bytes": 55988263519, "write_bytes": 24408685621, "digest": "d30af24c894f6eac",
+                        "sources": ("gemm_bwd.hip", "common.h")},
+    "v3_train_fp8": {"fetch_bytes": 37168045412, "write_bytes": 25352244192, "digest": "383ac4ea96a0acc0",
+                     "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
+}
+
 # Source files of the kernels each workload's expert GEMM runs.
 GEMM_SOURCES = {"v3_decode_fp8w": ("gemm_w8.hip", "common.h")}
 DEFAULT_GEMM_SOURCES = ("gemm_mfma.hip", "common.h")
 
 
-def gemm_source_digest(workload):
+def gemm_source_digest(workload, sources=None):
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES.get(workload, DEFAULT_GEMM_SOURCES):
+    for f in sources or GEMM_SOURCES.get(workload, DEFAULT_GEMM_SOURCES):
         with open(os.path.join(ROOT, "sparse_expert_routing_sigmoid_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -431,8 +441,12 @@ def train_main(args, cfg, dev, stream):
         kernels = ("moe_expert_gemm_backward_w8 call: k_quant_1x128 (dy), k_dgrad8 (down + SwiGLU backward), "
                    "k_quant_1x128 ([da|db]), k_dgrad8 (gate/up), k_wgrad (down), k_wgrad (gate/up); peak = the "
                    "call's flops over their time at the E4M3 (dgrad) and bf16 (wgrad) peaks")
+    tt = TRAIN_TRAFFIC.get(cfg.name) if (w8 is not None) == fp8_step else None
+    traffic = None
+    if tt and gemm_source_digest(cfg.name, tt["sources"]) == tt["digest"]:
+        traffic = (tt["fetch_bytes"] + tt["write_bytes"]) / 1e9
     roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": None, "kernel": kernels,
+            "frac": achieved / peak, "traffic": traffic, "traffic_unit": "GB per call", "kernel": kernels,
             "units_per_launch": {"rows": rows, "flops": bwd_flops}, "avg_launch_ms": bwd_ms}
     out = {
         "metric": TRAIN_METRIC,
