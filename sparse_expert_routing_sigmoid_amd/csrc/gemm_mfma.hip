@@ -523,6 +523,7 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
   __shared__ int s_ustart[SCHED_MAXU + 1], s_urows[SCHED_MAXU], s_order[SCHED_MAXU];
   __shared__ int s_uoffA[SCHED_MAXU], s_uoffB[SCHED_MAXU];
   __shared__ unsigned char s_uxcd[SCHED_MAXU];
+  __shared__ int s_xlist[SCHED_MAXU + 16];  // each XCD's units in deal order
   __shared__ int s_part[1024];
   __shared__ int s_nu, s_xA[8], s_xB[8];
   const int tid = threadIdx.x;
@@ -582,10 +583,14 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
   __syncthreads();
   // Deal the units in rank order in snake rounds (0..7, 7..0, ...), each
   // round's largest to the XCD that got the smallest of the last round.  Then
-  // one thread per XCD walks its units to place their items.
+  // one thread per XCD walks its units to place their items: phase A largest
+  // unit first; phase B alternately from the large and the small end, so the
+  // weight-streaming items of few-row experts run next to the MFMA-bound
+  // items of many-row ones.
   if (tid < 8) {
     const int x = tid;
-    int nA = 0, nB = 0;
+    const int stride = (nu + 7) / 8 + 1;  // an XCD gets at most one unit per round of 8
+    int nA = 0, m = 0;
     for (int i = 0;; ++i) {
       const int r = 8 * i + ((i & 1) ? 7 - x : x);
       if (r >= nu) break;
@@ -593,9 +598,14 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
       const int len = s_ustart[v + 1] - s_ustart[v];
       s_uxcd[v] = (unsigned char)x;
       s_uoffA[v] = nA;
-      s_uoffB[v] = nB;
       nA += len * ntA;
-      nB += len * ntB;
+      s_xlist[x * stride + m++] = v;
+    }
+    int nB = 0;
+    for (int k = 0; k < m; ++k) {
+      const int v = s_xlist[x * stride + ((k & 1) ? m - 1 - (k >> 1) : (k >> 1))];
+      s_uoffB[v] = nB;
+      nB += (s_ustart[v + 1] - s_ustart[v]) * ntB;
     }
     s_xA[x] = nA;
     s_xB[x] = nB;
