@@ -341,7 +341,8 @@ moe_status moe_combine_backward(const void* grad_out, moe_dtype g_t, const void*
  *   h, ab          device, from moe_expert_gemm_train
  *   dy             device [P_max, d] bf16 from moe_combine_backward
  *   ws             device, moe_gemm_backward_workspace_bytes(...) bytes
- *                  (holds [da | db] of every row)
+ *                  (holds [da | db] of every row and the weight-gradient
+ *                  kernels' list of experts per XCD)
  *   dx             device [P_max, d] bf16 out (padding rows unwritten)
  *   dw13, dw2      device [Nr+Ns, 2I, d] and [Nr+Ns, d, I] out (overwritten;
  *                  experts with no rows get zeros), dw_t MOE_F32 or MOE_BF16

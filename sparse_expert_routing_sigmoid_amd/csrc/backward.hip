@@ -42,12 +42,13 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
                        const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
                        int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
-                       uint8_t* dabq, float* dabs, uint16_t* dx, void* dw13, void* dw2, bool dw_f32, hipStream_t st);
+                       uint8_t* dabq, float* dabs, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                       hipStream_t st);
 void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const uint16_t* h,
                          const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset, const int32_t* row_token,
                          const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d,
-                         int I, int Nr, int Ns, uint16_t* dab, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
-                         hipStream_t st);
+                         int I, int Nr, int Ns, uint16_t* dab, int* deal, uint16_t* dx, void* dw13, void* dw2,
+                         bool dw_f32, hipStream_t st);
 
 namespace {
 
@@ -401,9 +402,14 @@ moe_status combine_backward(const void* grad_out, moe_dtype g_t, const void* y, 
   return launch_status("moe_combine_backward");
 }
 
+// Workspace of the bf16 backward: [da | db] bf16 [P, 2I], then the wgrad's
+// expert-to-XCD deal (8 x ceil(Nr / 8) int32).
+static size_t deal_bytes(int Nr) { return (size_t)8 * ((Nr + 7) / 8) * 4; }
+static size_t bwd_deal_offset(size_t P, int I) { return (P * (size_t)(2 * I) * 2 + 255) / 256 * 256; }
+
 size_t gemm_backward_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
   if (T < 0 || d < 1 || I < 1 || Nr < 1 || Ns < 0 || K < 1 || tile_m < 1) return 0;
-  return permute_rows(T, K, Nr, Ns, tile_m) * (size_t)(2 * I) * 2;
+  return bwd_deal_offset(permute_rows(T, K, Nr, Ns, tile_m), I) + deal_bytes(Nr);
 }
 
 moe_status expert_gemm_backward(const void* x, const void* w13, const void* w2, const void* h, const void* ab,
@@ -429,29 +435,31 @@ moe_status expert_gemm_backward(const void* x, const void* w13, const void* w2, 
   const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
   launch_ffn_bwd_bf16(cp<uint16_t>(x), cp<uint16_t>(w13), cp<uint16_t>(w2), cp<uint16_t>(h), cp<uint16_t>(ab),
                       cp<uint16_t>(dy), seg_offset, row_token, tile_map, n_tiles, tiles_max, T, (long long)P, d, I, Nr,
-                      Ns, static_cast<uint16_t*>(ws), static_cast<uint16_t*>(dx), dw13, dw2, dw_t == MOE_F32,
-                      as_stream(stream));
+                      Ns, static_cast<uint16_t*>(ws),
+                      reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + bwd_deal_offset(P, I)),
+                      static_cast<uint16_t*>(dx), dw13, dw2, dw_t == MOE_F32, as_stream(stream));
   return launch_status("moe_expert_gemm_backward");
 }
 
 // Workspace of the E4M3-dgrad backward: [da | db] bf16, its E4M3 codes, the
 // codes of dy, then the fp32 1x128 scales of both, each part 256-byte aligned.
 struct W8Ws {
-  size_t dab, dabq, dyq, dabs, dys, total;
-  W8Ws(size_t P, int d, int I) {
+  size_t dab, dabq, dyq, dabs, dys, deal, total;
+  W8Ws(size_t P, int d, int I, int Nr) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     dab = 0;
     dabq = dab + up(P * 2 * I * 2);
     dyq = dabq + up(P * 2 * I);
     dabs = dyq + up(P * d);
     dys = dabs + up(P * (2 * I / 128) * 4);
-    total = dys + up(P * (d / 128) * 4);
+    deal = dys + up(P * (d / 128) * 4);
+    total = deal + deal_bytes(Nr);
   }
 };
 
 size_t gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
   if (T < 0 || d < 128 || I < 64 || Nr < 1 || Ns < 0 || K < 1 || tile_m < 1) return 0;
-  return W8Ws(permute_rows(T, K, Nr, Ns, tile_m), d, I).total;
+  return W8Ws(permute_rows(T, K, Nr, Ns, tile_m), d, I, Nr).total;
 }
 
 moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
@@ -475,7 +483,7 @@ moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const floa
   MOE_REQUIRE(fits31((unsigned long long)T * d * 2) && fits31((unsigned long long)P * d * 2) &&
                   fits31((unsigned long long)P * 2 * I * 2) && fits31((unsigned long long)2 * I * d * 2),
               MOE_EUNSUPPORTED, "backward: operand of 2 GiB or more");
-  const W8Ws L(P, d, I);
+  const W8Ws L(P, d, I, Nr);
   MOE_REQUIRE(ws && ws_bytes >= L.total, MOE_EWORKSPACE, "workspace smaller than moe_gemm_backward_w8_workspace_bytes");
   // T == 0 still launches: the weight-gradient kernels write the zeros of
   // the experts without rows (every expert here)
@@ -484,8 +492,8 @@ moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const floa
   launch_ffn_bwd_w8(cp<uint16_t>(x), w13, w13_scale, w2, w2_scale, cp<uint16_t>(h), cp<uint16_t>(ab),
                     cp<uint16_t>(dy), seg_offset, row_token, tile_map, n_tiles, tiles_max, T, (long long)P, d, I, Nr,
                     Ns, reinterpret_cast<uint16_t*>(wb + L.dab), wb + L.dyq, reinterpret_cast<float*>(wb + L.dys),
-                    wb + L.dabq, reinterpret_cast<float*>(wb + L.dabs), static_cast<uint16_t*>(dx), dw13, dw2,
-                    dw_t == MOE_F32, as_stream(stream));
+                    wb + L.dabq, reinterpret_cast<float*>(wb + L.dabs), reinterpret_cast<int*>(wb + L.deal),
+                    static_cast<uint16_t*>(dx), dw13, dw2, dw_t == MOE_F32, as_stream(stream));
   return launch_status("moe_expert_gemm_backward_w8");
 }
 

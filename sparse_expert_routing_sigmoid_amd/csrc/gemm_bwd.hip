@@ -862,6 +862,27 @@ __device__ __forceinline__ void wgrad_run(SegRows<GATHER, 8>& S, uint8_t* __rest
   }
 }
 
+// The routed experts of the wgrad dealt to the 8 XCDs by their (padded)
+// row counts: ranked largest first (ties: lower index first), dealt in
+// snake rounds (0..7, 7..0, ...), so every XCD gets a like share of the
+// rows.  deal[x * S + i] is XCD x's i-th expert, -1 past its last;
+// S = ceil(Nr / 8).  One block; Nr <= 1024.
+__global__ __launch_bounds__(1024) void k_wgrad_deal(const int32_t* __restrict__ seg_offset, int Nr,
+                                                     int* __restrict__ deal) {
+  __shared__ int s_len[1024];
+  const int S = (Nr + 7) / 8;
+  for (int v = threadIdx.x; v < Nr; v += 1024) s_len[v] = seg_offset[v + 1] - seg_offset[v];
+  for (int q = threadIdx.x; q < 8 * S; q += 1024) deal[q] = -1;
+  __syncthreads();
+  for (int v = threadIdx.x; v < Nr; v += 1024) {
+    const int lv = s_len[v];
+    int rank = 0;
+    for (int w = 0; w < Nr; ++w) rank += (s_len[w] > lv) || (s_len[w] == lv && w < v);
+    const int i = rank >> 3, k = rank & 7;
+    deal[((i & 1) ? 7 - k : k) * S + i] = v;
+  }
+}
+
 // dW_e [M, N] = A_e^T B_e over the K-rows of segment e.  An item is (expert,
 // M tile, run of N tiles): one block computes the N tiles of the run one
 // after the other with the same K-rows (the tokens are fetched once per
@@ -878,7 +899,7 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
                                                     const int32_t* __restrict__ seg_offset,
                                                     const int32_t* __restrict__ row_token, int P_rows, int E, int Nr,
                                                     int Md, int Nd, int nch, uint32_t a_bytes, uint32_t b_bytes,
-                                                    OT* __restrict__ out) {
+                                                    const int* __restrict__ deal, OT* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP];
   __shared__ __attribute__((aligned(1024))) uint8_t stq[BOP];
@@ -887,8 +908,9 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
   const int ntm = (Md + BT - 1) / BT, ntn = (Nd + BT - 1) / BT;
   const int runs = (ntn + nch - 1) / nch;  // runs of a routed expert's M tile
   // Block b runs on XCD b % 8.  XCD x takes every 8th shared item (from x),
-  // then all items of the routed experts x, x + 8, ..., so the blocks that
-  // share an expert's rows run together in one L2.
+  // then all items of its routed experts (k_wgrad_deal: shares of like row
+  // counts), so the blocks that share an expert's rows run together in one
+  // L2.
   const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int shared_items = (E - Nr) * ntm * ntn;
   const int my_shared = shared_items > x ? (shared_items - x + 7) / 8 : 0;
@@ -901,9 +923,12 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
     n0 = rem % ntn;
     n1 = n0 + 1;
   } else {
-    const int r = slot - my_shared;
-    e = x + 8 * (r / (ntm * runs));
-    if (e >= Nr) return;
+    const int r = slot - my_shared, i = r / (ntm * runs), S = (Nr + 7) / 8;
+    // the grid gives every XCD ceil(shared items / 8) shared slots: an XCD
+    // with one shared item fewer has one slot past its list (i == S)
+    if (i >= S) return;
+    e = deal[x * S + i];
+    if (e < 0) return;
     const int rem = r % (ntm * runs);
     m = rem / runs;
     n0 = (rem % runs) * nch;
@@ -948,8 +973,9 @@ bool ffn_bwd_ok(int d, int I) { return d % 256 == 0 && I % 128 == 0; }
 // in dw_f32 ? fp32 : bf16, routed runs of 4 N tiles.
 static void launch_wgrads(const uint16_t* x, const uint16_t* h, const uint16_t* dy, const uint16_t* dab,
                           const int32_t* seg_offset, const int32_t* row_token, int T, long long P, int d, int I,
-                          int Nr, int Ns, void* dw13, void* dw2, bool dw_f32, hipStream_t st) {
+                          int Nr, int Ns, int* deal, void* dw13, void* dw2, bool dw_f32, hipStream_t st) {
   const int E = Nr + Ns;
+  hipLaunchKernelGGL(k_wgrad_deal, dim3(1), dim3(1024), 0, st, seg_offset, Nr, deal);
   const uint32_t dy_bytes = (uint32_t)(P * d * 2), dab_bytes = (uint32_t)(P * 2 * I * 2);
   const uint32_t h_bytes = (uint32_t)(P * I * 2), x_bytes = (uint32_t)((long long)T * d * 2);
   {
@@ -957,20 +983,20 @@ static void launch_wgrads(const uint16_t* x, const uint16_t* h, const uint16_t* 
     const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
     if (dw_f32)
       hipLaunchKernelGGL((k_wgrad<false, float>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
-                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<float*>(dw2));
+                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, deal, static_cast<float*>(dw2));
     else
       hipLaunchKernelGGL((k_wgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, h, seg_offset, row_token,
-                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, static_cast<uint16_t*>(dw2));
+                         (int)P, E, Nr, d, I, nch, dy_bytes, h_bytes, deal, static_cast<uint16_t*>(dw2));
   }
   {
     const int ntm = 2 * I / BT, ntn = d / BT, nch = 4;
     const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
     if (dw_f32)
       hipLaunchKernelGGL((k_wgrad<true, float>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
-                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<float*>(dw13));
+                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, deal, static_cast<float*>(dw13));
     else
       hipLaunchKernelGGL((k_wgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, x, seg_offset, row_token,
-                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, static_cast<uint16_t*>(dw13));
+                         (int)P, E, Nr, 2 * I, d, nch, dab_bytes, x_bytes, deal, static_cast<uint16_t*>(dw13));
   }
 }
 
@@ -980,8 +1006,8 @@ static void launch_wgrads(const uint16_t* x, const uint16_t* h, const uint16_t* 
 void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const uint16_t* h,
                          const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset, const int32_t* row_token,
                          const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d,
-                         int I, int Nr, int Ns, uint16_t* dab, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
-                         hipStream_t st) {
+                         int I, int Nr, int Ns, uint16_t* dab, int* deal, uint16_t* dx, void* dw13, void* dw2,
+                         bool dw_f32, hipStream_t st) {
   const uint32_t dy_bytes = (uint32_t)(P * d * 2), dab_bytes = (uint32_t)(P * 2 * I * 2);
   // dgrad, down + SwiGLU: N = I
   {
@@ -997,7 +1023,7 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
     hipLaunchKernelGGL((k_dgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, w13, tile_map, n_tiles,
                        2 * I, d, dab_bytes, nullptr, dx);
   }
-  launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, dw13, dw2, dw_f32, st);
+  launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, deal, dw13, dw2, dw_f32, st);
 }
 
 // d <= 16384 and I <= 8192: a lane holds the block scales of two K blocks.
@@ -1011,7 +1037,7 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
                        const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
                        int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
-                       uint8_t* dabq, float* dabs, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                       uint8_t* dabq, float* dabs, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
                        hipStream_t st) {
   // with no tokens every row is padding: nothing to quantise (and dy may be NULL)
   if (T > 0) quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
@@ -1029,7 +1055,7 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        tile_map, n_tiles, 2 * I, d, (uint32_t)(P * 2 * I), (uint32_t)(P * (2 * I / 128) * 4), nullptr,
                        dx);
   }
-  launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, dw13, dw2, dw_f32, st);
+  launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, deal, dw13, dw2, dw_f32, st);
 }
 
 }  // namespace moe

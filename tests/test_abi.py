@@ -152,7 +152,7 @@ def test_backward_entry_points_reject_bad_arguments():
     assert gb(dy=ctypes.c_void_p(0x1002))[0] == M.MOE_EINVAL   # misaligned
     assert gb(wsb=16)[0] == M.MOE_EWORKSPACE
     need = M.moe_gemm_backward_workspace_bytes(T, K, Nr, Ns, d, I, tm)
-    assert need == M.moe_permute_rows(T, K, Nr, Ns, tm) * 2 * I * 2
+    assert need >= M.moe_permute_rows(T, K, Nr, Ns, tm) * 2 * I * 2 + 8 * ((Nr + 7) // 8) * 4
     g8 = lambda **kw: _status(L.moe_expert_gemm_backward_w8, *[kw.get(k, v) for k, v in dict(
         x=F, w13=F, w13s=F, w2=F, w2s=F, h=F, ab=F, dy=F, T=T, K=K, Nr=Nr, Ns=Ns, d=d, I=I, tm=tm, so=F, rt=F,
         tmap=F, nt=F, ws=F, wsb=big, dx=F, dw13=F, dw2=F, dwt=M.MOE_BF16, st=None).items()])
