@@ -26,18 +26,26 @@ every tensor in E4M3 with 1x128 tiles for activations and 128x128 blocks for
 weights.  Reading B2: the two input-gradient products (dh = dy W2 and
 dx = [da | db] W13) take the activation gradient in 1x128 tiles along their
 K axis and the weights in the forward's 128x128 blocks, each tile with its
-power-of-two scale (R10 of oracle/moe.py); the activation gradient is
-rounded to fp32 before it is quantised.  The weight-gradient products stay
+power-of-two scale (R10 of oracle/moe.py).  The weight-gradient products stay
 unquantised: their K axis is the token axis, along which the pages give no
 tiling.
 
+Reading B4 (the precision in which an E4M3 code is decided): activations and
+activation gradients are bf16 tensors, as every activation of the layer is
+stored.  So dy and [da | db] are rounded to bf16 (through fp32, round to
+nearest even) before their 1x128 quantisation, and the SwiGLU backward is
+evaluated at the pre-activations a, b as the training forward keeps them,
+rounded to bf16.  The codes are then decided from the same values the GPU
+quantises; the weight gradients, which decide no code, use the unrounded
+fp64 values.
+
 FP8 training step (ffn_backward_fp8_train): the forward of the FP8 path
 (oracle/moe.py, R8: x in 1x128 tiles, h re-quantised in 1x128 tiles, the
-weights in 128x128 blocks) followed by the backward of reading B2.  Reading
-B3: every quantiser passes the gradient straight through (it is treated as
-the identity when differentiated), so dW2 uses the quantised h that the
-down projection multiplied, and dW13 uses the unquantised expert input x
-(the token rows as stored, which the weight-gradient products read).
+weights in 128x128 blocks) followed by the backward of readings B2 and B4.
+Reading B3: every quantiser of the forward passes the gradient straight
+through (it is the identity when differentiated), so each weight gradient
+uses the quantised operand that its forward product multiplied: dW2 the
+quantised h, dW13 the quantised expert input Q(x).
 """
 from __future__ import annotations
 
@@ -95,24 +103,47 @@ def ffn_backward(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray)
     return dx, dw13, dw2, y
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """x as the GPU stores an fp32 result in bf16 (reading B4): rounded to
+    fp32, then to the nearest bf16, ties to even.  bf16 keeps the sign, the 8
+    exponent bits and the top 7 fraction bits of an fp32, so rounding adds
+    half of the dropped 16-bit field (minus one unless the kept lowest bit is
+    set) and truncates.  Returns fp64 (exact).  Finite input only."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if not np.all(np.isfinite(f)):
+        raise ValueError("round_bf16: non-finite input")
+    bits = f.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def _q_act(g: np.ndarray) -> np.ndarray:
-    """g rounded to fp32, then through 1x128 E4M3 tiles (code x scale, fp64)."""
+    """g rounded to fp32, then through 1x128 E4M3 tiles (code x scale, fp64):
+    the forward's activation quantiser (R8)."""
     q, s = quantize_tiles(np.asarray(g, dtype=np.float64).astype(np.float32), 1, 128)
     return dequantize_tiles(q, s, 1, 128)
 
 
+def _q_grad(g: np.ndarray) -> np.ndarray:
+    """An activation gradient as the E4M3 backward products take it: rounded
+    to bf16 (B4), then through 1x128 E4M3 tiles (B2)."""
+    return _q_act(round_bf16(g))
+
+
 def fp8_tile_matmul(g: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """g [n, K] @ w [K, N] with both operands in E4M3 (reading B2): g in
-    1x128 tiles along K (rounded to fp32 first), w in 128x128 blocks of its
-    stored layout; the dequantised values (code x power-of-two scale, exact)
-    are multiplied in fp64."""
+    """g [n, K] @ w [K, N] with both operands in E4M3 (reading B2): g, whose
+    values must be exact in fp32, in 1x128 tiles along K, w in 128x128 blocks
+    of its stored layout; the dequantised values (code x power-of-two scale,
+    exact) are multiplied in fp64."""
     wq, ws = quantize_tiles(np.asarray(w, dtype=np.float64).astype(np.float32), 128, 128)
-    return _q_act(g) @ dequantize_tiles(wq, ws, 128, 128)
+    gq, gs = quantize_tiles(np.asarray(g), 1, 128)
+    return dequantize_tiles(gq, gs, 1, 128) @ dequantize_tiles(wq, ws, 128, 128)
 
 
 def ffn_backward_fp8(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray):
-    """ffn_backward with the input-gradient products in E4M3 (reading B2):
-    dh = Q(dy) Q(W2), dx = Q([da | db]) Q(W13); the weight gradients use the
+    """ffn_backward with the input-gradient products in E4M3 (readings B2,
+    B4): dh = Q(bf16(dy)) Q(W2), dx = Q(bf16([da | db])) Q(W13), with da, db
+    evaluated at the bf16 pre-activations; the weight gradients use the
     unquantised dy and [da | db].  Returns (dx, dw13, dw2, y)."""
     x, w13, w2, dy = _f64(x), _f64(w13), _f64(w2), _f64(dy)
     I = w2.shape[1]
@@ -121,36 +152,39 @@ def ffn_backward_fp8(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndar
     h = silu(a) * b
     y = h @ w2.T
     dw2 = dy.T @ h
-    dh = fp8_tile_matmul(dy, w2)
-    da = dh * b * silu_grad(a)
-    db = dh * silu(a)
+    dh = fp8_tile_matmul(round_bf16(dy), w2)
+    ar, br = round_bf16(a), round_bf16(b)
+    da = dh * br * silu_grad(ar)
+    db = dh * silu(ar)
     dab = np.concatenate([da, db], axis=1)
     dw13 = dab.T @ x
-    dx = fp8_tile_matmul(dab, w13)
+    dx = fp8_tile_matmul(round_bf16(dab), w13)
     return dx, dw13, dw2, y
 
 
 def ffn_backward_fp8_train(x: np.ndarray, w13q: np.ndarray, w2q: np.ndarray, dy: np.ndarray):
-    """Forward and backward of one expert on the FP8 training path (reading
-    B3).  x [n, d] the expert's input rows as stored; w13q [2I, d], w2q
+    """Forward and backward of one expert on the FP8 training path (readings
+    B2-B4).  x [n, d] the expert's input rows as stored; w13q [2I, d], w2q
     [d, I] the decoded E4M3 weights (code x block scale).
       forward:  [a; b] = W13q Q(x),  h = Q(SiLU(a) b),  y = W2q h
-      backward: dW2 = dy^T h,  dh = Q(dy) W2q,  da, db as ffn_backward,
-                dW13 = [da | db]^T x,  dx = Q([da | db]) W13q
+      backward: dW2 = dy^T h,  dh = Q(bf16(dy)) W2q,  da, db at bf16(a), bf16(b),
+                dW13 = [da | db]^T Q(x),  dx = Q(bf16([da | db])) W13q
     Q: 1x128 E4M3 tiles along the row.  Returns (dx, dw13, dw2, y)."""
     x, w13q, w2q, dy = _f64(x), _f64(w13q), _f64(w2q), _f64(dy)
     I = w2q.shape[1]
-    ab = _q_act(x) @ w13q.T
+    xq = _q_act(x)
+    ab = xq @ w13q.T
     a, b = ab[:, :I], ab[:, I:]
     h = _q_act(silu(a) * b)
     y = h @ w2q.T
     dw2 = dy.T @ h
-    dh = _q_act(dy) @ w2q
-    da = dh * b * silu_grad(a)
-    db = dh * silu(a)
+    dh = _q_grad(dy) @ w2q
+    ar, br = round_bf16(a), round_bf16(b)
+    da = dh * br * silu_grad(ar)
+    db = dh * silu(ar)
     dab = np.concatenate([da, db], axis=1)
-    dw13 = dab.T @ x
-    dx = _q_act(dab) @ w13q
+    dw13 = dab.T @ xq
+    dx = _q_grad(dab) @ w13q
     return dx, dw13, dw2, y
 
 

@@ -85,15 +85,6 @@ class Routing:
     inner_gap: np.ndarray     # [T, K-1] v_(k) - v_(k+1) inside the selection
 
 
-def select_topk(v: np.ndarray, K: int) -> np.ndarray:
-    """Indices of the K largest keys per row, in (key desc, index asc) order.
-
-    A stable sort of -v keeps equal keys in ascending index order, which is
-    exactly reading R2 ([RG-MoE] gate equation: the Topk set, ordered)."""
-    order = np.argsort(-v, axis=1, kind="stable")
-    return order[:, :K]
-
-
 def route(u: np.ndarray, e: np.ndarray, b: np.ndarray, K: int) -> Routing:
     """Sigmoid routing with a bias that steers selection but not the gate.
 

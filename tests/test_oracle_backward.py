@@ -176,6 +176,7 @@ def test_fp8_tile_matmul_error_within_the_rounding_bound():
     2^-6), so each product entry is within sum |g| e_w + e_g |w| + e_g e_w."""
     rng = np.random.default_rng(6)
     g = rng.standard_normal((40, 256)) * np.exp(rng.standard_normal((40, 1)))
+    g = g.astype(np.float32).astype(np.float64)        # the operand must be exact in fp32
     w = rng.standard_normal((256, 384)) / 16
     got = B.fp8_tile_matmul(g, w)
     want = g @ w
@@ -187,7 +188,7 @@ def test_fp8_tile_matmul_error_within_the_rounding_bound():
         s = np.repeat(np.repeat(s, tile_rows, 0), tile_cols, 1)
         return np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10)
 
-    eg, ew = step_bound(g.astype(np.float32).astype(np.float64), 1, 128), step_bound(w, 128, 128)
+    eg, ew = step_bound(g, 1, 128), step_bound(w, 128, 128)
     bound = np.abs(g) @ ew + eg @ np.abs(w) + eg @ ew
     assert np.all(np.abs(got - want) <= bound * (1 + 1e-12) + 1e-300)
     assert np.linalg.norm(got - want) / np.linalg.norm(want) < 0.05
@@ -237,35 +238,161 @@ def test_fp8_train_step_forward_is_the_fp8_forward():
     assert np.allclose(g.dgate, dgate, rtol=1e-12, atol=1e-12)
 
 
-def test_fp8_train_step_straight_through_gradients():
-    """With quantisers treated as the identity (B3) the FP8 training step's
-    gradients equal the fp64 autograd gradients of the same function in which
-    each quantiser's output is a constant offset added to its input: checked
-    here by torch autograd with Q(z) = z + (Q(z) - z).detach()."""
-    rng = np.random.default_rng(8)
-    n, d, I = 16, 256, 128
-    x = rng.standard_normal((n, d))
-    w13q = O.quantize_activations(rng.standard_normal((2 * I, d)) / 16)
-    w2q = O.quantize_activations(rng.standard_normal((d, I)) / 16)
-    dy = rng.standard_normal((n, d))
-    dx, dw13, dw2, y = B.ffn_backward_fp8_train(x, w13q, w2q, dy)
+# ---------------------------------------------------------- exact pins --
+# The FP8 backward variants against fp64 PyTorch autograd.  The readings are
+# built into the autograd graph with three devices of its own, none of which
+# restates the oracle's derivative formulas:
+#   st_q(t)     value Q(t), gradient the identity (a straight-through
+#               quantiser of the forward, B3);
+#   GradQ       value t, gradient Q(bf16(dL/dt)) (the gradient operand of an
+#               E4M3 input-gradient product, B2 and B4);
+#   at_bf16(t)  value bf16(t), gradient the identity, so that autograd's own
+#               derivative of the SwiGLU is taken at the stored bf16
+#               pre-activations (B4) while the forward value stays exact.
+# A product whose two gradients differ (dW from the unquantised gradient, dX
+# from the quantised one times the E4M3 weight Wq) is split as
+# X.detach() W^T + GradQ(X Wq^T) - (X Wq^T).detach(): its value is X W^T,
+# autograd sends dL/dY to dW and Q(bf16(dL/dY)) Wq to dX.
 
-    def q(t):   # forward value of the oracle's quantiser, gradient of the identity
-        return t + (torch.from_numpy(O.quantize_activations(t.detach().numpy().astype(np.float32))) - t).detach()
+def _q_tiles(a: np.ndarray, rows: int = 1) -> np.ndarray:
+    from oracle.e4m3 import dequantize_tiles, quantize_tiles
+    return dequantize_tiles(*quantize_tiles(a.astype(np.float32), rows, 128), rows, 128)
 
+
+def _bf16(a: np.ndarray) -> np.ndarray:
+    """torch's own bf16 rounding (independent of oracle.backward.round_bf16)."""
+    return torch.from_numpy(np.asarray(a, dtype=np.float64)).float().to(torch.bfloat16).double().numpy()
+
+
+class GradQ(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, t):
+        return t.view_as(t)
+
+    @staticmethod
+    def backward(ctx, g):
+        return torch.from_numpy(_q_tiles(_bf16(g.numpy())))
+
+
+def st_q(t):
+    return t + (torch.from_numpy(_q_tiles(t.detach().numpy())) - t).detach()
+
+
+def at_bf16(t):
+    return t + (torch.from_numpy(_bf16(t.detach().numpy())) - t).detach()
+
+
+def _split_product(x, w, wq):
+    return x.detach() @ w.T + GradQ.apply(x @ wq.T) - (x @ wq.T).detach()
+
+
+def _autograd_ffn(x, w13, w2, dy, train: bool):
+    """(dx, dW13, dW2, y) of one expert by autograd; train: the FP8 training
+    step (forward quantisers st_q on x and h), else the bf16 forward."""
+    I = w2.shape[1]
     xt = torch.tensor(x, requires_grad=True)
-    W13 = torch.tensor(w13q, requires_grad=True)
-    W2 = torch.tensor(w2q, requires_grad=True)
-    ab = q(xt) @ W13.T
+    W13 = torch.tensor(w13, requires_grad=True)
+    W2 = torch.tensor(w2, requires_grad=True)
+    W13q = torch.from_numpy(_q_tiles(w13, 128))   # the E4M3 weights of the dgrad products
+    W2q = torch.from_numpy(_q_tiles(w2, 128))
+    xin = st_q(xt) if train else xt
+    ab = _split_product(xin, W13, W13q)
     a, b = ab[:, :I], ab[:, I:]
-    h = q(a * torch.sigmoid(a) * b)
-    yt = h @ W2.T
-    assert np.allclose(yt.detach().numpy(), y, rtol=1e-12, atol=1e-12)
-    (yt * torch.from_numpy(dy)).sum().backward()
-    # dW2 and the exact dW13 of this function (through Q(x)) vs the oracle's
-    assert np.allclose(W2.grad.numpy(), dw2, rtol=1e-10, atol=1e-10)
-    # the oracle's dW13 reads the unquantised x (B3) and its dx quantises the
-    # gradients (B2): both differ from straight-through autograd by E4M3 error only
-    rel = lambda u_, v: np.linalg.norm(u_ - v) / np.linalg.norm(v)
-    assert rel(dw13, W13.grad.numpy()) < 0.05
-    assert rel(dx, xt.grad.numpy()) < 0.08
+    h_val = (a * torch.sigmoid(a) * b).detach()
+    if train:
+        h_val = torch.from_numpy(_q_tiles(h_val.numpy()))
+    ar, br = at_bf16(a), at_bf16(b)
+    h_r = ar * torch.sigmoid(ar) * br
+    h = h_val + (h_r - h_r.detach())      # value h (Q(h) in training); gradient at bf16(a), bf16(b)
+    y = _split_product(h, W2, W2q)
+    (y * torch.from_numpy(dy)).sum().backward()
+    return xt.grad.numpy(), W13.grad.numpy(), W2.grad.numpy(), y.detach().numpy()
+
+
+def _assert_same(got, want, name):
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-13 * np.abs(want).max(), err_msg=name)
+
+
+@pytest.mark.parametrize("seed", [8, 9])
+def test_fp8_train_step_gradients_equal_autograd(seed):
+    """ffn_backward_fp8_train: forward Q(x), Q(h) (R8); quantisers straight
+    through (B3: dW13 = [da | db]^T Q(x), dW2 = dy^T Q(h)); E4M3 input-gradient
+    products (B2) of bf16 gradients; SwiGLU backward at the bf16
+    pre-activations (B4).  Equal to fp64 autograd of that graph."""
+    rng = np.random.default_rng(seed)
+    n, d, I = 16, 256, 128
+    x = _bf16(rng.standard_normal((n, d)))
+    w13q = O.quantize_activations(rng.standard_normal((2 * I, d)) / 16)   # E4M3 values, any fixed tiling
+    w2q = O.quantize_activations(rng.standard_normal((d, I)) / 16)
+    w13q, w2q = _q_tiles(w13q, 128), _q_tiles(w2q, 128)                  # on the 128x128-block grid
+    dy = _bf16(rng.standard_normal((n, d)) * 0.3)
+    dx, dw13, dw2, y = B.ffn_backward_fp8_train(x, w13q, w2q, dy)
+    gx, g13, g2, yt = _autograd_ffn(x, w13q, w2q, dy, train=True)
+    np.testing.assert_allclose(y, yt, rtol=1e-12, atol=1e-12)
+    _assert_same(dw2, g2, "dW2")
+    _assert_same(dw13, g13, "dW13")
+    _assert_same(dx, gx, "dx")
+
+
+def test_fp8_dgrad_gradients_equal_autograd():
+    """ffn_backward_fp8 (bf16 forward, E4M3 input-gradient products on the
+    weights' 128x128 blocks): the same graph without the forward
+    quantisers."""
+    rng = np.random.default_rng(10)
+    n, d, I = 24, 256, 128
+    x = _bf16(rng.standard_normal((n, d)))
+    w13 = _bf16(rng.standard_normal((2 * I, d)) / 16)
+    w2 = _bf16(rng.standard_normal((d, I)) / 16)
+    dy = _bf16(rng.standard_normal((n, d)) * 0.3)
+    dx, dw13, dw2, y = B.ffn_backward_fp8(x, w13, w2, dy)
+    gx, g13, g2, yt = _autograd_ffn(x, w13, w2, dy, train=False)
+    np.testing.assert_allclose(y, yt, rtol=1e-12, atol=1e-12)
+    _assert_same(dw2, g2, "dW2")
+    _assert_same(dw13, g13, "dW13")
+    _assert_same(dx, gx, "dx")
+
+
+def test_fp8_train_step_plausible_mistakes_fail_the_pin():
+    """Each reading of the FP8 training step is visible to the autograd pin:
+    the unquantised x in dW13, quantising from fp32 instead of bf16, and the
+    SwiGLU backward at the fp64 pre-activations all move the gradients by
+    more than its tolerance."""
+    rng = np.random.default_rng(11)
+    n, d, I = 16, 256, 128
+    x = _bf16(rng.standard_normal((n, d)))
+    w13q = _q_tiles(O.quantize_activations(rng.standard_normal((2 * I, d)) / 16), 128)
+    w2q = _q_tiles(O.quantize_activations(rng.standard_normal((d, I)) / 16), 128)
+    dy = _bf16(rng.standard_normal((n, d)) * 0.3)
+    gx, g13, g2, _ = _autograd_ffn(x, w13q, w2q, dy, train=True)
+    xq = _q_tiles(x)
+    ab = xq @ w13q.T
+    a, b = ab[:, :I], ab[:, I:]
+    dh = _q_tiles(_bf16(dy)) @ w2q
+    far = lambda got, want: np.max(np.abs(got - want)) > 1e-6 * np.abs(want).max()
+    # dW13 from the unquantised rows
+    ar, br = _bf16(a), _bf16(b)
+    dab = np.concatenate([dh * br * B.silu_grad(ar), dh * B.silu(ar)], axis=1)
+    assert far(dab.T @ x, g13) and not far(dab.T @ xq, g13)
+    # the SwiGLU backward at the fp64 pre-activations
+    dab64 = np.concatenate([dh * b * B.silu_grad(a), dh * B.silu(a)], axis=1)
+    assert far(dab64.T @ xq, g13)
+    # [da | db] quantised from fp32 instead of bf16
+    assert far(_q_tiles(dab) @ w13q, gx) and not far(_q_tiles(_bf16(dab)) @ w13q, gx)
+
+
+def test_round_bf16_matches_torch_and_hand_cases():
+    """round_bf16 against torch's bf16 cast (an independent routine) over
+    normal, subnormal and tie values, and hand-worked ties: 1 + 2^-8 sits
+    halfway between 1 and 1 + 2^-7 and goes to the even 1; 1 + 3*2^-8 sits
+    halfway between 1 + 2^-7 and 1 + 2^-6 and goes to the even 1 + 2^-6."""
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.standard_normal(20000) * np.exp2(rng.integers(-140, 120, 20000)),
+                        (1 + rng.integers(0, 2 ** 16, 4000) * 2.0 ** -16) * np.exp2(rng.integers(-130, 100, 4000)),
+                        (rng.integers(0, 2 ** 8, 4000) * 2 + 1) * 2.0 ** -8])
+    x = x.astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(x).float().to(torch.bfloat16).double().numpy()
+    assert np.array_equal(B.round_bf16(x), want)
+    assert B.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert B.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    assert B.round_bf16(np.array([-(1 + 3 * 2.0 ** -8)]))[0] == -(1 + 2.0 ** -6)
+    assert B.round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -20]))[0] == 1 + 2.0 ** -7
