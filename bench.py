@@ -214,10 +214,10 @@ def main():
     roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) / 1e9 if tr and tr["digest"] == digest else None
     roof["traffic_unit"] = "GB per launch"
     roof["kernel_digest"] = digest
-    roof["kernel"] = ("moe_expert_gemm call: k_ffn_w8a16 phase A (gate/up + SwiGLU) + phase B (down), "
-                      "each on two halves of the tile map (phase B of the first half on a side stream)"
+    roof["kernel"] = ("moe_expert_gemm call: k_ffn_w8a16 phase A (gate/up + SwiGLU), then phase B (down), "
+                      "each launched on the two halves of the tile map"
                       if cfg.weights == "e4m3" and not cfg.x_fp8 else
-                      "moe_expert_gemm call: k_zero_counters + k_ffn_persistent phase A (gate/up + SwiGLU) + phase B (down)")
+                      "moe_expert_gemm call: k_ffn_schedule + k_ffn_persistent phase A (gate/up + SwiGLU) + phase B (down)")
     roof["units_per_launch"] = {"rows": rows, "flops": gemm_flops, "algorithmic_bytes": gemm_bytes}
     roof["avg_launch_ms"] = gemm_ms
 

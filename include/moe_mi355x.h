@@ -22,17 +22,12 @@
  * ---------------------------------------
  *  - Pointers named as device pointers must point to device memory (HBM) of
  *    the current HIP device; the caller owns every buffer.  The library
- *    allocates and frees no memory and keeps no pointer after a call
- *    returns.
+ *    allocates and frees no memory, keeps no pointer after a call returns
+ *    and holds no state between calls (no stream, event, lock or cache of
+ *    its own).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call
  *    enqueues its kernels on it and returns without synchronising; calls on
- *    distinct streams may run concurrently from different threads.  One
- *    exception: moe_expert_gemm on the (BF16, E4M3) path forks half of its
- *    down-projection kernels onto a side stream of the library's own (one
- *    per device, created with two events on first use and kept until the
- *    process ends) and joins it back into `stream` with an event before it
- *    returns, so to the caller all its work is still ordered on `stream`
- *    (a mutex serialises the fork between threads).
+ *    distinct streams may run concurrently from different threads.
  *  - Tensors are row-major and contiguous, element offsets are 64-bit.
  *    Data tensors (u, centroids, x, weights, y, out, q and the workspaces)
  *    must be 16-byte aligned (hipMalloc and torch allocations are 256-byte
@@ -58,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Limits of this implementation. */
 #define MOE_MAX_EXPERTS 1024   /* routed + shared experts */
@@ -168,7 +163,6 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, in
  *   w2          device [Nr+Ns, d, I]: W_down
  *   w2_scale    device [Nr+Ns, d/128, I/128] fp32 for MOE_E4M3, else NULL
  *   seg_offset, row_token, tile_map, n_tiles: from moe_permute
- *   tiles_max   capacity of tile_map (moe_permute_tiles_max)
  *   ws          device workspace, moe_gemm_workspace_bytes(...) bytes: holds
  *               the hidden state h of every row
  *   y, y_t      device [P_max, d] out, MOE_F32 or MOE_BF16
@@ -252,6 +246,23 @@ moe_status moe_bias_update(const int32_t* expert_load, int Nr, long long total_a
  * ---------------------------------------------------------------------- */
 moe_status fp8_quantize_tiles(const void* x, moe_dtype x_t, long long rows, long long cols,
                               int tile_rows, int tile_cols, uint8_t* q, float* scale, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_dequantize_tiles: the values that E4M3 tiles stand for ([RG-FP8]
+ * tiles), out[r, c] = decode(q[r, c]) * scale[r / tile_rows, c / 128]: the
+ * operand an E4M3 product multiplies.  With power-of-two scales (as
+ * fp8_quantize_tiles writes them) every value is exact in fp32, and in bf16
+ * for scales >= 2^-124.  The E4M3 training step uses it for Q(u), the input
+ * its gate/up weight gradient takes (straight-through quantisers).
+ *
+ *   q          device [rows, cols] uint8 E4M3 codes
+ *   scale      device [rows/tile_rows, cols/128] fp32
+ *   tile_rows  1 or 128; tile_cols 128 (as fp8_quantize_tiles)
+ *   out, out_t device [rows, cols] out, MOE_F32 or MOE_BF16
+ *   Errors: MOE_EINVAL for NULL pointers, bad sizes or tile shapes, out_t.
+ * ---------------------------------------------------------------------- */
+moe_status fp8_dequantize_tiles(const uint8_t* q, const float* scale, long long rows, long long cols,
+                                int tile_rows, int tile_cols, void* out, moe_dtype out_t, void* stream);
 
 /* ========================================================================
  * Backward pass (bf16 activations and weights).  The pages print no
@@ -370,7 +381,11 @@ moe_status moe_expert_gemm_backward(const void* x, const void* w13, const void* 
  *   dh = Q(dy) Q(W2),  dx = Q([da | db]) Q(W13)
  * The weight gradients are those of moe_expert_gemm_backward (bf16 dy,
  * [da | db], h, x): their K axis is the token axis, for which the pages give
- * no tiling.
+ * no tiling.  x is the expert input as the forward multiplied it: the bf16
+ * u after a bf16 forward; after the E4M3 forward (moe_expert_gemm_train_w8)
+ * Q(u) decoded by fp8_dequantize_tiles, so that dW13 = [da | db]^T Q(u) is
+ * the gradient through a straight-through quantiser.  Codes of dy and
+ * [da | db] are decided from their bf16 values.
  *   w13, w13_scale device E4M3 [Nr+Ns, 2I, d] with fp32 [Nr+Ns, 2I/128,
  *                  d/128] block scales, w2, w2_scale [Nr+Ns, d, I] with
  *                  [Nr+Ns, d/128, I/128] (as fp8_quantize_tiles writes them

@@ -44,6 +44,7 @@ SIGNATURES = {
     "moe_combine": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _u, _vp, _i, _vp]),
     "moe_bias_update": (_i, [_vp, _i, _ll, _f, _vp, _vp]),
     "fp8_quantize_tiles": (_i, [_vp, _i, _ll, _ll, _i, _i, _vp, _vp, _vp]),
+    "fp8_dequantize_tiles": (_i, [_vp, _vp, _ll, _ll, _i, _i, _vp, _i, _vp]),
     "moe_gemm_train_workspace_bytes": (_sz, [_i] * 7),
     "moe_expert_gemm_train": (_i, [_vp] * 3 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
     "moe_combine_backward": (_i, [_vp, _i, _vp, _i] + [_vp] * 4 + [_i] * 5 + [_vp] * 5),
@@ -262,6 +263,15 @@ def fp8_quantize_tiles(x, tile_rows, q, scale, tile_cols=128, stream=None):
                                     _stream(stream)))
 
 
+def fp8_dequantize_tiles(q, scale, tile_rows, out, tile_cols=128, stream=None):
+    """Values of E4M3 tiles (code x tile scale) into out (fp32 or bf16), q
+    viewed as [numel / last dim, last dim]."""
+    cols = q.shape[-1]
+    rows = q.numel() // cols if cols else 0
+    _check(lib().fp8_dequantize_tiles(_ptr(q), _ptr(scale), rows, cols, tile_rows, tile_cols, _ptr(out),
+                                      dtype_code(out), _stream(stream)))
+
+
 # ------------------------------------------------------- layer plumbing --
 @dataclass
 class ExpertWeights:
@@ -356,6 +366,9 @@ class MoeLayer:
             # dgrad_weights: E4M3 copies of the weights (quantize_weights); the
             # backward then runs its input-gradient products on E4M3 operands
             self.dgrad_w = dgrad_weights
+            # the E4M3 step's gate/up weight gradient takes Q(u), the operand
+            # its forward multiplied (straight-through quantisers)
+            self.xdq = torch.empty((T, d), **bf16) if self.train_fp8 else None
             if dgrad_weights is not None and dgrad_weights.w_t != MOE_E4M3:
                 raise ValueError("dgrad_weights must be E4M3 weights")
             ws_fn = moe_gemm_backward_workspace_bytes if dgrad_weights is None else moe_gemm_backward_w8_workspace_bytes
@@ -418,7 +431,11 @@ class MoeLayer:
                                      self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map,
                                      self.n_tiles, self.bwd_ws, self.dx, self.dw13, self.dw2, stream)
         else:
-            moe_expert_gemm_backward_w8(u, self.dgrad_w, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns,
+            x = u
+            if self.train_fp8:
+                fp8_dequantize_tiles(self.xq, self.xs, 1, self.xdq, stream=stream)
+                x = self.xdq
+            moe_expert_gemm_backward_w8(x, self.dgrad_w, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns,
                                         self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map,
                                         self.n_tiles, self.bwd_ws, self.dx, self.dw13, self.dw2, stream)
         moe_route_backward(grad_out, self.dx, u, centroids, self.topk_idx, self.inv_row, self.dz, self.dz_row,

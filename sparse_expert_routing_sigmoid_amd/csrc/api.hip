@@ -23,6 +23,8 @@ moe_status bias_update(const int32_t* expert_load, int Nr, long long total_assig
                        void* stream);
 moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long long cols, int tile_rows, int tile_cols,
                           uint8_t* q, float* scale, void* stream);
+moe_status dequantize_tiles(const uint8_t* q, const float* scale, long long rows, long long cols, int tile_rows,
+                            int tile_cols, void* out, moe_dtype out_t, void* stream);
 size_t gemm_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m, moe_dtype x_t, moe_dtype w_t);
 moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_dtype w_t, const void* w13,
                        const float* w13_scale, const void* w2, const float* w2_scale, int T, int K, int Nr, int Ns,
@@ -156,6 +158,12 @@ moe_status fp8_quantize_tiles(const void* x, moe_dtype x_t, long long rows, long
                               int tile_cols, uint8_t* q, float* scale, void* stream) {
   moe::clear_error();
   return moe::quantize_tiles(x, x_t, rows, cols, tile_rows, tile_cols, q, scale, stream);
+}
+
+moe_status fp8_dequantize_tiles(const uint8_t* q, const float* scale, long long rows, long long cols, int tile_rows,
+                                int tile_cols, void* out, moe_dtype out_t, void* stream) {
+  moe::clear_error();
+  return moe::dequantize_tiles(q, scale, rows, cols, tile_rows, tile_cols, out, out_t, stream);
 }
 
 size_t moe_gemm_train_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {

@@ -257,6 +257,42 @@ __global__ __launch_bounds__(256) void k_quant_128x128(const XT* __restrict__ x,
   if (tid == 0) scale[blockIdx.x] = sc;
 }
 
+// Codes x tile scale back to values: 8 consecutive codes of one row per
+// thread (they share a scale: 128 % 8 == 0).  e4m3_to_f32(code) * 2^k is
+// exact in fp32, and in bf16 too when 2^k >= 2^-124 (the smallest code step,
+// 2^-9 * 2^k, is then a bf16 subnormal step or coarser).
+__device__ __forceinline__ void store8v(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8v(uint16_t* p, const float (&v)[8]) {
+  uint4 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]);
+  w.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = w;
+}
+
+template <typename OT>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, const float* __restrict__ scale,
+                                                 long long rows, long long cols, int tile_rows,
+                                                 OT* __restrict__ out) {
+  const long long chunks = rows * (cols / 8);
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= chunks) return;
+  const long long r = i / (cols / 8), c = (i % (cols / 8)) * 8;
+  const float sc = scale[(r / tile_rows) * (cols / 128) + c / 128];
+  const uint2 w = *reinterpret_cast<const uint2*>(q + r * cols + c);
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = e4m3_to_f32((w.x >> (8 * j)) & 0xFFu) * sc;
+    v[4 + j] = e4m3_to_f32((w.y >> (8 * j)) & 0xFFu) * sc;
+  }
+  store8v(out + r * cols + c, v);
+}
+
 }  // namespace
 
 moe_status combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_t, const int32_t* inv_row,
@@ -331,6 +367,29 @@ moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long lon
                          cols, q, scale);
   }
   return launch_status("fp8_quantize_tiles");
+}
+
+moe_status dequantize_tiles(const uint8_t* q, const float* scale, long long rows, long long cols, int tile_rows,
+                            int tile_cols, void* out, moe_dtype out_t, void* stream) {
+  MOE_REQUIRE(out_t == MOE_F32 || out_t == MOE_BF16, MOE_EINVAL, "out_t must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(tile_cols == 128 && (tile_rows == 1 || tile_rows == 128), MOE_EINVAL,
+              "tiles must be 1x128 or 128x128");
+  MOE_REQUIRE(rows >= 0 && cols >= 0 && cols % 128 == 0 && rows % tile_rows == 0, MOE_EINVAL,
+              "rows/cols must be multiples of the tile");
+  MOE_REQUIRE(rows == 0 || cols == 0 || (q && scale && out), MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(aligned16(q) && aligned16(out), MOE_EINVAL, "q and out must be 16-byte aligned");
+  const long long chunks = rows * (cols / 8);
+  if (chunks == 0) return MOE_OK;
+  MOE_REQUIRE(chunks < (1LL << 31) * 256, MOE_EINVAL, "too many values");
+  hipStream_t st = as_stream(stream);
+  dim3 grid((unsigned)ceil_div(chunks, 256));
+  if (out_t == MOE_F32)
+    hipLaunchKernelGGL(k_dequant<float>, grid, dim3(256), 0, st, q, scale, rows, cols, tile_rows,
+                       static_cast<float*>(out));
+  else
+    hipLaunchKernelGGL(k_dequant<uint16_t>, grid, dim3(256), 0, st, q, scale, rows, cols, tile_rows,
+                       static_cast<uint16_t*>(out));
+  return launch_status("fp8_dequantize_tiles");
 }
 
 }  // namespace moe

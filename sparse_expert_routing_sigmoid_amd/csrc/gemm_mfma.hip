@@ -643,17 +643,14 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
   }
 }
 
+// One block per CU, a multiple of 8 so every XCD gets the same count (the
+// CU count is queried on every call: no state is kept between calls).
 int persistent_blocks() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cached[dev]) {
-    hipDeviceProp_t p;
-    int cus = 256;
-    if (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0) cus = p.multiProcessorCount;
-    cached[dev] = (cus / 8) * 8 > 0 ? (cus / 8) * 8 : 8;
-  }
-  return cached[dev];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return (cus / 8) * 8 > 0 ? (cus / 8) * 8 : 8;
 }
 
 }  // namespace

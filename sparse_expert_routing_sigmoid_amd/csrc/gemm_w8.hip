@@ -30,8 +30,6 @@
 // runs per step, issued back to back.
 #include "common.h"
 
-#include <mutex>
-
 namespace moe {
 
 namespace {
@@ -186,14 +184,14 @@ __device__ __forceinline__ void w8_pass(const W8Lanes& L, const int32_t* __restr
 //          [E, 2 Nd, Kd], out = h [P, Nd] bf16 with SwiGLU; Nd = I, Kd = d.
 // !PHASE_A: x = h [P, Kd] bf16, w = W2 codes [E, Nd, Kd], out = y [P, Nd].
 // w_scale: [E, rows of w / 128, Kd / 128] powers of two.
+// The items of one launch part are run by `nblocks` blocks; this block is
+// number `block` of them.
 template <bool PHASE_A, typename OT>
-__global__ __launch_bounds__(W8_THREADS) void k_ffn_w8a16(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
-                                                          const float* __restrict__ w_scale,
-                                                          const int32_t* __restrict__ row_token,
-                                                          const int32_t* __restrict__ tile_map,
-                                                          const int32_t* __restrict__ n_tiles, int Kd, int Nd,
-                                                          uint32_t x_bytes, int part, int parts,
-                                                          OT* __restrict__ out) {
+__device__ __forceinline__ void w8_items(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                         const float* __restrict__ w_scale, const int32_t* __restrict__ row_token,
+                                         const int32_t* __restrict__ tile_map, const int32_t* __restrict__ n_tiles,
+                                         int Kd, int Nd, uint32_t x_bytes, int part, int parts,
+                                         OT* __restrict__ out, int block, int nblocks) {
   constexpr int NCOL = PHASE_A ? 128 : 256;  // output columns per item
   const int NT = Nd / NCOL;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -205,7 +203,7 @@ __global__ __launch_bounds__(W8_THREADS) void k_ffn_w8a16(const uint16_t* __rest
   const int t_lo = (int)((long long)all_tiles * part / parts), t_hi = (int)((long long)all_tiles * (part + 1) / parts);
   const int tiles = t_hi - t_lo;
   const long long total = (long long)tiles * NT;
-  for (long long item = blockIdx.x; item < total; item += gridDim.x) {
+  for (long long item = block; item < total; item += nblocks) {
     // shared-expert tiles (at the end of the tile map, the largest) go first
     const int tile = t_hi - 1 - (int)(item / NT);
     const int n = (int)(item % NT);
@@ -251,59 +249,42 @@ __global__ __launch_bounds__(W8_THREADS) void k_ffn_w8a16(const uint16_t* __rest
   }
 }
 
+template <bool PHASE_A, typename OT>
+__global__ __launch_bounds__(W8_THREADS) void k_ffn_w8a16(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
+                                                          const float* __restrict__ w_scale,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ tile_map,
+                                                          const int32_t* __restrict__ n_tiles, int Kd, int Nd,
+                                                          uint32_t x_bytes, int part, int parts,
+                                                          OT* __restrict__ out) {
+  w8_items<PHASE_A, OT>(x, w, w_scale, row_token, tile_map, n_tiles, Kd, Nd, x_bytes, part, parts, out, blockIdx.x,
+                        gridDim.x);
+}
+
 int w8_grid(long long items) {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cached[dev]) {
-    hipDeviceProp_t p;
-    int cus = 256;
-    if (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0) cus = p.multiProcessorCount;
-    cached[dev] = cus * 8;  // enough blocks for several resident waves per SIMD
-  }
-  return (int)(items < cached[dev] ? (items > 0 ? items : 1) : cached[dev]);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const long long cap = (long long)cus * 8;  // enough blocks for several resident waves per SIMD
+  return (int)(items < cap ? (items > 0 ? items : 1) : cap);
 }
 
 }  // namespace
 
 bool ffn_w8a16_ok(int d, int I) { return d % 256 == 0 && I % 256 == 0 && d / 128 <= 64 && I / 128 <= 64; }
 
-// Side stream and events of the split launch, one set per device, created
-// on first use and kept for the life of the process.  Measured on the
-// 128-token decode step: 1.97 -> 1.92 ms per call (two halves; four
-// quarters were slower, 1.96).
-struct W8Fork {
-  hipStream_t side = nullptr;
-  hipEvent_t a_done = nullptr, b_done = nullptr;
-  bool ok = false;
-};
-
-W8Fork* w8_fork() {
-  static W8Fork forks[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  W8Fork& f = forks[dev];
-  if (!f.ok) {
-    if (hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&f.a_done, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&f.b_done, hipEventDisableTiming) != hipSuccess)
-      return nullptr;
-    f.ok = true;
-  }
-  return &f;
-}
-
 // x [T, d] bf16; W13 / W2 E4M3 codes with 128x128 block scales; h (workspace)
 // [P, I] bf16; y [P, d] bf16 or fp32.  tiles_max bounds the tile map.
 //
-// The tiles are split in two halves, A = gate/up, B = down:
-//   stream st:   A(half 0) -> A(half 1) -> B(half 1) -> wait B(half 0)
-//   side stream: wait A(half 0) -> B(half 0)
-// so B(half 0) runs while A(half 1) streams its weights, and each kernel's
-// tail (its last blocks, when most CUs are idle) overlaps the next one.
-// The halves share nothing but h rows of different tiles; the events order
-// every read of h after its writes.  Without a side stream (creation
-// failed) the four launches run in order on st.
+// Four launches on the caller's stream: gate/up of tile halves 0 and 1, then
+// down of halves 0 and 1.  Each half's grid is sized for its own items, so
+// the tail of one launch (its last blocks, when most CUs are idle) is
+// shorter than one launch over all tiles would leave.  Measured on the
+// 128-token decode step: 1.90 ms per call, the same as running the down
+// projection of half 0 on a second stream beside the gate/up of half 1
+// (1.91-1.92 ms), and 2.09 ms when those two run as the two roles of one
+// grid.
 void launch_ffn_w8a16(const uint16_t* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
                       const float* w2_scale, const int32_t* row_token, const int32_t* tile_map,
                       const int32_t* n_tiles, int tiles_max, int T, long long P, int d, int I, uint16_t* h, void* y,
@@ -312,31 +293,16 @@ void launch_ffn_w8a16(const uint16_t* x, const uint8_t* w13, const float* w13_sc
   const uint32_t h_bytes = (uint32_t)(P * I * 2);
   const int half = (tiles_max + 1) / 2;
   const int gA = w8_grid((long long)half * (I / 128)), gB = w8_grid((long long)half * (d / 256));
-  auto launchA = [&](int part, hipStream_t s) {
-    hipLaunchKernelGGL((k_ffn_w8a16<true, uint16_t>), dim3(gA), dim3(W8_THREADS), 0, s, x, w13, w13_scale,
+  for (int part = 0; part < 2; ++part)
+    hipLaunchKernelGGL((k_ffn_w8a16<true, uint16_t>), dim3(gA), dim3(W8_THREADS), 0, st, x, w13, w13_scale,
                        row_token, tile_map, n_tiles, d, I, x_bytes, part, 2, h);
-  };
-  auto launchB = [&](int part, hipStream_t s) {
+  for (int part = 0; part < 2; ++part) {
     if (y_f32)
-      hipLaunchKernelGGL((k_ffn_w8a16<false, float>), dim3(gB), dim3(W8_THREADS), 0, s, h, w2, w2_scale,
-                         row_token, tile_map, n_tiles, I, d, h_bytes, part, 2, static_cast<float*>(y));
+      hipLaunchKernelGGL((k_ffn_w8a16<false, float>), dim3(gB), dim3(W8_THREADS), 0, st, h, w2, w2_scale, row_token,
+                         tile_map, n_tiles, I, d, h_bytes, part, 2, static_cast<float*>(y));
     else
-      hipLaunchKernelGGL((k_ffn_w8a16<false, uint16_t>), dim3(gB), dim3(W8_THREADS), 0, s, h, w2, w2_scale,
+      hipLaunchKernelGGL((k_ffn_w8a16<false, uint16_t>), dim3(gB), dim3(W8_THREADS), 0, st, h, w2, w2_scale,
                          row_token, tile_map, n_tiles, I, d, h_bytes, part, 2, static_cast<uint16_t*>(y));
-  };
-  static std::mutex fork_mutex;  // one call at a time records and waits on the shared events
-  std::lock_guard<std::mutex> lock(fork_mutex);
-  W8Fork* f = w8_fork();
-  launchA(0, st);
-  if (f && hipEventRecord(f->a_done, st) == hipSuccess && hipStreamWaitEvent(f->side, f->a_done, 0) == hipSuccess) {
-    launchB(0, f->side);
-    launchA(1, st);
-    launchB(1, st);
-    if (hipEventRecord(f->b_done, f->side) == hipSuccess) (void)hipStreamWaitEvent(st, f->b_done, 0);
-  } else {
-    launchA(1, st);
-    launchB(0, st);
-    launchB(1, st);
   }
 }
 

@@ -241,14 +241,12 @@ moe_status launch_router_mfma(const uint16_t* u, const uint16_t* e3, int T, int 
                               hipStream_t st) {
   dim3 grid((T + TT - 1) / TT, ks);
   const size_t lds = 2 * (size_t)(TT + RM_BROWS) * RM_ROW;
-  static bool attr_set = false;  // raising the dynamic LDS limit is idempotent
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_router_logits_mfma<TT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-      set_error("moe_route: cannot raise the LDS limit of the router kernel");
-      return MOE_EHIP;
-    }
-    attr_set = true;
+  // The dynamic LDS limit is raised on every call (for the current device;
+  // idempotent and cheap), so the library keeps no per-process state for it.
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_router_logits_mfma<TT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+    set_error("moe_route: cannot raise the LDS limit of the router kernel");
+    return MOE_EHIP;
   }
   hipLaunchKernelGGL(k_router_logits_mfma<TT>, grid, dim3(256), lds, st, u, e3, T, d, Nr, d / ks, z);
   return MOE_OK;

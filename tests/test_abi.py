@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = M.lib()
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert L.moe_status_str(0) == b"MOE_OK"
     assert L.moe_status_str(3) == b"MOE_EWORKSPACE"
 
@@ -128,6 +128,10 @@ def test_combine_bias_quant_reject_bad_arguments():
     assert L.fp8_quantize_tiles(FAKE, M.MOE_BF16, 100, 128, 128, 128, FAKE, FAKE, None) == M.MOE_EINVAL
     assert L.fp8_quantize_tiles(FAKE, M.MOE_BF16, 4, 128, 2, 128, FAKE, FAKE, None) == M.MOE_EINVAL
     assert L.fp8_quantize_tiles(FAKE, M.MOE_E4M3, 4, 128, 1, 128, FAKE, FAKE, None) == M.MOE_EINVAL
+    assert L.fp8_dequantize_tiles(FAKE, FAKE, 4, 100, 1, 128, FAKE, M.MOE_BF16, None) == M.MOE_EINVAL
+    assert L.fp8_dequantize_tiles(FAKE, FAKE, 100, 128, 128, 128, FAKE, M.MOE_BF16, None) == M.MOE_EINVAL
+    assert L.fp8_dequantize_tiles(FAKE, FAKE, 4, 128, 1, 128, FAKE, M.MOE_E4M3, None) == M.MOE_EINVAL
+    assert L.fp8_dequantize_tiles(None, FAKE, 4, 128, 1, 128, FAKE, M.MOE_F32, None) == M.MOE_EINVAL
 
 
 def test_python_binding_raises_with_message():

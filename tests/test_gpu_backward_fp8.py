@@ -2,12 +2,14 @@
 (moe_expert_gemm_backward_w8, MoeLayer(dgrad_weights=...)) against the fp64
 oracle's layer_backward(fp8_dgrad=True) on the same seeded inputs.
 
-The oracle quantises the same bf16 weights in 128x128 blocks and its fp64
-activation gradients in 1x128 tiles; the GPU quantises its bf16 activation
-gradients, so a tile's scale can differ where its amax sits at a power-of-two
-boundary.  Tolerances: relative L2 <= 3e-2 (the FP8 bound) for what flows
-through the E4M3 products (du, dW13), 1e-2 for the paths that do not (dW2,
-gate and score gradients, de)."""
+The oracle quantises the same bf16 weights in 128x128 blocks and, like the
+GPU, decides the 1x128 codes of the activation gradients from their bf16
+values (dy, then [da | db] computed at the bf16 pre-activations), so the two
+sides quantise the same values up to fp32 accumulation order.  Tolerances:
+relative L2 <= 5e-3 for what flows through the E4M3 products of the
+backward (du, its expert part and dW13: the E4M3 bound of 3e-2 would only
+apply if the codes were decided from different values), 1e-2 for the
+paths that do not (dW2, gate and score gradients, de)."""
 import numpy as np
 import pytest
 import torch
@@ -20,7 +22,7 @@ from oracle import moe as O
 
 pytestmark = pytest.mark.gpu
 
-TOL8, TOL = 3e-2, 1e-2
+TOL8, TOL, MIRROR = 3e-2, 1e-2, 5e-3
 BASE = W.CONFIGS["mid_bf16"]
 CASES = {
     "small": BASE.with_(T=256, d=512, Nr=16, Ns=1, I=256, K=4),
@@ -63,7 +65,7 @@ def test_fp8_dgrad_backward_matches_oracle(name):
             "dgate": rel_l2(f64_of(layer.dgate), gr.dgate), "dz": rel_l2(f64_of(layer.dz), gr.dz)}
     print(errs8, errs, flush=True)
     for k, v in errs8.items():
-        assert v <= TOL8, (k, v)
+        assert v <= MIRROR, (k, v)
     for k, v in errs.items():
         assert v <= TOL, (k, v)
     # the E4M3 products do differ from the exact ones
@@ -138,7 +140,9 @@ def test_fp8_training_step_matches_oracle(name):
             "dz": rel_l2(f64_of(layer.dz), gr.dz)}
     print(errs, flush=True)
     for k, v in errs.items():
-        assert v <= TOL8, (k, v)
+        # du and dW13 pass through the E4M3 input-gradient products; dW2, de,
+        # dgate and dz through none of the backward's
+        assert v <= (MIRROR if k in ("du", "du_ffn", "dw13") else TOL), (k, v)
 
 
 def test_fp8_dgrad_experts_without_rows_and_no_tokens():

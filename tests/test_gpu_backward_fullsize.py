@@ -9,9 +9,11 @@ can compute exactly:
   token's K selected experts (K of K selected, the same gates) and the
   shared expert, which gives the full-layer du, gate and score gradients of
   that token;
-- the weight gradients of sampled routed experts: dW13_i and dW2_i depend
-  only on the rows of expert i, so the oracle's FFN backward on those rows
-  (dy = g * dL/dh') gives them exactly.
+- the weight gradients of the least loaded, a median and the most loaded
+  routed expert, and of every shared expert (every token, the longest
+  fp32 sums): dW13_i and dW2_i depend only on the rows of expert i, so the
+  oracle's FFN backward on those rows (dy = g * dL/dh', or dL/dh' for a
+  shared expert) gives them exactly.
 Tokens at a routing near-tie are not sampled, nor experts that hold one.
 """
 import numpy as np
@@ -91,15 +93,19 @@ def test_expert_weight_gradients_at_full_size(run):
     clean = [i for i in range(cfg.Nr) if load[i] > 0 and not any(t in run["tied"]
                                                                  for t in np.nonzero(np.any(r.idx == i, axis=1))[0])]
     by_load = sorted(clean, key=lambda i: load[i])
-    picks = [by_load[0], by_load[len(by_load) // 2]]
+    picks = [by_load[0], by_load[len(by_load) // 2], by_load[-1]] + list(range(cfg.Nr, cfg.Nr + cfg.Ns))
     for i in picks:
-        ts, ks = np.nonzero(r.idx == i)
         w13_i, w2_i = run["weights"](i)
-        dy = r.gate[ts, ks][:, None] * run["G"][ts]
+        if i < cfg.Nr:
+            ts, ks = np.nonzero(r.idx == i)
+            dy = r.gate[ts, ks][:, None] * run["G"][ts]
+        else:   # shared expert: every token, gate 1
+            ts = np.arange(cfg.T)
+            dy = run["G"]
         _, dw13, dw2, _ = OB.ffn_backward(run["u"][ts], w13_i, w2_i, dy)
         e13 = rel_l2(f64_of(layer.dw13[i]), dw13)
         e2 = rel_l2(f64_of(layer.dw2[i]), dw2)
-        print(f"expert {i} ({load[i]} rows): dW13 rel L2 {e13:.2e}, dW2 {e2:.2e}", flush=True)
+        print(f"expert {i} ({len(ts)} rows): dW13 rel L2 {e13:.2e}, dW2 {e2:.2e}", flush=True)
         assert e13 <= TOL and e2 <= TOL
     idle = np.nonzero(np_of(layer.expert_load) == 0)[0]
     for i in idle[:4]:

@@ -90,3 +90,38 @@ def test_weight_blocks_of_an_expert_tensor():
         assert np.array_equal(np_of(ew.w13[e]), qo) and np.array_equal(np_of(ew.w13_scale[e]), so)
         qo, so = e4m3.quantize_tiles(w2[e].cpu().numpy(), 128, 128)
         assert np.array_equal(np_of(ew.w2[e]), qo) and np.array_equal(np_of(ew.w2_scale[e]), so)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("tile_rows", [1, 128])
+def test_dequantize_is_code_times_scale(out_dtype, tile_rows):
+    """fp8_dequantize_tiles: each of the 254 finite codes, under scales
+    from 2^-100 to 2^40, gives exactly the oracle's decoded value (exact in
+    bf16 for these scales)."""
+    rows, cols = 256, 640
+    rng = np.random.default_rng(30 + tile_rows)
+    codes = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E                 # no NaN patterns
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    codes[0, :finite.size] = finite                      # every finite code once
+    nsc = (rows // tile_rows, cols // 128)
+    scales = np.exp2(rng.integers(-100, 41, size=nsc)).astype(np.float32)
+    q, s = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    out = torch.empty((rows, cols), dtype=out_dtype, device="cuda")
+    M.fp8_dequantize_tiles(q, s, tile_rows, out)
+    torch.cuda.synchronize()
+    want = e4m3.dequantize_tiles(codes, scales, tile_rows, 128)
+    assert np.array_equal(out.to("cpu", torch.float64).numpy(), want)
+
+
+def test_dequantize_round_trip_of_activations():
+    """Quantise then dequantise on the GPU: the oracle's quantised u."""
+    from oracle import moe as O
+    x = W.make_free((64, 1024), 1.0, 33, "cuda", torch.bfloat16)
+    q = torch.empty((64, 1024), dtype=torch.uint8, device="cuda")
+    s = torch.empty((64, 8), dtype=torch.float32, device="cuda")
+    out = torch.empty((64, 1024), dtype=torch.bfloat16, device="cuda")
+    M.fp8_quantize_tiles(x, 1, q, s)
+    M.fp8_dequantize_tiles(q, s, 1, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.to("cpu", torch.float64).numpy(), O.quantize_activations(x.to("cpu", torch.float64).numpy()))
