@@ -24,7 +24,8 @@
  *    the current HIP device; the caller owns every buffer.  The library
  *    allocates and frees no memory, keeps no pointer after a call returns
  *    and holds no state between calls (no stream, event, lock or cache of
- *    its own).
+ *    its own), except moe_permute_noalloc's device array and its address
+ *    per GPU.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call
  *    enqueues its kernels on it and returns without synchronising; calls on
  *    distinct streams may run concurrently from different threads.
@@ -145,6 +146,28 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, in
                        int32_t* seg_offset, int32_t* row_token, int32_t* inv_row,
                        int32_t* tile_map, int32_t* n_tiles,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute_noalloc: moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  It allocates nothing:
+ * the same kernels use a 4 MiB device array of the library's own (one copy
+ * per GPU, held until the process ends; its address is looked up once per
+ * device on the first call made with that device current).  Results are
+ * those of moe_permute, bit for bit.
+ *   Arguments, layouts and errors as moe_permute, without ws / ws_bytes;
+ *   MOE_EWORKSPACE when the sizes need more than the array holds:
+ *   moe_permute_workspace_bytes(T, K, Nr, Ns) must not exceed
+ *   moe_permute_noalloc_scratch_bytes() (4 MiB: e.g. T up to 1048576 tokens
+ *   with Nr = 256, T up to 262144 with Nr = 1024).
+ *   Every call on one GPU uses that GPU's array: calls that overlap in time
+ *   on one GPU (different streams or threads) race and must be serialised
+ *   by the caller.
+ * ---------------------------------------------------------------------- */
+size_t moe_permute_noalloc_scratch_bytes(void);
+moe_status moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int Nr, int Ns, int tile_m,
+                               int32_t* seg_offset, int32_t* row_token, int32_t* inv_row,
+                               int32_t* tile_map, int32_t* n_tiles, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_expert_gemm: every expert's SwiGLU FFN on its rows of the layout.

@@ -38,6 +38,8 @@ SIGNATURES = {
     "moe_permute_tiles_max": (_sz, [_i, _i, _i, _i, _i]),
     "moe_permute_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "moe_permute": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_permute_noalloc_scratch_bytes": (_sz, []),
+    "moe_permute_noalloc": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_gemm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "moe_expert_gemm": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                              _vp, _vp, _vp, _vp, _vp, _sz, _vp, _i, _vp]),
@@ -164,6 +166,13 @@ def moe_permute(topk_idx, Nr, Ns, tile_m, seg_offset, row_token, inv_row, tile_m
     _check(lib().moe_permute(_ptr(topk_idx), T, K, Nr, Ns, tile_m, _ptr(seg_offset), _ptr(row_token),
                              _ptr(inv_row), _ptr(tile_map), _ptr(n_tiles), _ptr(ws),
                              ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def moe_permute_noalloc(topk_idx, Nr, Ns, tile_m, seg_offset, row_token, inv_row, tile_map, n_tiles, stream=None):
+    """moe_permute with the library's own scratch array: allocates nothing."""
+    T, K = topk_idx.shape
+    _check(lib().moe_permute_noalloc(_ptr(topk_idx), T, K, Nr, Ns, tile_m, _ptr(seg_offset), _ptr(row_token),
+                                     _ptr(inv_row), _ptr(tile_map), _ptr(n_tiles), _stream(stream)))
 
 
 def moe_expert_gemm(x, x_scale, w_t, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns, d, I, tile_m,

@@ -16,6 +16,9 @@ size_t permute_workspace_bytes(int T, int K, int Nr, int Ns);
 moe_status permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, int tile_m, int32_t* seg_offset,
                    int32_t* row_token, int32_t* inv_row, int32_t* tile_map, int32_t* n_tiles, void* ws,
                    size_t ws_bytes, void* stream);
+size_t permute_noalloc_scratch_bytes();
+moe_status permute_noalloc(const int32_t* topk_idx, int T, int K, int Nr, int Ns, int tile_m, int32_t* seg_offset,
+                           int32_t* row_token, int32_t* inv_row, int32_t* tile_map, int32_t* n_tiles, void* stream);
 moe_status combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_t, const int32_t* inv_row,
                    const float* topk_gate, const int32_t* seg_offset, int T, int d, int K, int Nr, int Ns,
                    unsigned flags, void* out, moe_dtype out_t, void* stream);
@@ -124,6 +127,16 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, in
   moe::clear_error();
   return moe::permute(topk_idx, T, K, Nr, Ns, tile_m, seg_offset, row_token, inv_row, tile_map, n_tiles, ws, ws_bytes,
                       stream);
+}
+
+size_t moe_permute_noalloc_scratch_bytes(void) { return moe::permute_noalloc_scratch_bytes(); }
+
+moe_status moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int Nr, int Ns, int tile_m, int32_t* seg_offset,
+                               int32_t* row_token, int32_t* inv_row, int32_t* tile_map, int32_t* n_tiles,
+                               void* stream) {
+  moe::clear_error();
+  return moe::permute_noalloc(topk_idx, T, K, Nr, Ns, tile_m, seg_offset, row_token, inv_row, tile_map, n_tiles,
+                              stream);
 }
 
 size_t moe_gemm_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m, moe_dtype x_t,

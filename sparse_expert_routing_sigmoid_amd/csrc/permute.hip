@@ -18,6 +18,8 @@
 //                   that chose the same expert), then the row of (t, k).
 #include "common.h"
 
+#include <mutex>
+
 namespace moe {
 
 namespace {
@@ -182,6 +184,52 @@ moe_status permute(const int32_t* topk_idx, int T, int K, int Nr, int Ns, int ti
   hipLaunchKernelGGL(k_perm_scatter, dim3(sblk), dim3(PB_TOK), (size_t)PB_WAVES * Nr * sizeof(unsigned long long), st,
                      topk_idx, T, K, Nr, Ns, counts, seg_offset, row_token, inv_row, P_max);
   return launch_status("moe_permute");
+}
+
+// ------------------------------------------------- no-allocation variant --
+// moe_permute_noalloc runs the same kernels with their workspace (per-block
+// expert counts) in a device array of the library's own instead of a
+// caller's buffer, for callers that cannot allocate.  Every word the kernels
+// read there is written earlier in the same call, so nothing is cleared.
+// Each GPU holds its own copy of the array until the process ends; its
+// address on a device is looked up once, with that device current, and kept.
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(4) << 20;  // 4 MiB per GPU
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+std::once_flag g_scratch_once[NOALLOC_MAX_DEVICES];
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+hipError_t g_scratch_err[NOALLOC_MAX_DEVICES];
+
+}  // namespace
+
+size_t permute_noalloc_scratch_bytes() { return NOALLOC_SCRATCH_BYTES; }
+
+moe_status permute_noalloc(const int32_t* topk_idx, int T, int K, int Nr, int Ns, int tile_m, int32_t* seg_offset,
+                           int32_t* row_token, int32_t* inv_row, int32_t* tile_map, int32_t* n_tiles, void* stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    set_error("moe_permute_noalloc: no current HIP device");
+    return MOE_EHIP;
+  }
+  MOE_REQUIRE(dev < NOALLOC_MAX_DEVICES, MOE_EUNSUPPORTED, "device index beyond the library's limit");
+  MOE_REQUIRE(T >= 0 && Nr >= 1 && Ns >= 0, MOE_EINVAL, "sizes out of range");
+  MOE_REQUIRE(permute_workspace_bytes(T, K, Nr, Ns) <= NOALLOC_SCRATCH_BYTES, MOE_EWORKSPACE,
+              "sizes need more than the 4 MiB of built-in scratch: (ceil(T/256)*Nr + Nr + Ns + 64) * 4 bytes; use "
+              "moe_permute with a caller workspace");
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) {
+    set_error(std::string("moe_permute_noalloc: hipGetSymbolAddress of the scratch array: ") +
+              hipGetErrorString(g_scratch_err[dev]));
+    return MOE_EHIP;
+  }
+  return permute(topk_idx, T, K, Nr, Ns, tile_m, seg_offset, row_token, inv_row, tile_map, n_tiles,
+                 g_scratch_ptr[dev], NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // namespace moe
