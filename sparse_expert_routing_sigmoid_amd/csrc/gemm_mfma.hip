@@ -19,18 +19,21 @@
 // its XCD's list through an atomic counter, then helps the other XCDs.
 // Results do not depend on which block runs an item.
 //
-// Block tile: 256 rows x 256 weight rows x 128 bytes of K (64 bf16 or 128
-// E4M3 values: one scale block), 256 threads = 4 waves in a 2 x 2 grid, each
-// wave 128 x 128 as up to 4 x 4 MFMA 32x32 tiles (bf16: 32x32x16; E4M3:
-// the block-scaled 32x32x64, whose per-lane E8M0 scales carry the power-of-two
-// tile and block scales, so scaling is exact and costs no extra work) with
-// fp32 accumulators.  Operands go global -> LDS with the direct 16-byte LDS
-// load of buffer instructions (no register staging), two stages, XOR-swizzled
+// Block tile: 256 rows x 256 weight rows x 128 bytes of K per stage (64 bf16
+// or 128 E4M3 values: one scale block), 256 threads = 4 waves in a 2 x 2
+// grid, each wave 128 x 128 as up to 4 x 4 MFMA 32x32 tiles (bf16: 32x32x16;
+// E4M3: the block-scaled 32x32x64, whose per-lane E8M0 scales carry the
+// power-of-two tile and block scales, so scaling is exact and costs no extra
+// work) with fp32 accumulators.  Operands go global -> LDS with the direct
+// 16-byte LDS load of buffer instructions (no register staging), XOR-swizzled
 // 16-byte chunks so MFMA fragment reads (32 rows, one K chunk) spread over
-// the banks.  Rows past the tile's row count are loaded as zeros (out-of-range
-// buffer loads fetch nothing) and 32-row MFMA tiles with no live row are not
-// multiplied: each wave runs a variant compiled for its number of live tiles
-// (MT), so no accumulator is ever conditionally updated.
+// the banks.  bf16: two A stages and three B stages, B loaded two stages
+// ahead (deep_body); E4M3: two stages of A + its row scales and B (the row
+// scales leave no room for a third B stage).  Rows past the tile's row count
+// are loaded as zeros (out-of-range buffer loads fetch nothing) and 32-row
+// MFMA tiles with no live row are not multiplied: each wave runs a variant
+// compiled for its number of live tiles (MT), so no accumulator is ever
+// conditionally updated.
 #include "common.h"
 
 namespace moe {
@@ -110,21 +113,6 @@ __device__ __forceinline__ void issue_part(const Item& it, uint8_t* __restrict__
   }
 }
 
-template <int MT>
-__device__ __forceinline__ void load_frags_bf16(bf16x8_v (&af)[4], bf16x8_v (&bf)[4], const uint8_t* __restrict__ src,
-                                                const Item& it, int kk) {
-  const uint8_t* sb = src + P_TM * P_ROWB;
-  const int c = kk * 2 + (it.lane >> 5);
-  const int cofs = ((c ^ it.lsw) << 4);
-  const int lr = it.lane & 31;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    bf[j] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(sb + (it.brow[j] + lr) * P_ROWB + cofs));
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-    af[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(src + (it.mrow0 + i * 32 + lr) * P_ROWB + cofs));
-}
-
 // E4M3 fragments: 32 bytes per lane (two 16-byte chunks of K step kk).  A and
 // B use the same byte layout, and every scale is constant over the 64 K values
 // of one MFMA, so the hardware's K order inside a lane does not matter.
@@ -149,83 +137,168 @@ __device__ __forceinline__ void load_frags_fp8(i32x8_v (&af)[4], i32x8_v (&bf)[4
   for (int i = 0; i < MT; ++i) af[i] = frag32(src + (it.mrow0 + i * 32 + lr) * P_ROWB, c0, it.lsw);
 }
 
-// One k-step: a share of the next slab's loads, the fragments of the next
-// k-step, the MFMAs of this one.  Fragments are double-buffered by hand and
-// a scheduling barrier closes each k-step.  The stage pointers are
-// restrict-qualified so the compiler knows the loads into one stage never
-// alias the fragment reads of the other and does not wait for those loads
-// before the MFMAs.
-template <bool FP8, int MT, int KK, typename FragT>
-__device__ __forceinline__ void kstep(f32x16_v (&acc)[MT > 0 ? MT : 1][4], FragT (&af)[2][4], FragT (&bf)[2][4],
-                                      const int (&sa)[4], const int (&sbs)[4], const Item& it,
-                                      uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, bool load_next,
-                                      uint32_t next_kb) {
-  constexpr int KS = Fmt<FP8>::KSTEPS;
-  issue_part<FP8, KK, KS>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
-  if constexpr (MT > 0) {
-    if (KK + 1 < KS) {
-      if constexpr (FP8)
-        load_frags_fp8<MT>(af[(KK + 1) & 1], bf[(KK + 1) & 1], src, it, KK + 1);
-      else
-        load_frags_bf16<MT>(af[(KK + 1) & 1], bf[(KK + 1) & 1], src, it, KK + 1);
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (FP8)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[KK & 1][i], bf[KK & 1][j], acc[i][j], 0, 0,
-                                                                      0, sa[i], 0, sbs[j]);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[KK & 1][i], bf[KK & 1][j], acc[i][j], 0, 0, 0);
-      }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
+// One stage of the E4M3 K loop (two k-steps of the block-scaled 32x32x64
+// MFMA): half of the next slab's loads and the MFMAs of each k-step.
 template <bool FP8, int MT>
 __device__ __forceinline__ void pipe_step(f32x16_v (&acc)[MT > 0 ? MT : 1][4], const Item& it,
                                           uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int s,
                                           bool load_next, uint32_t next_kb) {
-  if constexpr (FP8) {
-    // 32-byte E4M3 fragments are not double-buffered (register budget); an
-    // FP8 k-step is long enough (16 MFMAs of 64 K) to cover the LDS reads.
-    int sa[4] = {127, 127, 127, 127}, sbs[4] = {127, 127, 127, 127};
-    if constexpr (MT > 0) {
-      const float* scl = reinterpret_cast<const float*>(src + P_OPS);
+  static_assert(FP8, "the bf16 kernels use the deep K loop");
+  // 32-byte E4M3 fragments are not double-buffered (register budget); an
+  // FP8 k-step is long enough (16 MFMAs of 64 K) to cover the LDS reads.
+  int sa[4] = {127, 127, 127, 127}, sbs[4] = {127, 127, 127, 127};
+  if constexpr (MT > 0) {
+    const float* scl = reinterpret_cast<const float*>(src + P_OPS);
 #pragma unroll
-      for (int i = 0; i < MT; ++i) sa[i] = e8m0_of(scl[it.mrow0 + i * 32 + (it.lane & 31)]);
-      const int b0 = e8m0_of(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_uint(it.bsc0), s)));
-      const int b1 = e8m0_of(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_uint(it.bsc1), s)));
-      sbs[0] = b0; sbs[1] = b0; sbs[2] = b1; sbs[3] = b1;
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (kk == 0)
-        issue_part<true, 0, 2>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
-      else
-        issue_part<true, 1, 2>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
-      if constexpr (MT > 0) {
-        i32x8_v af[4], bf[4];
-        load_frags_fp8<MT>(af, bf, src, it, kk);
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0,
-                                                                        sbs[j]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else {
-    bf16x8_v af[2][4], bf[2][4];
-    const int sa[4] = {0, 0, 0, 0}, sbs[4] = {0, 0, 0, 0};
-    if constexpr (MT > 0) load_frags_bf16<MT>(af[0], bf[0], src, it, 0);
-    kstep<false, MT, 0>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
-    kstep<false, MT, 1>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
-    kstep<false, MT, 2>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
-    kstep<false, MT, 3>(acc, af, bf, sa, sbs, it, dst, src, load_next, next_kb);
+    for (int i = 0; i < MT; ++i) sa[i] = e8m0_of(scl[it.mrow0 + i * 32 + (it.lane & 31)]);
+    const int b0 = e8m0_of(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_uint(it.bsc0), s)));
+    const int b1 = e8m0_of(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_uint(it.bsc1), s)));
+    sbs[0] = b0; sbs[1] = b0; sbs[2] = b1; sbs[3] = b1;
   }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    if (kk == 0)
+      issue_part<true, 0, 2>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
+    else
+      issue_part<true, 1, 2>(it, dst, next_kb, load_next ? 0u : 0x80000000u);
+    if constexpr (MT > 0) {
+      i32x8_v af[4], bf[4];
+      load_frags_fp8<MT>(af, bf, src, it, kk);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0,
+                                                                      sbs[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ------------------------------------------------------------------------
+// bf16 K loop with three weight stages.  LDS holds two 32 KB stages of the
+// activation tile (A) and three 32 KB stages of the weight tile (B): 160 KB.
+// B is loaded two stages ahead and A one (deep_body), so the weight stream
+// keeps 64 KB per CU in flight instead of 32 KB: a block is bound by its
+// weight stream whenever its tile has few rows, and that rate is the bytes
+// in flight over the memory latency.  Loads complete in issue order, so the
+// wait before a stage's barrier names how many of the latest loads may still
+// be outstanding (the B loads of two stages ahead).  Measured on the
+// 8192-token prefill layer (expert GEMM call, identical outputs): 8.31 ms
+// with the two-stage loop, 7.69 with three B stages, 7.44 with the next
+// k-step's fragment reads interleaved one per MFMA, 7.21 with the barrier
+// moved before the last k-step.
+constexpr int D_AB = P_TM * P_ROWB;   // 32 KB: one stage of A or of B
+constexpr int D_LDS = 5 * D_AB;       // A0 A1 B0 B1 B2
+
+// Blocks [J0, J1) of the wave's 8 1 KB blocks of the A (or B) K slab at
+// byte kb into dst.  oob as in issue_part.
+template <int J0, int J1>
+__device__ __forceinline__ void issue_a(const Item& it, uint8_t* __restrict__ dst, uint32_t kb, uint32_t oob) {
+#pragma unroll
+  for (int j = J0; j < J1; ++j) dma16(it.ra, dst + (it.wave * 8 + j) * 1024, it.a_off[j] | oob, kb);
+}
+template <int J0, int J1>
+__device__ __forceinline__ void issue_b(const Item& it, uint8_t* __restrict__ dst, uint32_t kb, uint32_t oob) {
+#pragma unroll
+  for (int j = J0; j < J1; ++j) dma16(it.rb, dst + (it.wave * 8 + j) * 1024, it.b_off[j] | oob, kb);
+}
+
+template <int MT>
+__device__ __forceinline__ void frags_ab(bf16x8_v (&af)[4], bf16x8_v (&bf)[4], const uint8_t* __restrict__ a_src,
+                                         const uint8_t* __restrict__ b_src, const Item& it, int kk) {
+  const int c = kk * 2 + (it.lane >> 5);
+  const int cofs = ((c ^ it.lsw) << 4);
+  const int lr = it.lane & 31;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bf[j] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(b_src + (it.brow[j] + lr) * P_ROWB + cofs));
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+    af[i] = __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const uint4*>(a_src + (it.mrow0 + i * 32 + lr) * P_ROWB + cofs));
+}
+
+template <int MT>
+__device__ __forceinline__ void mma_step(f32x16_v (&acc)[MT > 0 ? MT : 1][4], const bf16x8_v (&af)[4],
+                                         const bf16x8_v (&bf)[4]) {
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+// s_waitcnt with vmcnt(8), expcnt and lgkmcnt left at their maxima (no wait).
+constexpr unsigned WAIT_VM8 = (8u & 0xFu) | (0x7u << 4) | (0xFu << 8) | ((8u >> 4) << 14);
+// vmcnt(8) and lgkmcnt(0); vmcnt(16) and lgkmcnt(0).
+constexpr unsigned WAIT_VM8_LGKM0 = (8u & 0xFu) | (0x7u << 4) | ((8u >> 4) << 14);
+constexpr unsigned WAIT_VM16_LGKM0 = (16u & 0xFu) | (0x7u << 4) | ((16u >> 4) << 14);
+
+// Issue order inside a k-step: MFMA q, then LDS read q (the next k-step's
+// fragments) and global load q, so the LDS serves the reads and the
+// direct-to-LDS writes while the matrix pipe is busy.
+template <int NMFMA, int NDS, int NVM>
+__device__ __forceinline__ void order_kstep() {
+  constexpr int N = NMFMA > NDS ? (NMFMA > NVM ? NMFMA : NVM) : (NDS > NVM ? NDS : NVM);
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    if (q < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (q < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (q < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
+// One stage s of the bf16 K loop.  On entry the fragments of k-step 0 are
+// being read, A(s + 1) has been issued and B(s + 1) is in flight or landed.
+//   k-step 0: MFMAs of k 0, fragments of k 1, B(s + 2) blocks 0-3 -> b_dst
+//   k-step 1: MFMAs of k 1, fragments of k 2, B(s + 2) blocks 4-7
+//   k-step 2: MFMAs of k 2, fragments of k 3
+//   wait for this wave's LDS reads and for everything but B(s + 2), then the
+//   barrier: A(s + 1) and B(s + 1) have landed for every wave, and no wave
+//   reads A(s) or B(s) any more
+//   k-step 3: MFMAs of k 3, fragments of k-step 0 of stage s + 1 (a_nxt,
+//   b_nxt), A(s + 2) into the A(s) buffer (a_cur)
+// So the reads that start a stage run under the last MFMAs of the one
+// before, and B is loaded two stages ahead, A one.  The buffers named by
+// different restrict pointers are distinct; A(s + 2) goes through a_cur
+// itself, after the barrier.
+template <int MT>
+__device__ __forceinline__ void deep_body(f32x16_v (&acc)[MT > 0 ? MT : 1][4], bf16x8_v (&af)[2][4],
+                                          bf16x8_v (&bf)[2][4], const Item& it, uint8_t* __restrict__ a_cur,
+                                          const uint8_t* __restrict__ b_cur, const uint8_t* __restrict__ a_nxt,
+                                          const uint8_t* __restrict__ b_nxt, uint8_t* __restrict__ b_dst,
+                                          uint32_t b_kb, uint32_t b_oob, uint32_t a_kb, uint32_t a_oob) {
+  constexpr int NM = 4 * MT, ND = MT > 0 ? MT + 4 : 0;
+  issue_b<0, 4>(it, b_dst, b_kb, b_oob);
+  if constexpr (MT > 0) {
+    frags_ab<MT>(af[1], bf[1], a_cur, b_cur, it, 1);
+    mma_step<MT>(acc, af[0], bf[0]);
+  }
+  order_kstep<NM, ND, 4>();
+  __builtin_amdgcn_sched_barrier(0);
+  issue_b<4, 8>(it, b_dst, b_kb, b_oob);
+  if constexpr (MT > 0) {
+    frags_ab<MT>(af[0], bf[0], a_cur, b_cur, it, 2);
+    mma_step<MT>(acc, af[1], bf[1]);
+  }
+  order_kstep<NM, ND, 4>();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MT > 0) {
+    frags_ab<MT>(af[1], bf[1], a_cur, b_cur, it, 3);
+    mma_step<MT>(acc, af[0], bf[0]);
+  }
+  order_kstep<NM, ND, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(WAIT_VM8_LGKM0);  // own LDS reads done; A(s + 1), B(s + 1) landed
+  __builtin_amdgcn_s_barrier();               // ... for every wave
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a<0, 8>(it, a_cur, a_kb, a_oob);
+  if constexpr (MT > 0) {
+    frags_ab<MT>(af[0], bf[0], a_nxt, b_nxt, it, 0);
+    mma_step<MT>(acc, af[1], bf[1]);
+  }
+  order_kstep<NM, ND, 8>();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ void store8(uint16_t* p, float4 a, float4 b) {
@@ -383,6 +456,75 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
                                                       n);
 }
 
+// run_tile of the bf16 kernels: the K loop of deep_body (two A stages,
+// three B stages, rotated each stage), then the epilogue.  lds = D_LDS
+// bytes; the epilogue stages its rows through the first 128 KB.
+template <bool PHASE_A, int MT, typename OT, bool KEEP>
+__device__ __forceinline__ void run_tile_deep(const Item& it, uint8_t* lds, int wm, int wn, int tid,
+                                              OT* __restrict__ out, uint16_t* __restrict__ ab, int Nd, int n) {
+  constexpr int MA = MT > 0 ? MT : 1;
+  f32x16_v acc[MA][4];
+#pragma unroll
+  for (int i = 0; i < MA; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  uint8_t* a0 = lds;
+  uint8_t* a1 = lds + D_AB;
+  uint8_t* b0 = lds + 2 * D_AB;
+  uint8_t* b1 = lds + 3 * D_AB;
+  uint8_t* b2 = lds + 4 * D_AB;
+  const uint32_t OOB = 0x80000000u;
+  // prologue: A(0), B(0), then B(1), A(1) (all buffers are free); wait for
+  // the first two, read the fragments of stage 0, k-step 0
+  issue_a<0, 8>(it, a0, 0, 0u);
+  issue_b<0, 8>(it, b0, 0, 0u);
+  issue_b<0, 8>(it, b1, P_ROWB, it.nk > 1 ? 0u : OOB);
+  issue_a<0, 8>(it, a1, P_ROWB, it.nk > 1 ? 0u : OOB);
+  __builtin_amdgcn_s_waitcnt(WAIT_VM16_LGKM0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8_v af[2][4], bf[2][4];
+  if constexpr (MT > 0) frags_ab<MT>(af[0], bf[0], a0, b0, it, 0);
+  for (int s = 0; s < it.nk; ++s) {
+    deep_body<MT>(acc, af, bf, it, a0, b0, a1, b1, b2, (uint32_t)(s + 2) * P_ROWB, s + 2 < it.nk ? 0u : OOB,
+                  (uint32_t)(s + 2) * P_ROWB, s + 2 < it.nk ? 0u : OOB);
+    uint8_t* t = a0; a0 = a1; a1 = t;
+    t = b0; b0 = b1; b1 = b2; b2 = t;
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // the last zero loads land before LDS is reused
+  epilogue<PHASE_A, false, MT, MA, OT, KEEP>(acc, it, lds, lds + 2 * D_AB, wm, wn, tid, out, nullptr, ab, nullptr,
+                                             Nd, n);
+}
+
+// ------------------------------------------------------------------------
+// LDS of the kernel.  E4M3: two stages of A + row scales and B as separate
+// arrays (the compiler then knows they never overlap), and the item word.
+// bf16: the D_LDS bytes of the deep K loop; the item word sits in the second
+// A stage, which is first written by loads issued after the stage-0
+// barrier, when every wave has read it.
+template <bool FP8>
+struct KernelLds;
+template <>
+struct KernelLds<true> {
+  __attribute__((aligned(1024))) uint8_t st0[Fmt<true>::STAGE];
+  __attribute__((aligned(1024))) uint8_t st1[Fmt<true>::STAGE];
+  int item_word;
+  __device__ uint8_t* base() { return st0; }
+  __device__ uint8_t* stage0() { return st0; }
+  __device__ uint8_t* stage1() { return st1; }
+  __device__ int* item() { return &item_word; }
+};
+template <>
+struct KernelLds<false> {
+  __attribute__((aligned(1024))) uint8_t lds[D_LDS];
+  __device__ uint8_t* base() { return lds; }
+  __device__ uint8_t* stage0() { return lds; }
+  __device__ uint8_t* stage1() { return lds + 2 * D_AB; }
+  __device__ int* item() { return reinterpret_cast<int*>(lds + D_AB); }
+};
+
 // PHASE_A: x = tokens [T, Kd] gathered by row_token, w = W13 [E, 2*Nd, Kd],
 //          out = h [P, Nd] with SwiGLU; Nd = I, Kd = d.
 // !PHASE_A: x = h [P, Kd], w = W2 [E, Nd, Kd], out = y [P, Nd]; Nd = d, Kd = I.
@@ -408,9 +550,11 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
                                                             uint16_t* __restrict__ ab,
                                                             uint16_t* __restrict__ hb) {
   constexpr int EB = Fmt<FP8>::EB;
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[Fmt<FP8>::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[Fmt<FP8>::STAGE];
-  __shared__ int s_item;
+  __shared__ KernelLds<FP8> L;
+  uint8_t* lds = L.base();
+  uint8_t* st0 = L.stage0();
+  uint8_t* st1 = L.stage1();
+  int* s_item_p = L.item();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int xcd = blockIdx.x & 7;
@@ -419,7 +563,7 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
   const int kblocks = Kd * EB / P_ROWB;        // K blocks (stages) of a row
 
   for (;;) {
-    __syncthreads();  // previous item done with LDS and s_item
+    __syncthreads();  // previous item done with LDS and the item word
     if (tid == 0) {
       // this XCD's list first; when it is drained, help the other XCDs
       int got = -1;
@@ -430,10 +574,10 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
         const int i = atomicAdd(&counters[y], 1);
         if (i < tot) got = items[offsets[y] + i];
       }
-      s_item = got;
+      *s_item_p = got;
     }
     __syncthreads();
-    const int entry = s_item;
+    const int entry = *s_item_p;
     if (entry < 0) break;
     const int tile = entry >> 8;
     const int n = entry & 255;
@@ -490,12 +634,22 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
     it.mrow0 = wm * 128;
     int mt_live = (it.rows - it.mrow0 + 31) >> 5;  // 32-row MFMA tiles of this wave that hold rows
     mt_live = __builtin_amdgcn_readfirstlane(mt_live < 0 ? 0 : (mt_live > 4 ? 4 : mt_live));
-    switch (mt_live) {
-      case 4: run_tile<FP8, PHASE_A, 4, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-      case 3: run_tile<FP8, PHASE_A, 3, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-      case 2: run_tile<FP8, PHASE_A, 2, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-      case 1: run_tile<FP8, PHASE_A, 1, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-      default: run_tile<FP8, PHASE_A, 0, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+    if constexpr (FP8) {
+      switch (mt_live) {
+        case 4: run_tile<FP8, PHASE_A, 4, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 3: run_tile<FP8, PHASE_A, 3, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 2: run_tile<FP8, PHASE_A, 2, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 1: run_tile<FP8, PHASE_A, 1, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        default: run_tile<FP8, PHASE_A, 0, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+      }
+    } else {
+      switch (mt_live) {
+        case 4: run_tile_deep<PHASE_A, 4, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 3: run_tile_deep<PHASE_A, 3, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 2: run_tile_deep<PHASE_A, 2, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 1: run_tile_deep<PHASE_A, 1, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        default: run_tile_deep<PHASE_A, 0, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+      }
     }
   }
 }
@@ -514,6 +668,8 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
 // items per XCD, [32, 40) / [40, 48) first item of each XCD, then the item
 // lists of phase A (cap * ntA) and B (cap * ntB).
 constexpr int SCHED_HDR = 64;
+constexpr int SCHED_A_MODE = 1;
+constexpr int SCHED_SMALL = 128;
 constexpr int SCHED_MAXU = 4096;
 
 __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict__ tile_map,
@@ -597,9 +753,44 @@ __global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict
       const int v = s_order[r];
       const int len = s_ustart[v + 1] - s_ustart[v];
       s_uxcd[v] = (unsigned char)x;
-      s_uoffA[v] = nA;
       nA += len * ntA;
       s_xlist[x * stride + m++] = v;
+    }
+    {
+      // phase A order (SCHED_A_MODE): 0 largest first; 1 alternately from
+      // both ends; 2 units of at most SCHED_SMALL rows merged into the
+      // larger ones so that their items stay evenly spread over the list
+      int oA = 0;
+      if (SCHED_A_MODE == 0) {
+        for (int k = 0; k < m; ++k) {
+          const int v = s_xlist[x * stride + k];
+          s_uoffA[v] = oA;
+          oA += (s_ustart[v + 1] - s_ustart[v]) * ntA;
+        }
+      } else if (SCHED_A_MODE == 1) {
+        for (int k = 0; k < m; ++k) {
+          const int v = s_xlist[x * stride + ((k & 1) ? m - 1 - (k >> 1) : (k >> 1))];
+          s_uoffA[v] = oA;
+          oA += (s_ustart[v + 1] - s_ustart[v]) * ntA;
+        }
+      } else {
+        int ks = m;
+        while (ks > 0 && s_urows[s_xlist[x * stride + ks - 1]] <= SCHED_SMALL) --ks;
+        long long TL = 0, TS = 0, cL = 0, cS = 0;
+        for (int k = 0; k < m; ++k) {
+          const long long it = s_ustart[s_xlist[x * stride + k] + 1] - s_ustart[s_xlist[x * stride + k]];
+          if (k < ks) TL += it; else TS += it;
+        }
+        int i = 0, j = ks;
+        while (i < ks || j < m) {
+          const bool small = j < m && (i >= ks || cS * TL < cL * TS);
+          const int v = s_xlist[x * stride + (small ? j++ : i++)];
+          const int len = s_ustart[v + 1] - s_ustart[v];
+          s_uoffA[v] = oA;
+          oA += len * ntA;
+          if (small) cS += len; else cL += len;
+        }
+      }
     }
     int nB = 0;
     for (int k = 0; k < m; ++k) {
