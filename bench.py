@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--dgrad-fp8", action="store_true",
                    help="with --train: the backward's input-gradient products on E4M3 operands "
                         "(moe_expert_gemm_backward_w8; E4M3 weights prepared once at set-up)")
+    p.add_argument("--fused-combine", action="store_true",
+                   help="the expert GEMMs with the combine fused into the down projection (fp32 atomics, "
+                        "moe_expert_gemm_combine) instead of moe_expert_gemm + moe_combine")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (calibrates HBM byte counters) and exit")
     return p.parse_args()
@@ -143,7 +146,7 @@ def main():
     else:
         weights = M.ExpertWeights(M.MOE_F32 if cfg.weights == "f32" else M.MOE_BF16, w13, w2)
     layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, W.TORCH_DTYPE[cfg.act], weights,
-                       x_fp8=cfg.x_fp8, tile_m=args.tile_m, device=dev)
+                       x_fp8=cfg.x_fp8, tile_m=args.tile_m, device=dev, fused_combine=args.fused_combine)
     torch.cuda.synchronize()
 
     bias = bias0.clone()
@@ -161,11 +164,15 @@ def main():
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
             ev0.record(stream)
-        layer.experts(u)
+        if args.fused_combine:
+            layer.experts_combine(u)
+        else:
+            layer.experts(u)
         if timed:
             ev1.record(stream)
             gemm_events.append((ev0, ev1))
-        layer.combine(u)
+        if not args.fused_combine:
+            layer.combine(u)
         layer.update_bias(bias, cfg.gamma)
         if timed:
             sv1 = torch.cuda.Event(enable_timing=True)
@@ -210,13 +217,16 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": mfma_peak / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / mfma_peak}
     digest = gemm_source_digest(cfg.name)
-    tr = TRAFFIC.get(cfg.name)
+    tr = TRAFFIC.get(cfg.name + (":fused" if args.fused_combine else ""))
     roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) / 1e9 if tr and tr["digest"] == digest else None
     roof["traffic_unit"] = "GB per launch"
     roof["kernel_digest"] = digest
     roof["kernel"] = ("moe_expert_gemm call: k_ffn_w8a16 phase A (gate/up + SwiGLU), then phase B (down), "
                       "each launched on the two halves of the tile map"
                       if cfg.weights == "e4m3" and not cfg.x_fp8 else
+                      "moe_expert_gemm_combine call: k_fused_prep + k_ffn_schedule + k_ffn_persistent phase A "
+                      "(gate/up + SwiGLU) + phase B (down, combine fused: fp32 atomics into the layer output)"
+                      if args.fused_combine else
                       "moe_expert_gemm call: k_ffn_schedule + k_ffn_persistent phase A (gate/up + SwiGLU) + phase B (down)")
     roof["units_per_launch"] = {"rows": rows, "flops": gemm_flops, "algorithmic_bytes": gemm_bytes}
     roof["avg_launch_ms"] = gemm_ms
@@ -238,7 +248,9 @@ def main():
         "data": "synthetic (seeded; random-init expert weights and centroids of the V3 MoE-layer shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "Nr": cfg.Nr, "Ns": cfg.Ns, "I": cfg.I,
                    "K": cfg.K, "routing": cfg.routing, "weights": cfg.weights, "x_fp8": cfg.x_fp8,
-                   "tile_m": args.tile_m, "bias_update": "every step", "parallelism": "single GPU"},
+                   "tile_m": args.tile_m, "bias_update": "every step", "parallelism": "single GPU",
+                   "combine": "fused into the down projection (fp32 atomics)" if args.fused_combine else
+                   "moe_combine (deterministic)"},
         "layer": {"tflops": gemm_flops / layer_time / 1e12,
                   "mfma_frac": gemm_flops / layer_time / (PEAK["fp8"] if cfg.x_fp8 else PEAK["bf16"]),
                   "hbm_gbs": layer_bytes / layer_time / 1e9, "hbm_frac": layer_bytes / layer_time / PEAK["hbm"],

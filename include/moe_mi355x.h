@@ -235,6 +235,39 @@ moe_status moe_combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_
                        void* out, moe_dtype out_t, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_expert_gemm_combine: moe_expert_gemm and moe_combine in one call, the
+ * combine fused into the down projection ([RG-MoE] combine equation):
+ *   out[t] = u_t + sum_j y[shared_j(t)] + sum_k g[t,k] y[inv_row[t,k]]
+ * with every y row added to its token's row of out by fp32 atomic adds in
+ * the down projection's epilogue, so y is never written to memory (about
+ * 2 GB less traffic per 8192-token V3 prefill step than moe_expert_gemm +
+ * moe_combine).  The order of the adds is not fixed: results agree with
+ * moe_combine's to fp32 rounding of the sum and are not bitwise
+ * reproducible (use moe_combine for that).  y rows are summed unrounded
+ * (moe_combine reads them rounded to y_t).
+ *   Arguments as moe_expert_gemm (x, weights, layout, tile_m), plus
+ *   inv_row, topk_gate device [T, K] from moe_permute / moe_route
+ *   u, u_t       device [T, d] tokens, MOE_F32 or MOE_BF16 (the residual)
+ *   flags        MOE_COMBINE_* bits, as moe_combine
+ *   ws           device, moe_gemm_combine_workspace_bytes(...) bytes
+ *   out          device [T, d] fp32 out (overwritten; may not alias u)
+ *   Supported (x_t, w_t): (BF16, BF16) with d % 256 == 0 and I % 128 == 0;
+ *   (E4M3, E4M3) with d, I multiples of 256 up to 8192; else
+ *   MOE_EUNSUPPORTED.  Other errors as moe_expert_gemm and moe_combine.
+ * ---------------------------------------------------------------------- */
+size_t moe_gemm_combine_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                        moe_dtype x_t, moe_dtype w_t);
+moe_status moe_expert_gemm_combine(const void* x, moe_dtype x_t, const float* x_scale,
+                                   moe_dtype w_t, const void* w13, const float* w13_scale,
+                                   const void* w2, const float* w2_scale,
+                                   int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                   const int32_t* seg_offset, const int32_t* row_token,
+                                   const int32_t* tile_map, const int32_t* n_tiles,
+                                   const int32_t* inv_row, const float* topk_gate,
+                                   const void* u, moe_dtype u_t, unsigned flags,
+                                   void* ws, size_t ws_bytes, float* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_bias_update: end-of-step bias rule ([RG-MoE] bias rule).  The pages do
  * not define "overloaded"; this library compares the load with the mean
  * load T*K/Nr exactly in integers: Nr*c_i > T*K -> b_i -= gamma,

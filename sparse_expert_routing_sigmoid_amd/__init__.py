@@ -43,6 +43,9 @@ SIGNATURES = {
     "moe_gemm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "moe_expert_gemm": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                              _vp, _vp, _vp, _vp, _vp, _sz, _vp, _i, _vp]),
+    "moe_gemm_combine_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "moe_expert_gemm_combine": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _vp] + [_i] * 7 + [_vp] * 6 +
+                                [_vp, _i, _u, _vp, _sz, _vp, _vp]),
     "moe_combine": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _u, _vp, _i, _vp]),
     "moe_bias_update": (_i, [_vp, _i, _ll, _f, _vp, _vp]),
     "fp8_quantize_tiles": (_i, [_vp, _i, _ll, _ll, _i, _i, _vp, _vp, _vp]),
@@ -185,6 +188,23 @@ def moe_expert_gemm(x, x_scale, w_t, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns,
                                  _ptr(y), dtype_code(y), _stream(stream)))
 
 
+def moe_gemm_combine_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t):
+    return lib().moe_gemm_combine_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t)
+
+
+def moe_expert_gemm_combine(x, x_scale, w_t, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns, d, I, tile_m, seg_offset,
+                            row_token, tile_map, n_tiles, inv_row, topk_gate, u, ws, out, flags=0, x_t=None,
+                            stream=None):
+    """Expert GEMMs with the combine fused into the down projection (fp32
+    atomics; not bitwise reproducible); out [T, d] fp32."""
+    x_t = dtype_code(x) if x_t is None else x_t
+    _check(lib().moe_expert_gemm_combine(_ptr(x), x_t, _ptr(x_scale), w_t, _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                         _ptr(w2_scale), T, K, Nr, Ns, d, I, tile_m, _ptr(seg_offset),
+                                         _ptr(row_token), _ptr(tile_map), _ptr(n_tiles), _ptr(inv_row),
+                                         _ptr(topk_gate), _ptr(u), dtype_code(u), flags, _ptr(ws), _nbytes(ws),
+                                         _ptr(out), _stream(stream)))
+
+
 def moe_expert_gemm_train(x, w13, w2, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token, tile_map, n_tiles,
                           ws, h, ab, y, stream=None):
     _check(lib().moe_expert_gemm_train(_ptr(x), _ptr(w13), _ptr(w2), T, K, Nr, Ns, d, I, tile_m, _ptr(seg_offset),
@@ -316,7 +336,8 @@ class MoeLayer:
     synchronisation happens inside forward()."""
 
     def __init__(self, T, d, Nr, Ns, I, K, act_dtype, weights: ExpertWeights, x_fp8=False,
-                 tile_m=32, out_dtype=None, device="cuda", train=False, grad_dtype=None, dgrad_weights=None):
+                 tile_m=32, out_dtype=None, device="cuda", train=False, grad_dtype=None, dgrad_weights=None,
+                 fused_combine=False):
         self.T, self.d, self.Nr, self.Ns, self.I, self.K = T, d, Nr, Ns, I, K
         self.tile_m, self.x_fp8, self.w = tile_m, x_fp8, weights
         dev = torch.device(device)
@@ -345,8 +366,16 @@ class MoeLayer:
                                                                   weights.w_t), 1),),
                                    dtype=torch.uint8, device=dev)
         out_dtype = act_dtype if out_dtype is None else out_dtype
-        self.y = torch.empty((P, d), dtype=out_dtype, device=dev)
-        self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
+        self.fused = fused_combine
+        if fused_combine:
+            # moe_expert_gemm_combine: no y rows; the output is fp32
+            self.fc_ws = torch.empty((max(moe_gemm_combine_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, self.x_t,
+                                                                           weights.w_t), 1),),
+                                     dtype=torch.uint8, device=dev)
+            self.out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        else:
+            self.y = torch.empty((P, d), dtype=out_dtype, device=dev)
+            self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
         self.train = train
         if train:
             # the training forward keeps h and the pre-activations [a | b]
@@ -421,9 +450,26 @@ class MoeLayer:
         moe_combine(u, self.y, self.inv_row, self.topk_gate, self.seg_offset, self.Nr, self.Ns, out, flags, stream)
         return out
 
+    def experts_combine(self, u, flags=0, stream=None):
+        """Expert GEMMs with the combine fused into the down projection
+        (moe_expert_gemm_combine); returns the fp32 layer output."""
+        w = self.w
+        if self.x_fp8:
+            fp8_quantize_tiles(u, 1, self.xq, self.xs, stream=stream)
+            x, xs = self.xq, self.xs
+        else:
+            x, xs = u, None
+        moe_expert_gemm_combine(x, xs, w.w_t, w.w13, w.w13_scale, w.w2, w.w2_scale, self.T, self.K, self.Nr, self.Ns,
+                                self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map,
+                                self.n_tiles, self.inv_row, self.topk_gate, u, self.fc_ws, self.out, flags,
+                                x_t=self.x_t, stream=stream)
+        return self.out
+
     def forward(self, u, centroids, bias, stream=None):
         self.route(u, centroids, bias, stream)
         self.permute(stream)
+        if self.fused:
+            return self.experts_combine(u, stream=stream)
         self.experts(u, stream)
         return self.combine(u, stream=stream)
 

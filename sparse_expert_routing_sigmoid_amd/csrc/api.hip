@@ -35,6 +35,14 @@ moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_d
                        const int32_t* tile_map, const int32_t* n_tiles, void* ws, size_t ws_bytes, void* y,
                        moe_dtype y_t, void* stream);
 
+size_t gemm_combine_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m, moe_dtype x_t,
+                                    moe_dtype w_t);
+moe_status expert_gemm_combine(const void* x, moe_dtype x_t, const float* x_scale, moe_dtype w_t, const void* w13,
+                               const float* w13_scale, const void* w2, const float* w2_scale, int T, int K, int Nr,
+                               int Ns, int d, int I, int tile_m, const int32_t* seg_offset, const int32_t* row_token,
+                               const int32_t* tile_map, const int32_t* n_tiles, const int32_t* inv_row,
+                               const float* topk_gate, const void* u, moe_dtype u_t, unsigned flags, void* ws,
+                               size_t ws_bytes, float* out, void* stream);
 size_t gemm_train_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
 moe_status expert_gemm_train(const void* x, const void* w13, const void* w2, int T, int K, int Nr, int Ns, int d,
                              int I, int tile_m, const int32_t* seg_offset, const int32_t* row_token,
@@ -152,6 +160,23 @@ moe_status moe_expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, m
   moe::clear_error();
   return moe::expert_gemm(x, x_t, x_scale, w_t, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns, d, I, tile_m, seg_offset,
                           row_token, tile_map, n_tiles, ws, ws_bytes, y, y_t, stream);
+}
+
+size_t moe_gemm_combine_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m, moe_dtype x_t,
+                                        moe_dtype w_t) {
+  return moe::gemm_combine_workspace_bytes(T, K, Nr, Ns, d, I, tile_m, x_t, w_t);
+}
+
+moe_status moe_expert_gemm_combine(const void* x, moe_dtype x_t, const float* x_scale, moe_dtype w_t, const void* w13,
+                                   const float* w13_scale, const void* w2, const float* w2_scale, int T, int K,
+                                   int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                   const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                   const int32_t* inv_row, const float* topk_gate, const void* u, moe_dtype u_t,
+                                   unsigned flags, void* ws, size_t ws_bytes, float* out, void* stream) {
+  moe::clear_error();
+  return moe::expert_gemm_combine(x, x_t, x_scale, w_t, w13, w13_scale, w2, w2_scale, T, K, Nr, Ns, d, I, tile_m,
+                                  seg_offset, row_token, tile_map, n_tiles, inv_row, topk_gate, u, u_t, flags, ws,
+                                  ws_bytes, out, stream);
 }
 
 moe_status moe_combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_t, const int32_t* inv_row,

@@ -29,7 +29,7 @@ int ffn_schedule_max_tiles();
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                                 const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                 int Nr, int cap, uint16_t* h, uint16_t* ab, void* y, bool y_f32, int* sched,
-                                hipStream_t st);
+                                hipStream_t st, const float* row_gate = nullptr);
 bool ffn_bwd_ok(int d, int I);
 bool ffn_bwd_w8_ok(int d, int I);
 bool ffn_fp8_persistent_ok(int d, int I);
@@ -37,7 +37,7 @@ void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uin
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                int Nr, int cap, uint8_t* h, float* h_scale, void* y, bool y_f32, int* sched,
-                               hipStream_t st, uint16_t* ab, uint16_t* hb);
+                               hipStream_t st, uint16_t* ab, uint16_t* hb, const float* row_gate = nullptr);
 void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
                        const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
                        const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,

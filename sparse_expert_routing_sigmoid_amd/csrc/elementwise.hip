@@ -160,6 +160,33 @@ void launch_combine(const void* u, const void* y, const int32_t* inv_row, const 
                      static_cast<OT*>(out));
 }
 
+// ------------------------------------------------------ fused combine --
+// Set-up of the fused combine (moe_expert_gemm_combine): out[t, :] = u[t, :]
+// widened to fp32 (0 without the residual), and the gate of every token row
+// of the layout: g[t, k] at row inv_row[t, k], 1 at the shared rows of t (0
+// for a dropped term).  One block per token; padding rows are never read.
+template <typename UT>
+__global__ __launch_bounds__(256) void k_fused_prep(const UT* __restrict__ u, const int32_t* __restrict__ inv_row,
+                                                    const float* __restrict__ gate,
+                                                    const int32_t* __restrict__ seg_offset, int d, int K, int Nr,
+                                                    int Ns, unsigned flags, float* __restrict__ out,
+                                                    float* __restrict__ row_gate) {
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const bool res = !(flags & MOE_COMBINE_NO_RESIDUAL), sh = !(flags & MOE_COMBINE_NO_SHARED),
+             ro = !(flags & MOE_COMBINE_NO_ROUTED);
+  for (int c = tid * 8; c < d; c += 256 * 8) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (res) Vec8<UT>::load(u + (long long)t * d + c, v);
+    Vec8<float>::store(out + (long long)t * d + c, v);
+  }
+  for (int q = tid; q < K + Ns; q += 256) {
+    if (q < K)
+      row_gate[inv_row[(long long)t * K + q]] = ro ? gate[(long long)t * K + q] : 0.f;
+    else
+      row_gate[(long long)seg_offset[Nr + q - K] + t] = sh ? 1.f : 0.f;
+  }
+}
+
 // ---------------------------------------------------------------- bias --
 __global__ void k_bias_update(const int32_t* __restrict__ load, int Nr, long long total, float gamma,
                               float* __restrict__ bias) {
@@ -390,6 +417,17 @@ moe_status dequantize_tiles(const uint8_t* q, const float* scale, long long rows
     hipLaunchKernelGGL(k_dequant<uint16_t>, grid, dim3(256), 0, st, q, scale, rows, cols, tile_rows,
                        static_cast<uint16_t*>(out));
   return launch_status("fp8_dequantize_tiles");
+}
+
+void launch_fused_combine_prep(const void* u, moe_dtype u_t, const int32_t* inv_row, const float* topk_gate,
+                               const int32_t* seg_offset, int T, int d, int K, int Nr, int Ns, unsigned flags,
+                               float* out, float* row_gate, hipStream_t st) {
+  if (u_t == MOE_BF16)
+    hipLaunchKernelGGL(k_fused_prep<uint16_t>, dim3(T), dim3(256), 0, st, static_cast<const uint16_t*>(u), inv_row,
+                       topk_gate, seg_offset, d, K, Nr, Ns, flags, out, row_gate);
+  else
+    hipLaunchKernelGGL(k_fused_prep<float>, dim3(T), dim3(256), 0, st, static_cast<const float*>(u), inv_row,
+                       topk_gate, seg_offset, d, K, Nr, Ns, flags, out, row_gate);
 }
 
 }  // namespace moe

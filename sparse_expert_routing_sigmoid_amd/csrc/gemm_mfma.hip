@@ -85,6 +85,8 @@ struct Item {
   int brow[4];                  // B rows of this wave's four 32-column MFMA tiles
   int mrow0;                    // first tile row of this wave
   int rows, row0, nk;
+  const int32_t* tok;           // fused combine: token of every permuted row
+  const float* gate;            // fused combine: gate of every permuted row
 };
 
 // Loads part Q (of P) of the K slab starting at byte `kb` into stage buffer
@@ -329,7 +331,7 @@ __device__ __forceinline__ float absmax8(float4 a, float4 b) {
 // are quantised as one 1x128 E4M3 tile (power-of-two scale, round to nearest
 // even): the 16 threads holding a row find its amax with lane shuffles.
 // MT == 0: the wave has no rows.
-template <bool PHASE_A, bool H_FP8, int MT, int MA, typename OT, bool KEEP>
+template <bool PHASE_A, bool H_FP8, int MT, int MA, typename OT, bool KEEP, bool FUSE = false>
 __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Item& it, uint8_t* st0, uint8_t* st1,
                                          int wm, int wn, int tid, OT* __restrict__ out, float* __restrict__ out_scale,
                                          uint16_t* __restrict__ ab, uint16_t* __restrict__ hb, int Nd, int n) {
@@ -337,6 +339,32 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
   constexpr int LSTR = P_TN * 4;
   const int lcol = it.lane & 31;
   const long long col0 = (long long)n * NC;
+  if constexpr (!PHASE_A && FUSE) {
+    // Fused combine: out [T, Nd] fp32 holds the layer output; every token
+    // row adds gate * y to its token's row with hardware fp32 atomics (one
+    // 4-byte add per value; the 32 lanes of a row segment hit consecutive
+    // columns).  The order of the adds is not fixed.
+    static_assert(sizeof(OT) == 4, "the fused combine accumulates in fp32");
+    float* ob = reinterpret_cast<float*>(out) + col0 + wn * 128 + lcol;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = wm * 128 + i * 32 + acc_row32(e, it.lane);
+        if (r < it.rows) {
+          const long long t = it.tok[it.row0 + r];
+          const float g = it.gate[it.row0 + r];
+          float* rowp = ob + t * Nd;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc[i][j][e]));
+            unsafeAtomicAdd(rowp + j * 32, g * v);
+          }
+        }
+      }
+    return;
+  }
   if constexpr (!PHASE_A && sizeof(OT) == 2) {
     // bf16 y straight from the accumulators, one 2-byte store per value: no
     // LDS round trip and no barriers (6.4 -> 5.4 us per 256 x 256 item).
@@ -430,7 +458,7 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
 // K loop (two-stage pipeline, unrolled by two so each step names its
 // buffers and the loop has a single exit) and epilogue, all in one
 // instantiation.
-template <bool FP8, bool PHASE_A, int MT, typename OT, bool KEEP>
+template <bool FP8, bool PHASE_A, int MT, typename OT, bool KEEP, bool FUSE>
 __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* st1, int wm, int wn, int tid,
                                          OT* __restrict__ out, float* __restrict__ out_scale,
                                          uint16_t* __restrict__ ab, uint16_t* __restrict__ hb, int Nd, int n) {
@@ -452,14 +480,14 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
     pipe_step<FP8, MT>(acc, it, st0, st1, s + 1, s + 2 < it.nk, (uint32_t)(s + 2) * P_ROWB);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's zero loads land before LDS is reused
-  epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT, KEEP>(acc, it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd,
+  epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT, KEEP, FUSE>(acc, it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd,
                                                       n);
 }
 
 // run_tile of the bf16 kernels: the K loop of deep_body (two A stages,
 // three B stages, rotated each stage), then the epilogue.  lds = D_LDS
 // bytes; the epilogue stages its rows through the first 128 KB.
-template <bool PHASE_A, int MT, typename OT, bool KEEP>
+template <bool PHASE_A, int MT, typename OT, bool KEEP, bool FUSE>
 __device__ __forceinline__ void run_tile_deep(const Item& it, uint8_t* lds, int wm, int wn, int tid,
                                               OT* __restrict__ out, uint16_t* __restrict__ ab, int Nd, int n) {
   constexpr int MA = MT > 0 ? MT : 1;
@@ -494,7 +522,7 @@ __device__ __forceinline__ void run_tile_deep(const Item& it, uint8_t* lds, int 
     t = b0; b0 = b1; b1 = b2; b2 = t;
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // the last zero loads land before LDS is reused
-  epilogue<PHASE_A, false, MT, MA, OT, KEEP>(acc, it, lds, lds + 2 * D_AB, wm, wn, tid, out, nullptr, ab, nullptr,
+  epilogue<PHASE_A, false, MT, MA, OT, KEEP, FUSE>(acc, it, lds, lds + 2 * D_AB, wm, wn, tid, out, nullptr, ab, nullptr,
                                              Nd, n);
 }
 
@@ -533,7 +561,9 @@ struct KernelLds<false> {
 //      phase A writes h as E4M3 codes with scales out_scale [P, Nd/128].
 // ab (bf16 phase A only, may be NULL): [P, 2 Nd] gets the pre-activations
 //      a (columns 0..Nd-1) and b (Nd..2Nd-1) of every token row.
-template <bool FP8, bool PHASE_A, typename OT, bool KEEP = false>
+// FUSE (phase B): out = the layer output [T, Nd] fp32; each token row adds
+//      row_gate[row] * y to the row of its token (fused combine).
+template <bool FP8, bool PHASE_A, typename OT, bool KEEP = false, bool FUSE = false>
 __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __restrict__ x,
                                                             const uint8_t* __restrict__ w,
                                                             const float* __restrict__ x_scale,
@@ -548,7 +578,8 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
                                                             const int* __restrict__ items,
                                                             OT* __restrict__ out, float* __restrict__ out_scale,
                                                             uint16_t* __restrict__ ab,
-                                                            uint16_t* __restrict__ hb) {
+                                                            uint16_t* __restrict__ hb,
+                                                            const float* __restrict__ row_gate) {
   constexpr int EB = Fmt<FP8>::EB;
   __shared__ KernelLds<FP8> L;
   uint8_t* lds = L.base();
@@ -591,6 +622,8 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
     it.rows = tm.w;  // token rows; the tile's padding rows are skipped
     it.row0 = tm.y;
     it.nk = kblocks;
+    it.tok = row_token;
+    it.gate = row_gate;
     it.lane = lane;
     it.lsw = (lane & 7) ^ ((lane >> 3) & 1);
     it.wave = __builtin_amdgcn_readfirstlane(wave);
@@ -636,19 +669,19 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
     mt_live = __builtin_amdgcn_readfirstlane(mt_live < 0 ? 0 : (mt_live > 4 ? 4 : mt_live));
     if constexpr (FP8) {
       switch (mt_live) {
-        case 4: run_tile<FP8, PHASE_A, 4, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        case 3: run_tile<FP8, PHASE_A, 3, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        case 2: run_tile<FP8, PHASE_A, 2, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        case 1: run_tile<FP8, PHASE_A, 1, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        default: run_tile<FP8, PHASE_A, 0, OT, KEEP>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 4: run_tile<FP8, PHASE_A, 4, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 3: run_tile<FP8, PHASE_A, 3, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 2: run_tile<FP8, PHASE_A, 2, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 1: run_tile<FP8, PHASE_A, 1, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        default: run_tile<FP8, PHASE_A, 0, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
       }
     } else {
       switch (mt_live) {
-        case 4: run_tile_deep<PHASE_A, 4, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        case 3: run_tile_deep<PHASE_A, 3, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        case 2: run_tile_deep<PHASE_A, 2, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        case 1: run_tile_deep<PHASE_A, 1, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        default: run_tile_deep<PHASE_A, 0, OT, KEEP>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 4: run_tile_deep<PHASE_A, 4, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 3: run_tile_deep<PHASE_A, 3, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 2: run_tile_deep<PHASE_A, 2, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 1: run_tile_deep<PHASE_A, 1, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        default: run_tile_deep<PHASE_A, 0, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
       }
     }
   }
@@ -880,7 +913,7 @@ PhaseSched phase_sched(int* sched, int phase, int cap, int ntA) {
 void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const int32_t* row_token,
                                 const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                 int Nr, int cap, uint16_t* h, uint16_t* ab, void* y, bool y_f32, int* sched,
-                                hipStream_t st) {
+                                hipStream_t st, const float* row_gate) {
   const int nb = persistent_blocks();
   const uint32_t x_bytes = (uint32_t)((long long)T * d * 2);
   const uint32_t h_bytes = (uint32_t)(P * I * 2);
@@ -890,17 +923,23 @@ void launch_ffn_bf16_persistent(const uint16_t* x, const uint16_t* w13, const ui
   const PhaseSched a = phase_sched(sched, 0, cap, ntA), b = phase_sched(sched, 1, cap, ntA);
   hipLaunchKernelGGL((k_ffn_persistent<false, true, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, xb,
                      reinterpret_cast<const uint8_t*>(w13), nullptr, nullptr, row_token, tile_map, n_tiles, d, I,
-                     x_bytes, 0u, a.cnt, a.tot, a.off, a.items, h, nullptr, ab, nullptr);
+                     x_bytes, 0u, a.cnt, a.tot, a.off, a.items, h, nullptr, ab, nullptr, nullptr);
   const uint8_t* hb = reinterpret_cast<const uint8_t*>(h);
-  if (y_f32)
+  if (row_gate)  // fused combine: y is the layer output [T, d] fp32
+    hipLaunchKernelGGL((k_ffn_persistent<false, false, float, false, true>), dim3(nb), dim3(P_THREADS), 0, st, hb,
+                       reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr, nullptr, nullptr,
+                       row_gate);
+  else if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<false, false, float>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
-                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr, nullptr, nullptr);
+                       h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<float*>(y), nullptr, nullptr, nullptr,
+                       nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<false, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, hb,
                        reinterpret_cast<const uint8_t*>(w2), nullptr, nullptr, row_token, tile_map, n_tiles, I, d,
                        h_bytes, 0u, b.cnt, b.tot, b.off, b.items, static_cast<uint16_t*>(y), nullptr, nullptr,
-                       nullptr);
+                       nullptr, nullptr);
 }
 
 // E4M3 x E4M3: x codes [T, d] with x_scale [T, d/128]; W13 / W2 codes with
@@ -911,7 +950,7 @@ void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uin
                                const uint8_t* w2, const float* w2_scale, const int32_t* row_token,
                                const int32_t* tile_map, const int32_t* n_tiles, int T, long long P, int d, int I,
                                int Nr, int cap, uint8_t* h, float* h_scale, void* y, bool y_f32, int* sched,
-                               hipStream_t st, uint16_t* ab, uint16_t* hb) {
+                               hipStream_t st, uint16_t* ab, uint16_t* hb, const float* row_gate) {
   const int nb = persistent_blocks();
   const uint32_t x_bytes = (uint32_t)((long long)T * d);
   const uint32_t xs_bytes = (uint32_t)((long long)T * (d / 128) * 4);
@@ -923,19 +962,23 @@ void launch_ffn_fp8_persistent(const uint8_t* x, const float* x_scale, const uin
   if (ab || hb)
     hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t, true>), dim3(nb), dim3(P_THREADS), 0, st, x, w13,
                        x_scale, w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, xs_bytes, a.cnt, a.tot, a.off,
-                       a.items, h, h_scale, ab, hb);
+                       a.items, h, h_scale, ab, hb, nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<true, true, uint8_t>), dim3(nb), dim3(P_THREADS), 0, st, x, w13, x_scale,
                        w13_scale, row_token, tile_map, n_tiles, d, I, x_bytes, xs_bytes, a.cnt, a.tot, a.off, a.items,
-                       h, h_scale, nullptr, nullptr);
-  if (y_f32)
+                       h, h_scale, nullptr, nullptr, nullptr);
+  if (row_gate)  // fused combine: y is the layer output [T, d] fp32
+    hipLaunchKernelGGL((k_ffn_persistent<true, false, float, false, true>), dim3(nb), dim3(P_THREADS), 0, st, h, w2,
+                       h_scale, w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off,
+                       b.items, static_cast<float*>(y), nullptr, nullptr, nullptr, row_gate);
+  else if (y_f32)
     hipLaunchKernelGGL((k_ffn_persistent<true, false, float>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
                        w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
-                       static_cast<float*>(y), nullptr, nullptr, nullptr);
+                       static_cast<float*>(y), nullptr, nullptr, nullptr, nullptr);
   else
     hipLaunchKernelGGL((k_ffn_persistent<true, false, uint16_t>), dim3(nb), dim3(P_THREADS), 0, st, h, w2, h_scale,
                        w2_scale, row_token, tile_map, n_tiles, I, d, h_bytes, hs_bytes, b.cnt, b.tot, b.off, b.items,
-                       static_cast<uint16_t*>(y), nullptr, nullptr, nullptr);
+                       static_cast<uint16_t*>(y), nullptr, nullptr, nullptr, nullptr);
 }
 
 }  // namespace moe

@@ -134,6 +134,24 @@ def test_combine_bias_quant_reject_bad_arguments():
     assert L.fp8_dequantize_tiles(None, FAKE, 4, 128, 1, 128, FAKE, M.MOE_F32, None) == M.MOE_EINVAL
 
 
+def test_fused_combine_rejects_bad_arguments():
+    L = M.lib()
+    fake, fake_out = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)   # never dereferenced
+    T, K, Nr, Ns, d, I = 512, 4, 16, 1, 512, 256
+
+    def call(x_t=M.MOE_BF16, w_t=M.MOE_BF16, flags=0, out=fake_out, u_t=M.MOE_BF16, d=d):
+        return L.moe_expert_gemm_combine(fake, x_t, None, w_t, fake, None, fake, None, T, K, Nr, Ns, d, I, 32,
+                                         fake, fake, fake, fake, fake, fake, fake, u_t, flags, fake, 1 << 40, out,
+                                         None)
+    assert call(x_t=M.MOE_F32, w_t=M.MOE_F32) == M.MOE_EUNSUPPORTED      # only the persistent MFMA paths
+    assert call(x_t=M.MOE_BF16, w_t=M.MOE_E4M3) == M.MOE_EUNSUPPORTED    # nor the decode path
+    assert call(flags=8) == M.MOE_EINVAL
+    assert call(out=fake) == M.MOE_EINVAL                                 # out aliases u
+    assert call(u_t=M.MOE_E4M3) == M.MOE_EINVAL
+    assert call(d=520) == M.MOE_EUNSUPPORTED                               # bf16 persistent needs d % 256 == 0
+    assert b"persistent" in L.moe_last_error() or b"256" in L.moe_last_error()
+
+
 def test_python_binding_raises_with_message():
     import torch
     with pytest.raises(M.MoeError, match="MOE_EINVAL"):
