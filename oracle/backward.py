@@ -46,6 +46,17 @@ Reading B3: every quantiser of the forward passes the gradient straight
 through (it is the identity when differentiated), so each weight gradient
 uses the quantised operand that its forward product multiplied: dW2 the
 quantised h, dW13 the quantised expert input Q(x).
+
+Reading B5 (E4M3 weight gradients, fp8_wgrad=True): the weight-gradient
+products dW2 = dy^T Q(h) and dW13 = [da | db]^T Q(x) sum over one expert's
+rows, the token axis, and the pages give no tile shape along it.  B2's rule
+for activation operands (1x128 tiles along the product's K axis) is kept:
+both operands are quantised column by column in runs of 128 consecutive
+rows of the expert, its rows taken in token order, the last run shorter
+(as if padded with zero rows), each run with its own power-of-two scale.
+The codes are decided from bf16 values (B4): dy and [da | db] are rounded
+to bf16 first; Q(h) and Q(x) are decoded E4M3 values, exact in bf16, and
+are quantised again along the token axis.
 """
 from __future__ import annotations
 
@@ -140,6 +151,28 @@ def fp8_tile_matmul(g: np.ndarray, w: np.ndarray) -> np.ndarray:
     return dequantize_tiles(gq, gs, 1, 128) @ dequantize_tiles(wq, ws, 128, 128)
 
 
+def quantize_token_runs(m: np.ndarray) -> np.ndarray:
+    """Reading B5: m [n, C] (values exact in fp32; the n rows of one expert in
+    token order) through E4M3 with one power-of-two scale per column and run
+    of 128 consecutive rows, the last run shorter.  Returns the decoded values
+    (code x scale, fp64, exact)."""
+    m = np.asarray(m, dtype=np.float64)
+    n, C = m.shape
+    if n == 0:
+        return np.zeros((0, C))
+    padded = np.zeros((-(-n // 128) * 128, C))
+    padded[:n] = m                       # zero rows change no run's largest magnitude
+    q, s = quantize_tiles(padded, 128, 1)
+    return dequantize_tiles(q, s, 128, 1)[:n]
+
+
+def fp8_wgrad(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """a^T b [M, N] over the rows of one expert (a [n, M], b [n, N], values
+    exact in fp32) with both operands in E4M3 runs along the rows (reading
+    B5); the decoded values are multiplied in fp64."""
+    return quantize_token_runs(a).T @ quantize_token_runs(b)
+
+
 def ffn_backward_fp8(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndarray):
     """ffn_backward with the input-gradient products in E4M3 (readings B2,
     B4): dh = Q(bf16(dy)) Q(W2), dx = Q(bf16([da | db])) Q(W13), with da, db
@@ -162,14 +195,19 @@ def ffn_backward_fp8(x: np.ndarray, w13: np.ndarray, w2: np.ndarray, dy: np.ndar
     return dx, dw13, dw2, y
 
 
-def ffn_backward_fp8_train(x: np.ndarray, w13q: np.ndarray, w2q: np.ndarray, dy: np.ndarray):
+def ffn_backward_fp8_train(x: np.ndarray, w13q: np.ndarray, w2q: np.ndarray, dy: np.ndarray,
+                           fp8_wgrad_products: bool = False):
     """Forward and backward of one expert on the FP8 training path (readings
     B2-B4).  x [n, d] the expert's input rows as stored; w13q [2I, d], w2q
     [d, I] the decoded E4M3 weights (code x block scale).
       forward:  [a; b] = W13q Q(x),  h = Q(SiLU(a) b),  y = W2q h
       backward: dW2 = dy^T h,  dh = Q(bf16(dy)) W2q,  da, db at bf16(a), bf16(b),
                 dW13 = [da | db]^T Q(x),  dx = Q(bf16([da | db])) W13q
-    Q: 1x128 E4M3 tiles along the row.  Returns (dx, dw13, dw2, y)."""
+    Q: 1x128 E4M3 tiles along the row.  fp8_wgrad_products: the two weight
+    gradients on E4M3 operands (reading B5),
+                dW2 = R(bf16(dy))^T R(h),  dW13 = R(bf16([da | db]))^T R(Q(x))
+    with R the runs of 128 rows of quantize_token_runs.  Returns (dx, dw13,
+    dw2, y)."""
     x, w13q, w2q, dy = _f64(x), _f64(w13q), _f64(w2q), _f64(dy)
     I = w2q.shape[1]
     xq = _q_act(x)
@@ -177,19 +215,19 @@ def ffn_backward_fp8_train(x: np.ndarray, w13q: np.ndarray, w2q: np.ndarray, dy:
     a, b = ab[:, :I], ab[:, I:]
     h = _q_act(silu(a) * b)
     y = h @ w2q.T
-    dw2 = dy.T @ h
+    dw2 = fp8_wgrad(round_bf16(dy), h) if fp8_wgrad_products else dy.T @ h
     dh = _q_grad(dy) @ w2q
     ar, br = round_bf16(a), round_bf16(b)
     da = dh * br * silu_grad(ar)
     db = dh * silu(ar)
     dab = np.concatenate([da, db], axis=1)
-    dw13 = dab.T @ xq
+    dw13 = fp8_wgrad(round_bf16(dab), xq) if fp8_wgrad_products else dab.T @ xq
     dx = _q_grad(dab) @ w13q
     return dx, dw13, dw2, y
 
 
 def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out, fp8_dgrad: bool = False,
-                   fp8_train: bool = False) -> LayerGrads:
+                   fp8_train: bool = False, fp8_wgrad: bool = False) -> LayerGrads:
     """Gradients of L = sum(grad_out * out) for the layer of
     oracle.moe.layer_forward (bf16 / fp32 path, no FP8 quantisation).
 
@@ -197,8 +235,15 @@ def layer_backward(u, e, b, w13, w2, Nr: int, Ns: int, K: int, grad_out, fp8_dgr
     grad_out [T, d] = dL/dout.  fp8_dgrad: every expert's backward is
     ffn_backward_fp8 instead of ffn_backward.  fp8_train: the whole FP8
     training step, ffn_backward_fp8_train, with w13 / w2 the decoded E4M3
-    weights; the router still sees the unquantised u (R8)."""
-    ffn_bwd = ffn_backward_fp8_train if fp8_train else (ffn_backward_fp8 if fp8_dgrad else ffn_backward)
+    weights; the router still sees the unquantised u (R8).  fp8_wgrad (with
+    fp8_train only): the weight gradients on E4M3 operands as well (B5), each
+    expert's runs of 128 rows counted from its first row."""
+    if fp8_wgrad and not fp8_train:
+        raise ValueError("layer_backward: fp8_wgrad needs fp8_train")
+    if fp8_train:
+        ffn_bwd = lambda *a: ffn_backward_fp8_train(*a, fp8_wgrad_products=fp8_wgrad)
+    else:
+        ffn_bwd = ffn_backward_fp8 if fp8_dgrad else ffn_backward
     u, e, G = _f64(u), _f64(e), _f64(grad_out)
     w13, w2 = _f64(w13), _f64(w2)
     T, d = u.shape

@@ -396,3 +396,236 @@ def test_round_bf16_matches_torch_and_hand_cases():
     assert B.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
     assert B.round_bf16(np.array([-(1 + 3 * 2.0 ** -8)]))[0] == -(1 + 2.0 ** -6)
     assert B.round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -20]))[0] == 1 + 2.0 ** -7
+
+
+# ------------------------------------------------- E4M3 weight gradients --
+# Reading B5: both operands of a weight gradient in E4M3 runs of 128 rows
+# (the token axis) per column.  The pins below use a quantiser written here
+# by exhaustive search over the format's values, not the oracle's codec.
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Every finite non-negative E4M3FN value, indexed by its 7-bit code,
+    from the fields: exponent code >> 3 (bias 7, 0 subnormal), mantissa
+    code & 7; code 127 is NaN."""
+    return np.array([(c & 7) / 8.0 * 2.0 ** -6 if c >> 3 == 0 else (1 + (c & 7) / 8.0) * 2.0 ** ((c >> 3) - 7)
+                     for c in range(127)])
+
+
+_MAGS = _e4m3_magnitudes()
+
+
+def _search_scale(amax: float) -> float:
+    if amax == 0.0:
+        return 1.0
+    k = -126
+    while amax > 448.0 * 2.0 ** k:
+        k += 1
+    return 2.0 ** k
+
+
+def _nearest_e4m3(v: np.ndarray) -> np.ndarray:
+    """Each |v| <= 448 to the nearest E4M3 value by exhaustive search; of two
+    equally near values the one with the even code (mantissa bit 0 clear)."""
+    dist = np.abs(np.abs(v)[:, None] - _MAGS[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    tie_ok = (dist == best) & (np.arange(127)[None, :] % 2 == 0)
+    only = (dist == best).sum(axis=1) == 1
+    code = np.where(only, np.argmin(dist, axis=1), np.argmax(tie_ok, axis=1))
+    return np.copysign(_MAGS[code], v)
+
+
+def _search_token_runs(m: np.ndarray) -> np.ndarray:
+    """Runs of 128 rows per column, each scaled by its own searched power of
+    two, rounded by exhaustive search, decoded."""
+    m = np.asarray(m, dtype=np.float64)
+    out = np.zeros_like(m)
+    for c in range(m.shape[1]):
+        for r0 in range(0, m.shape[0], 128):
+            run = m[r0:r0 + 128, c]
+            s = _search_scale(float(np.abs(run).max()))
+            out[r0:r0 + 128, c] = _nearest_e4m3(run / s) * s
+    return out
+
+
+def test_token_runs_match_exhaustive_search():
+    """quantize_token_runs against the searched quantiser: 300 rows (runs of
+    128, 128 and 44), columns of very different magnitude, exact zeros, a
+    zero column, and values halfway between two E4M3 values of their run."""
+    rng = np.random.default_rng(20)
+    m = rng.standard_normal((300, 7)) * np.exp2(rng.integers(-20, 20, (1, 7)))
+    m[:, 3] = 0.0
+    m[5:9, 1] = 0.0
+    m[128, 2] = 448.0 * 2.0 ** -3          # run 2 of column 2: scale 2^-3
+    m[129:140, 2] = np.array([1.0625, 1.1875, 3.125, 0.5 + 2.0 ** -5, 2.0 ** -9 * 1.5, 2.0 ** -9 * 0.5, 13.5, 26.0,
+                              -1.0625, -3.125, 200.0]) * 2.0 ** -3   # midpoints at that scale (26: on the grid)
+    m = m.astype(np.float32).astype(np.float64)
+    got = B.quantize_token_runs(m)
+    want = _search_token_runs(m)
+    assert np.array_equal(got, want)
+    assert np.all(got[:, 3] == 0.0)
+    # ties went to the even neighbour (mantissa field even): 1.0625 -> 1,
+    # 1.1875 -> 1.25, 3.125 -> 3, 0.53125 -> 0.5, 1.5 * 2^-9 -> 2^-8,
+    # 0.5 * 2^-9 -> 0, 13.5 -> 14, 200 -> 192
+    assert list(got[129:140, 2] * 8) == [1.0, 1.25, 3.0, 0.5, 2.0 ** -8, 0.0, 14.0, 26.0, -1.0, -3.0, 192.0]
+    assert B.quantize_token_runs(np.zeros((0, 5))).shape == (0, 5)
+
+
+def _on_grid_runs(rng, rows, cols, kmin=-6, kmax=6):
+    """Every run of 128 rows of every column holds E4M3 values times its own
+    2^k and one entry of magnitude 448 * 2^k: the run's scale is 2^k and the
+    quantiser is the identity on it."""
+    x = _e4m3_grid_values(rng, (rows, cols))
+    for c in range(cols):
+        for r0 in range(0, rows, 128):
+            run = x[r0:r0 + 128, c]
+            run[rng.integers(0, run.size)] = 448.0 if rng.random() < .5 else -448.0
+            x[r0:r0 + 128, c] = run * 2.0 ** int(rng.integers(kmin, kmax + 1))
+    return x
+
+
+def test_fp8_wgrad_is_exact_on_the_grid():
+    """Operands on the grid of their runs give exactly the fp64 product.  The
+    exponent changes from run to run and from column to column, so runs cut
+    along the columns, of another length, or not restarted at row 0 would mix
+    exponents and round the smaller entries."""
+    rng = np.random.default_rng(21)
+    a = _on_grid_runs(rng, 300, 40)
+    b = _on_grid_runs(rng, 300, 24)
+    assert np.array_equal(B.fp8_wgrad(a, b), a.T @ b)
+    # one run shifted by a row: its scale no longer holds for the row that moved in
+    shifted = np.concatenate([np.zeros((1, 40)), a[:-1]])
+    shifted[0] = a[-1]
+    assert not np.array_equal(B.quantize_token_runs(shifted), shifted)
+
+
+def test_fp8_wgrad_error_within_the_rounding_bound():
+    """Random operands (fp32-exact, per-row outliers): each entry is off by
+    at most half an E4M3 step of its run, so each product entry is within
+    |a|^T e_b + e_a^T |b| + e_a^T e_b."""
+    rng = np.random.default_rng(22)
+    a = (rng.standard_normal((333, 48)) * np.exp(2 * rng.standard_normal((333, 1)))).astype(np.float32).astype(
+        np.float64)
+    b = (rng.standard_normal((333, 40)) / 16).astype(np.float32).astype(np.float64)
+    got = B.fp8_wgrad(a, b)
+    want = a.T @ b
+
+    def step_bound(x):
+        e = np.zeros_like(x)
+        for c in range(x.shape[1]):
+            for r0 in range(0, x.shape[0], 128):
+                run = x[r0:r0 + 128, c]
+                s = _search_scale(float(np.abs(run).max()))
+                e[r0:r0 + 128, c] = np.maximum(np.abs(run) * 2.0 ** -4, s * 2.0 ** -10)
+        return e
+
+    ea, eb = step_bound(a), step_bound(b)
+    bound = np.abs(a).T @ eb + ea.T @ np.abs(b) + ea.T @ eb
+    assert np.all(np.abs(got - want) <= bound * (1 + 1e-12) + 1e-300)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert 1e-4 < rel < 0.05
+
+
+class GradQRuns(torch.autograd.Function):
+    """value t, gradient R(bf16(dL/dt)): the gradient operand of an E4M3
+    weight-gradient product, in runs of 128 rows (B5, B4)."""
+    @staticmethod
+    def forward(ctx, t):
+        return t.view_as(t)
+
+    @staticmethod
+    def backward(ctx, g):
+        return torch.from_numpy(_search_token_runs(_bf16(g.numpy())))
+
+
+def _split_product_w8(x, w, wq):
+    """Value x wq^T; dW = R(bf16(dY))^T R(x), dX = Q(bf16(dY)) wq."""
+    xr = torch.from_numpy(_search_token_runs(x.detach().numpy()))
+    p1 = GradQRuns.apply(xr @ w.T)
+    return GradQ.apply(x @ wq.T) + p1 - p1.detach()
+
+
+def _autograd_ffn_w8(x, w13, w2, dy):
+    """_autograd_ffn(train=True) with both weight gradients on E4M3 runs."""
+    I = w2.shape[1]
+    xt = torch.tensor(x, requires_grad=True)
+    W13 = torch.tensor(w13, requires_grad=True)
+    W2 = torch.tensor(w2, requires_grad=True)
+    W13q = torch.from_numpy(_q_tiles(w13, 128))
+    W2q = torch.from_numpy(_q_tiles(w2, 128))
+    ab = _split_product_w8(st_q(xt), W13, W13q)
+    a, b = ab[:, :I], ab[:, I:]
+    h_val = torch.from_numpy(_q_tiles((a * torch.sigmoid(a) * b).detach().numpy()))
+    ar, br = at_bf16(a), at_bf16(b)
+    h_r = ar * torch.sigmoid(ar) * br
+    h = h_val + (h_r - h_r.detach())
+    y = _split_product_w8(h, W2, W2q)
+    (y * torch.from_numpy(dy)).sum().backward()
+    return xt.grad.numpy(), W13.grad.numpy(), W2.grad.numpy(), y.detach().numpy()
+
+
+@pytest.mark.parametrize("n", [200, 77])
+def test_fp8_wgrad_train_step_equals_autograd(n):
+    """ffn_backward_fp8_train(fp8_wgrad_products=True) against fp64 autograd
+    of the training step's graph with both weight-gradient products on runs of
+    128 rows (B5): dW2 = R(bf16(dy))^T R(Q(h)), dW13 = R(bf16([da | db]))^T
+    R(Q(x)); dx and y as without (B2-B4)."""
+    rng = np.random.default_rng(23 + n)
+    d, I = 256, 128
+    x = _bf16(rng.standard_normal((n, d)))
+    w13q = _q_tiles(O.quantize_activations(rng.standard_normal((2 * I, d)) / 16), 128)
+    w2q = _q_tiles(O.quantize_activations(rng.standard_normal((d, I)) / 16), 128)
+    dy = _bf16(rng.standard_normal((n, d)) * 0.3 * np.exp(rng.standard_normal((n, 1))))
+    dx, dw13, dw2, y = B.ffn_backward_fp8_train(x, w13q, w2q, dy, fp8_wgrad_products=True)
+    gx, g13, g2, yt = _autograd_ffn_w8(x, w13q, w2q, dy)
+    np.testing.assert_allclose(y, yt, rtol=1e-12, atol=1e-12)
+    _assert_same(dw2, g2, "dW2")
+    _assert_same(dw13, g13, "dW13")
+    _assert_same(dx, gx, "dx")
+    # the quantisation of the weight-gradient operands did happen
+    dx0, dw13_0, dw2_0, _ = B.ffn_backward_fp8_train(x, w13q, w2q, dy)
+    far = lambda p, q: np.max(np.abs(p - q)) > 1e-6 * np.abs(q).max()
+    assert far(dw2, dw2_0) and far(dw13, dw13_0) and np.array_equal(dx, dx0)
+
+
+def test_fp8_wgrad_plausible_mistakes_fail_the_pin():
+    """Runs of 128 along the columns instead of the rows, and the gradient
+    operand quantised from fp32 instead of bf16, both move dW2 past the
+    autograd pin's tolerance."""
+    rng = np.random.default_rng(24)
+    n, d, I = 200, 256, 128
+    dy = rng.standard_normal((n, d)) * 0.3 * np.exp(rng.standard_normal((n, 1)))
+    h = _q_tiles(rng.standard_normal((n, I)) * np.exp(rng.standard_normal((n, 1))))
+    want = _search_token_runs(_bf16(dy)).T @ _search_token_runs(h)
+    assert np.array_equal(B.fp8_wgrad(B.round_bf16(dy), h), want)
+    far = lambda p, q: np.max(np.abs(p - q)) > 1e-6 * np.abs(q).max()
+    along_cols = _q_tiles(_bf16(dy)).T @ _q_tiles(h)
+    assert far(along_cols, want)
+    from_f32 = _search_token_runs(dy.astype(np.float32).astype(np.float64)).T @ _search_token_runs(h)
+    assert far(from_f32, want)
+
+
+def test_fp8_wgrad_layer_switch():
+    """layer_backward(fp8_train, fp8_wgrad) changes dW13 and dW2 only; each
+    expert's runs start at its own first row (an expert with more than 128
+    rows checked against the single-expert function); fp8_wgrad alone is
+    refused."""
+    p = tiny_inputs(25, T=300, d=256, Nr=2, Ns=1, I=128, K=1)
+    w13q = np.stack([_q_tiles(O.quantize_activations(w), 128) for w in p["w13"]])
+    w2q = np.stack([_q_tiles(O.quantize_activations(w), 128) for w in p["w2"]])
+    g = B.layer_backward(p["u"], p["e"], p["b"], w13q, w2q, 2, 1, 1, p["G"], fp8_train=True)
+    g8 = B.layer_backward(p["u"], p["e"], p["b"], w13q, w2q, 2, 1, 1, p["G"], fp8_train=True, fp8_wgrad=True)
+    for name in ("du", "de", "dgate", "dz", "du_ffn", "du_router"):
+        assert np.array_equal(getattr(g8, name), getattr(g, name)), name
+    assert not np.array_equal(g8.dw13, g.dw13) and not np.array_equal(g8.dw2, g.dw2)
+    r = O.route(p["u"], p["e"], p["b"], 1)
+    for i in range(2):
+        t_sel = np.nonzero(r.idx[:, 0] == i)[0]
+        if t_sel.size > 128:
+            dy = r.gate[t_sel, 0][:, None] * p["G"][t_sel]
+            _, dw13, dw2, _ = B.ffn_backward_fp8_train(p["u"][t_sel], w13q[i], w2q[i], dy, fp8_wgrad_products=True)
+            assert np.array_equal(g8.dw13[i], dw13) and np.array_equal(g8.dw2[i], dw2)
+            break
+    else:
+        pytest.fail("no expert with more than 128 rows")
+    with pytest.raises(ValueError):
+        B.layer_backward(p["u"], p["e"], p["b"], w13q, w2q, 2, 1, 1, p["G"], fp8_wgrad=True)
