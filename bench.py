@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--dgrad-fp8", action="store_true",
                    help="with --train: the backward's input-gradient products on E4M3 operands "
                         "(moe_expert_gemm_backward_w8; E4M3 weights prepared once at set-up)")
+    p.add_argument("--wgrad-bf16", action="store_true",
+                   help="with --train on an E4M3 workload: bf16 weight gradients (moe_expert_gemm_backward_w8) "
+                        "instead of E4M3 ones (moe_expert_gemm_backward_f8)")
     p.add_argument("--fused-combine", action="store_true",
                    help="the expert GEMMs with the combine fused into the down projection (fp32 atomics, "
                         "moe_expert_gemm_combine) instead of moe_expert_gemm + moe_combine")
@@ -74,13 +77,14 @@ TRAFFIC = {
 }
 
 # HBM traffic of one backward expert GEMM call of the training step
-# (moe_expert_gemm_backward / _w8; the latter with its two 1x128
-# quantisation passes), taken the same way from `--train` runs.
+# (moe_expert_gemm_backward / _w8 / _f8, with their quantisation passes),
+# taken the same way from `--train` runs; keyed by workload, and for the
+# E4M3 step with bf16 weight gradients by workload + ":bf16wgrad".
 TRAIN_TRAFFIC = {
     "v3_prefill_bf16": {"fetch_bytes": 57156214931, "write_bytes": 24405509994, "digest": "21e05a20a7e4b31b",
                         "sources": ("gemm_bwd.hip", "common.h")},
-    "v3_train_fp8": {"fetch_bytes": 38621066352, "write_bytes": 25457392501, "digest": "ccb532542fa76c72",
-                     "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
+    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 38621066352, "write_bytes": 25457392501, "digest": "ccb532542fa76c72",
+                               "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
 }
 
 # Source files of the kernels each workload's expert GEMM runs.
@@ -370,7 +374,9 @@ def train_main(args, cfg, dev, stream):
     roofline object describes the moe_expert_gemm_backward call (dgrad and
     wgrad of both expert projections, 12 d I flops per row).  On an E4M3
     workload (x_fp8, E4M3 weights) the step is the FP8 one:
-    moe_expert_gemm_train_w8 and moe_expert_gemm_backward_w8."""
+    moe_expert_gemm_train_w8, Q(u) decoded for the gate/up weight gradient,
+    and moe_expert_gemm_backward_f8 (every backward product on E4M3
+    operands; --wgrad-bf16: moe_expert_gemm_backward_w8)."""
     import numpy as np
     import torch
 
@@ -389,9 +395,11 @@ def train_main(args, cfg, dev, stream):
     w13, w2 = W.make_expert_weights(cfg, dev)
     # E4M3 weights: quantised once per optimizer step, outside the layer step
     w8 = M.quantize_weights(w13, w2) if (args.dgrad_fp8 or fp8_step) else None
+    wgrad8 = fp8_step and not args.wgrad_bf16
     if fp8_step:
         layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True,
-                           tile_m=args.tile_m, device=dev, train=True, grad_dtype=torch.bfloat16)
+                           tile_m=args.tile_m, device=dev, train=True, grad_dtype=torch.bfloat16,
+                           wgrad_fp8=wgrad8)
     else:
         layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16,
                            M.ExpertWeights(M.MOE_BF16, w13, w2), tile_m=args.tile_m, device=dev, train=True,
@@ -405,6 +413,10 @@ def train_main(args, cfg, dev, stream):
         layer.forward(u, e, bias)
         M.moe_combine_backward(G, layer.y, layer.inv_row, layer.topk_gate, layer.topk_score, layer.seg_offset,
                                cfg.Nr, cfg.Ns, layer.dy, layer.dgate, layer.dz, layer.dz_row)
+        x = u
+        if fp8_step:   # the gate/up weight gradient takes the Q(u) the forward multiplied
+            M.fp8_dequantize_tiles(layer.xq, layer.xs, 1, layer.xdq)
+            x = layer.xdq
         if timed:
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
@@ -414,9 +426,10 @@ def train_main(args, cfg, dev, stream):
                                        cfg.I, args.tile_m, layer.seg_offset, layer.row_token, layer.tile_map,
                                        layer.n_tiles, layer.bwd_ws, layer.dx, layer.dw13, layer.dw2)
         else:
-            M.moe_expert_gemm_backward_w8(u, w8, layer.h, layer.ab, layer.dy, cfg.T, cfg.K, cfg.Nr, cfg.Ns, cfg.d,
-                                          cfg.I, args.tile_m, layer.seg_offset, layer.row_token, layer.tile_map,
-                                          layer.n_tiles, layer.bwd_ws, layer.dx, layer.dw13, layer.dw2)
+            bwd = M.moe_expert_gemm_backward_f8 if wgrad8 else M.moe_expert_gemm_backward_w8
+            bwd(x, w8, layer.h, layer.ab, layer.dy, cfg.T, cfg.K, cfg.Nr, cfg.Ns, cfg.d, cfg.I, args.tile_m,
+                layer.seg_offset, layer.row_token, layer.tile_map, layer.n_tiles, layer.bwd_ws, layer.dx, layer.dw13,
+                layer.dw2)
         if timed:
             ev1.record(stream)
             bwd_events.append((ev0, ev1))
@@ -437,14 +450,23 @@ def train_main(args, cfg, dev, stream):
     rows = int(cfg.T * cfg.K + cfg.T * cfg.Ns)
     bwd_flops = 12.0 * cfg.d * cfg.I * rows
     step_flops = 18.0 * cfg.d * cfg.I * rows
-    step_peak = PEAK["bf16"] if not fp8_step else step_flops / (12.0 / 18 * step_flops / PEAK["fp8"] +
-                                                               6.0 / 18 * step_flops / PEAK["bf16"])
+    if not fp8_step:
+        step_peak = PEAK["bf16"]
+    elif wgrad8:
+        step_peak = PEAK["fp8"]
+    else:   # the weight gradients (6 of the 18 d I flops per row) in bf16
+        step_peak = step_flops / (12.0 / 18 * step_flops / PEAK["fp8"] + 6.0 / 18 * step_flops / PEAK["bf16"])
     loads = layer.expert_load.cpu().numpy().astype(np.int64)
     achieved = bwd_flops / (bwd_ms * 1e-3)
     if w8 is None:
         peak = PEAK["bf16"]
         kernels = ("moe_expert_gemm_backward call: k_dgrad (down + SwiGLU backward), k_dgrad (gate/up), "
                    "k_wgrad (down), k_wgrad (gate/up)")
+    elif wgrad8:
+        peak = PEAK["fp8"]
+        kernels = ("moe_expert_gemm_backward_f8 call: k_quant_1x128 (dy), k_dgrad8 (down + SwiGLU backward), "
+                   "k_quant_1x128 ([da|db]), k_dgrad8 (gate/up), k_run_offsets, 4 x k_quant_runs (dy, h, [da|db], "
+                   "gathered x), k_wgrad_deal, k_wgrad8 (down), k_wgrad8 (gate/up); every product E4M3")
     else:
         # half the flops (the input-gradient products) at the E4M3 peak, half
         # (the weight gradients) at the bf16 peak: the call's time at peak
@@ -453,7 +475,8 @@ def train_main(args, cfg, dev, stream):
         kernels = ("moe_expert_gemm_backward_w8 call: k_quant_1x128 (dy), k_dgrad8 (down + SwiGLU backward), "
                    "k_quant_1x128 ([da|db]), k_dgrad8 (gate/up), k_wgrad (down), k_wgrad (gate/up); peak = the "
                    "call's flops over their time at the E4M3 (dgrad) and bf16 (wgrad) peaks")
-    tt = TRAIN_TRAFFIC.get(cfg.name) if (w8 is not None) == fp8_step else None
+    tkey = cfg.name + (":bf16wgrad" if fp8_step and not wgrad8 else "")
+    tt = TRAIN_TRAFFIC.get(tkey) if (w8 is not None) == fp8_step else None
     traffic = None
     if tt and gemm_source_digest(cfg.name, tt["sources"]) == tt["digest"]:
         traffic = (tt["fetch_bytes"] + tt["write_bytes"]) / 1e9
@@ -471,13 +494,15 @@ def train_main(args, cfg, dev, stream):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 + bf16 wgrad" if fp8_step else ("bf16" if w8 is None else "bf16 + e4m3 dgrad"),
+        "dtype": ("e4m3" if wgrad8 else "e4m3 + bf16 wgrad") if fp8_step else (
+            "bf16" if w8 is None else "bf16 + e4m3 dgrad"),
         "data": "synthetic (seeded; random-init expert weights and centroids, seeded bf16 output gradients)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "Nr": cfg.Nr, "Ns": cfg.Ns, "I": cfg.I,
                    "K": cfg.K, "routing": cfg.routing, "weights": cfg.weights, "tile_m": args.tile_m,
                    "step": "training forward + backward + bias rule" + (
-                       "; E4M3 forward and backward input-gradient products, bf16 weight gradients "
-                       "(weights quantised once per optimizer step, not in the step)" if fp8_step else
+                       ("; E4M3 forward and every backward product (weight gradients on runs of 128 tokens)"
+                        if wgrad8 else "; E4M3 forward and backward input-gradient products, bf16 weight gradients")
+                       + " (weights quantised once per optimizer step, not in the step)" if fp8_step else
                        "; backward input-gradient products on E4M3 (weights quantised once at set-up, "
                        "not in the step)" if w8 is not None else ""), "grad_dtype": "bf16",
                    "parallelism": "single GPU"},
@@ -488,7 +513,8 @@ def train_main(args, cfg, dev, stream):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_train(cfg, us[0], gs[0], e, bias0, w13, w2, args.cpu_seconds,
-                                                 fp8="train" if fp8_step else w8 is not None)
+                                                 fp8=("train8" if wgrad8 else "train") if fp8_step else
+                                                 w8 is not None)
     print(json.dumps(out), flush=True)
 
 
@@ -528,13 +554,15 @@ def cpu_baseline_train(cfg, u, G, e, b, w13, w2, seconds, fp8=False):
             ts, ks = np.nonzero(r.idx == i)
             x, dy = u_s[ts], r.gate[ts, ks][:, None] * G_s[ts]
         t1 = time.perf_counter()
-        fn = OB.ffn_backward_fp8_train if fp8 == "train" else (OB.ffn_backward_fp8 if fp8 else OB.ffn_backward)
-        fn(x, w13_i, w2_i, dy)
+        if fp8 in ("train", "train8"):
+            OB.ffn_backward_fp8_train(x, w13_i, w2_i, dy, fp8_wgrad_products=fp8 == "train8")
+        else:
+            (OB.ffn_backward_fp8 if fp8 else OB.ffn_backward)(x, w13_i, w2_i, dy)
         total += time.perf_counter() - t1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": S / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens of step 0: fp64 SwiGLU FFN backward"
-                      f"{' of the FP8 training step' if fp8 == 'train' else ' with E4M3 input-gradient products' if fp8 else ''}"
+                      f"{' of the FP8 training step' if fp8 == 'train' else ' of the FP8 training step with E4M3 weight gradients' if fp8 == 'train8' else ' with E4M3 input-gradient products' if fp8 else ''}"
                       f" (forward recomputed, "
                       f"dx, dW13, dW2) of the {cfg.K} routed + {cfg.Ns} shared experts of each token, "
                       f"{len(need)} experts touched; routing, gate and centroid gradients not timed",

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Limits of this implementation. */
 #define MOE_MAX_EXPERTS 1024   /* routed + shared experts */
@@ -320,6 +320,39 @@ moe_status fp8_quantize_tiles(const void* x, moe_dtype x_t, long long rows, long
 moe_status fp8_dequantize_tiles(const uint8_t* q, const float* scale, long long rows, long long cols,
                                 int tile_rows, int tile_cols, void* out, moe_dtype out_t, void* stream);
 
+/* ------------------------------------------------------------------------
+ * fp8_quantize_runs: E4M3 along the rows of the permuted layout, the token
+ * axis along which a weight gradient sums ([RG-FP8] gives E4M3 for all
+ * tensors but no tile along the tokens; the reading kept here is its 1x128
+ * activation tile turned along that axis).  Segment e, rows
+ * seg_offset[e] .. seg_offset[e+1]-1 (bounds clamped to [0, P]), is cut
+ * into runs of 128 rows from its first row, the last run shorter; each
+ * column of each run gets its own power-of-two scale by the rule of
+ * fp8_quantize_tiles.  Run r of segment e is scale row run_offset[e] + r.
+ *
+ *   x, x_t     device, MOE_F32 or MOE_BF16: gather == 0: [P, cols], row r
+ *              of the layout is x row r; gather != 0: [x_rows, cols], row r
+ *              is x row row_token[r] (the token rows of moe_permute)
+ *   row_token  device [P]: a row with row_token < 0 (padding), or whose
+ *              token is not a row of x, counts as zeros
+ *   seg_offset device [n_seg + 1] (moe_permute's, n_seg = Nr + Ns)
+ *   run_offset device [n_seg + 1] int32 out: run_offset[e] = sum over
+ *              e' < e of ceil(rows of e' / 128), run_offset[n_seg] = runs
+ *   q          device [P, cols] uint8 out: codes of the rows of every
+ *              segment (0 on padding rows); other rows untouched
+ *   scale      device [fp8_quantize_runs_max(P, n_seg), cols] fp32 out:
+ *              rows 0 .. runs-1 written
+ *   Errors: MOE_EINVAL for NULL pointers (x may be NULL when it has no
+ *   rows to read: P == 0, or gather with x_rows == 0), bad sizes
+ *   (cols % 128 != 0, P < 0, n_seg < 1, gather == 0 with x_rows < P), x_t;
+ *   MOE_EUNSUPPORTED for an operand of 2 GiB or more.
+ * ---------------------------------------------------------------------- */
+long long fp8_quantize_runs_max(long long P, int n_seg);  /* (P + 127 n_seg) / 128 */
+moe_status fp8_quantize_runs(const void* x, moe_dtype x_t, long long x_rows, int cols,
+                             const int32_t* row_token, int gather, const int32_t* seg_offset,
+                             int n_seg, long long P, int32_t* run_offset, uint8_t* q,
+                             float* scale, void* stream);
+
 /* ========================================================================
  * Backward pass (bf16 activations and weights).  The pages print no
  * backward pass; these calls compute the chain rule through the forward
@@ -453,6 +486,32 @@ moe_status moe_expert_gemm_backward(const void* x, const void* w13, const void* 
  * ---------------------------------------------------------------------- */
 size_t moe_gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
 moe_status moe_expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale,
+                                       const uint8_t* w2, const float* w2_scale,
+                                       const void* h, const void* ab, const void* dy,
+                                       int T, int K, int Nr, int Ns, int d, int I, int tile_m,
+                                       const int32_t* seg_offset, const int32_t* row_token,
+                                       const int32_t* tile_map, const int32_t* n_tiles,
+                                       void* ws, size_t ws_bytes, void* dx,
+                                       void* dw13, void* dw2, moe_dtype dw_t, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_expert_gemm_backward_f8: moe_expert_gemm_backward_w8 with the two
+ * weight-gradient products on E4M3 operands too, so that every product of
+ * the backward is E4M3 ([RG-FP8]: E4M3 for all tensors).  Their K axis is
+ * the token axis: both operands are quantised in runs of 128 rows of one
+ * expert per column (fp8_quantize_runs), each run and column with its
+ * power-of-two scale, and multiply on the block-scaled matrix cores:
+ *   dW2_e  = R(dy_e)^T R(h_e),  dW13_e = R([da | db]_e)^T R(x_e)
+ * (fp32 accumulation).  dy and [da | db] are quantised from their bf16
+ * values; h and x are the bf16 operands of the forward (after the E4M3
+ * forward: the decoded E4M3 h and Q(u), exact in bf16), quantised again
+ * along the tokens.  dx as in moe_expert_gemm_backward_w8.
+ *   ws  device, moe_gemm_backward_f8_workspace_bytes(...) bytes
+ *   every other argument as moe_expert_gemm_backward_w8
+ *   Errors: as moe_expert_gemm_backward_w8.
+ * ---------------------------------------------------------------------- */
+size_t moe_gemm_backward_f8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status moe_expert_gemm_backward_f8(const void* x, const uint8_t* w13, const float* w13_scale,
                                        const uint8_t* w2, const float* w2_scale,
                                        const void* h, const void* ab, const void* dy,
                                        int T, int K, int Nr, int Ns, int d, int I, int tile_m,

@@ -59,6 +59,10 @@ SIGNATURES = {
     "moe_expert_gemm_train_w8": (_i, [_vp] * 6 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
     "moe_gemm_backward_w8_workspace_bytes": (_sz, [_i] * 7),
     "moe_expert_gemm_backward_w8": (_i, [_vp] * 8 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
+    "moe_gemm_backward_f8_workspace_bytes": (_sz, [_i] * 7),
+    "moe_expert_gemm_backward_f8": (_i, [_vp] * 8 + [_i] * 7 + [_vp] * 5 + [_sz] + [_vp] * 3 + [_i, _vp]),
+    "fp8_quantize_runs_max": (_ll, [_ll, _i]),
+    "fp8_quantize_runs": (_i, [_vp, _i, _ll, _i, _vp, _i, _vp, _i, _ll, _vp, _vp, _vp, _vp]),
     "moe_route_backward": (_i, [_vp, _i, _vp, _vp, _i] + [_vp] * 7 + [_i] * 5 + [_vp, _i, _vp, _vp]),
 }
 
@@ -262,6 +266,37 @@ def moe_expert_gemm_backward_w8(x, w8: "ExpertWeights", h, ab, dy, T, K, Nr, Ns,
                                              dtype_code(dw13), _stream(stream)))
 
 
+def moe_gemm_backward_f8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m):
+    return lib().moe_gemm_backward_f8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m)
+
+
+def moe_expert_gemm_backward_f8(x, w8: "ExpertWeights", h, ab, dy, T, K, Nr, Ns, d, I, tile_m, seg_offset, row_token,
+                                tile_map, n_tiles, ws, dx, dw13, dw2, stream=None):
+    """moe_expert_gemm_backward_w8 with the weight-gradient products on E4M3
+    operands too (runs of 128 rows along the tokens)."""
+    if w8.w_t != MOE_E4M3:
+        raise ValueError("moe_expert_gemm_backward_f8 needs E4M3 weights")
+    _check(lib().moe_expert_gemm_backward_f8(_ptr(x), _ptr(w8.w13), _ptr(w8.w13_scale), _ptr(w8.w2),
+                                             _ptr(w8.w2_scale), _ptr(h), _ptr(ab), _ptr(dy), T, K, Nr, Ns, d, I,
+                                             tile_m, _ptr(seg_offset), _ptr(row_token), _ptr(tile_map),
+                                             _ptr(n_tiles), _ptr(ws), _nbytes(ws), _ptr(dx), _ptr(dw13), _ptr(dw2),
+                                             dtype_code(dw13), _stream(stream)))
+
+
+def fp8_quantize_runs_max(P, n_seg):
+    return lib().fp8_quantize_runs_max(P, n_seg)
+
+
+def fp8_quantize_runs(x, row_token, gather, seg_offset, P, run_offset, q, scale, stream=None):
+    """E4M3 along the rows of the permuted layout: each segment of
+    seg_offset in runs of 128 rows, one power-of-two scale per run and
+    column.  x [P, cols], or with gather [rows, cols] read at row_token."""
+    rows, cols = x.shape
+    _check(lib().fp8_quantize_runs(_ptr(x), dtype_code(x), rows, cols, _ptr(row_token), int(bool(gather)),
+                                   _ptr(seg_offset), seg_offset.shape[0] - 1, P, _ptr(run_offset), _ptr(q),
+                                   _ptr(scale), _stream(stream)))
+
+
 def moe_route_backward(grad_out, dx, u, centroids, topk_idx, inv_row, dz, dz_row, seg_offset, row_token, Nr, Ns,
                        du, de, stream=None):
     T, d = u.shape
@@ -337,7 +372,7 @@ class MoeLayer:
 
     def __init__(self, T, d, Nr, Ns, I, K, act_dtype, weights: ExpertWeights, x_fp8=False,
                  tile_m=32, out_dtype=None, device="cuda", train=False, grad_dtype=None, dgrad_weights=None,
-                 fused_combine=False):
+                 fused_combine=False, wgrad_fp8=None):
         self.T, self.d, self.Nr, self.Ns, self.I, self.K = T, d, Nr, Ns, I, K
         self.tile_m, self.x_fp8, self.w = tile_m, x_fp8, weights
         dev = torch.device(device)
@@ -409,7 +444,15 @@ class MoeLayer:
             self.xdq = torch.empty((T, d), **bf16) if self.train_fp8 else None
             if dgrad_weights is not None and dgrad_weights.w_t != MOE_E4M3:
                 raise ValueError("dgrad_weights must be E4M3 weights")
-            ws_fn = moe_gemm_backward_workspace_bytes if dgrad_weights is None else moe_gemm_backward_w8_workspace_bytes
+            # wgrad_fp8: the weight gradients on E4M3 operands too
+            # (moe_expert_gemm_backward_f8); the E4M3 training step's default
+            self.wgrad_fp8 = self.train_fp8 if wgrad_fp8 is None else bool(wgrad_fp8)
+            if self.wgrad_fp8 and not self.train_fp8:
+                raise ValueError("wgrad_fp8 needs the E4M3 training path (x_fp8 with E4M3 weights)")
+            if dgrad_weights is None:
+                ws_fn = moe_gemm_backward_workspace_bytes
+            else:
+                ws_fn = moe_gemm_backward_f8_workspace_bytes if self.wgrad_fp8 else moe_gemm_backward_w8_workspace_bytes
             self.bwd_ws = torch.empty((max(ws_fn(T, K, Nr, Ns, d, I, tile_m), 1),), dtype=torch.uint8, device=dev)
             self.dw13 = torch.empty((E, 2 * I, d), dtype=gd, device=dev)
             self.dw2 = torch.empty((E, d, I), dtype=gd, device=dev)
@@ -490,9 +533,10 @@ class MoeLayer:
             if self.train_fp8:
                 fp8_dequantize_tiles(self.xq, self.xs, 1, self.xdq, stream=stream)
                 x = self.xdq
-            moe_expert_gemm_backward_w8(x, self.dgrad_w, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns,
-                                        self.d, self.I, self.tile_m, self.seg_offset, self.row_token, self.tile_map,
-                                        self.n_tiles, self.bwd_ws, self.dx, self.dw13, self.dw2, stream)
+            bwd = moe_expert_gemm_backward_f8 if self.wgrad_fp8 else moe_expert_gemm_backward_w8
+            bwd(x, self.dgrad_w, self.h, self.ab, self.dy, self.T, self.K, self.Nr, self.Ns, self.d, self.I,
+                self.tile_m, self.seg_offset, self.row_token, self.tile_map, self.n_tiles, self.bwd_ws, self.dx,
+                self.dw13, self.dw2, stream)
         moe_route_backward(grad_out, self.dx, u, centroids, self.topk_idx, self.inv_row, self.dz, self.dz_row,
                            self.seg_offset, self.row_token, self.Nr, self.Ns, self.du, self.de, stream)
         return self.du, self.de, self.dw13, self.dw2

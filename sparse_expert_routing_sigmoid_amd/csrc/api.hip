@@ -28,6 +28,10 @@ moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long lon
                           uint8_t* q, float* scale, void* stream);
 moe_status dequantize_tiles(const uint8_t* q, const float* scale, long long rows, long long cols, int tile_rows,
                             int tile_cols, void* out, moe_dtype out_t, void* stream);
+long long quantize_runs_max(long long P, int n_seg);
+moe_status quantize_runs(const void* x, moe_dtype x_t, long long x_rows, int cols, const int32_t* row_token,
+                         int gather, const int32_t* seg_offset, int n_seg, long long P, int32_t* run_offset,
+                         uint8_t* q, float* scale, void* stream);
 size_t gemm_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m, moe_dtype x_t, moe_dtype w_t);
 moe_status expert_gemm(const void* x, moe_dtype x_t, const float* x_scale, moe_dtype w_t, const void* w13,
                        const float* w13_scale, const void* w2, const float* w2_scale, int T, int K, int Nr, int Ns,
@@ -66,6 +70,13 @@ moe_status expert_gemm_train_w8(const uint8_t* x, const float* x_scale, const ui
                                 void* ab, void* y, moe_dtype y_t, void* stream);
 size_t gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
 moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                   const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
+                                   int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                   const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                   void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
+                                   void* stream);
+size_t gemm_backward_f8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m);
+moe_status expert_gemm_backward_f8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
                                    const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
                                    int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
                                    const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
@@ -204,6 +215,18 @@ moe_status fp8_dequantize_tiles(const uint8_t* q, const float* scale, long long 
   return moe::dequantize_tiles(q, scale, rows, cols, tile_rows, tile_cols, out, out_t, stream);
 }
 
+long long fp8_quantize_runs_max(long long P, int n_seg) {
+  return P < 0 || n_seg < 0 ? 0 : moe::quantize_runs_max(P, n_seg);
+}
+
+moe_status fp8_quantize_runs(const void* x, moe_dtype x_t, long long x_rows, int cols, const int32_t* row_token,
+                             int gather, const int32_t* seg_offset, int n_seg, long long P, int32_t* run_offset,
+                             uint8_t* q, float* scale, void* stream) {
+  moe::clear_error();
+  return moe::quantize_runs(x, x_t, x_rows, cols, row_token, gather, seg_offset, n_seg, P, run_offset, q, scale,
+                            stream);
+}
+
 size_t moe_gemm_train_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
   return moe::gemm_train_workspace_bytes(T, K, Nr, Ns, d, I, tile_m);
 }
@@ -267,6 +290,22 @@ moe_status moe_expert_gemm_backward_w8(const void* x, const uint8_t* w13, const 
                                        void* stream) {
   moe::clear_error();
   return moe::expert_gemm_backward_w8(x, w13, w13_scale, w2, w2_scale, h, ab, dy, T, K, Nr, Ns, d, I, tile_m,
+                                      seg_offset, row_token, tile_map, n_tiles, ws, ws_bytes, dx, dw13, dw2, dw_t,
+                                      stream);
+}
+
+size_t moe_gemm_backward_f8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  return moe::gemm_backward_f8_workspace_bytes(T, K, Nr, Ns, d, I, tile_m);
+}
+
+moe_status moe_expert_gemm_backward_f8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                       const float* w2_scale, const void* h, const void* ab, const void* dy, int T,
+                                       int K, int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                       void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
+                                       void* stream) {
+  moe::clear_error();
+  return moe::expert_gemm_backward_f8(x, w13, w13_scale, w2, w2_scale, h, ab, dy, T, K, Nr, Ns, d, I, tile_m,
                                       seg_offset, row_token, tile_map, n_tiles, ws, ws_bytes, dx, dw13, dw2, dw_t,
                                       stream);
 }

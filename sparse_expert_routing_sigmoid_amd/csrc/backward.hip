@@ -44,6 +44,14 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
                        uint8_t* dabq, float* dabs, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
                        hipStream_t st);
+void launch_ffn_bwd_f8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
+                       const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
+                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
+                       int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
+                       uint8_t* dabq, float* dabs, uint8_t* hr, uint8_t* xr, float* dyrs, float* hrs, float* dabrs,
+                       float* xrs, int32_t* run_offset, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                       hipStream_t st);
+long long quantize_runs_max(long long P, int n_seg);
 void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const uint16_t* h,
                          const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset, const int32_t* row_token,
                          const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d,
@@ -272,8 +280,6 @@ __global__ __launch_bounds__(CG_THREADS) void k_centroid_grad(const UT* __restri
   }
 }
 
-bool fits31(unsigned long long bytes) { return bytes < (1ull << 31); }
-
 }  // namespace
 
 // ---------------------------------------------------------------- host --
@@ -462,12 +468,37 @@ size_t gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int
   return W8Ws(permute_rows(T, K, Nr, Ns, tile_m), d, I, Nr).total;
 }
 
-moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
-                                   const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
-                                   int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
-                                   const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
-                                   void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
-                                   void* stream) {
+// Workspace of the all-E4M3 backward: W8Ws, then the run codes of h and of
+// the gathered x, the four run-scale arrays [runs, C] (dy, h, [da | db], x)
+// and run_offset [Nr + Ns + 1].
+struct F8Ws {
+  W8Ws w8;
+  size_t hr, xr, dyrs, hrs, dabrs, xrs, run_offset, total;
+  F8Ws(size_t P, int d, int I, int Nr, int Ns) : w8(P, d, I, Nr) {
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t runs = (size_t)quantize_runs_max((long long)P, Nr + Ns);
+    hr = up(w8.total);
+    xr = hr + up(P * I);
+    dyrs = xr + up(P * d);
+    hrs = dyrs + up(runs * d * 4);
+    dabrs = hrs + up(runs * I * 4);
+    xrs = dabrs + up(runs * 2 * I * 4);
+    run_offset = xrs + up(runs * d * 4);
+    total = run_offset + up((size_t)(Nr + Ns + 1) * 4);
+  }
+};
+
+size_t gemm_backward_f8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int I, int tile_m) {
+  if (T < 0 || d < 128 || I < 64 || Nr < 1 || Ns < 0 || K < 1 || tile_m < 1) return 0;
+  return F8Ws(permute_rows(T, K, Nr, Ns, tile_m), d, I, Nr, Ns).total;
+}
+
+// The argument checks of the E4M3 backward calls; P the permuted rows.
+static moe_status check_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                    const float* w2_scale, const void* h, const void* ab, const void* dy, int T,
+                                    int K, int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                    const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                    void* ws, void* dx, void* dw13, void* dw2, moe_dtype dw_t, size_t& P) {
   const moe_status cs = check_layer(T, K, Nr, Ns, d, I, tile_m);
   if (cs != MOE_OK) return cs;
   MOE_REQUIRE(dw_t == MOE_F32 || dw_t == MOE_BF16, MOE_EINVAL, "dw_t must be MOE_F32 or MOE_BF16");
@@ -479,10 +510,50 @@ moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const floa
               MOE_EINVAL, "data tensors and ws must be 16-byte aligned");
   MOE_REQUIRE(ffn_bwd_w8_ok(d, I), MOE_EUNSUPPORTED,
               "E4M3 backward needs d % 256 == 0, I % 128 == 0, d <= 16384 and I <= 8192");
-  const size_t P = permute_rows(T, K, Nr, Ns, tile_m);
+  P = permute_rows(T, K, Nr, Ns, tile_m);
   MOE_REQUIRE(fits31((unsigned long long)T * d * 2) && fits31((unsigned long long)P * d * 2) &&
                   fits31((unsigned long long)P * 2 * I * 2) && fits31((unsigned long long)2 * I * d * 2),
               MOE_EUNSUPPORTED, "backward: operand of 2 GiB or more");
+  return MOE_OK;
+}
+
+moe_status expert_gemm_backward_f8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                   const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
+                                   int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                   const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                   void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
+                                   void* stream) {
+  size_t P = 0;
+  const moe_status cs = check_backward_w8(x, w13, w13_scale, w2, w2_scale, h, ab, dy, T, K, Nr, Ns, d, I, tile_m,
+                                          seg_offset, row_token, tile_map, n_tiles, ws, dx, dw13, dw2, dw_t, P);
+  if (cs != MOE_OK) return cs;
+  const size_t runs = (size_t)quantize_runs_max((long long)P, Nr + Ns);
+  MOE_REQUIRE(fits31((unsigned long long)runs * d * 4) && fits31((unsigned long long)runs * 2 * I * 4),
+              MOE_EUNSUPPORTED, "backward: operand of 2 GiB or more");
+  const F8Ws L(P, d, I, Nr, Ns);
+  MOE_REQUIRE(ws && ws_bytes >= L.total, MOE_EWORKSPACE, "workspace smaller than moe_gemm_backward_f8_workspace_bytes");
+  const int tiles_max = (int)permute_tiles_max(T, K, Nr, Ns, tile_m);
+  uint8_t* wb = static_cast<uint8_t*>(ws);
+  auto f = [&](size_t o) { return reinterpret_cast<float*>(wb + o); };
+  launch_ffn_bwd_f8(cp<uint16_t>(x), w13, w13_scale, w2, w2_scale, cp<uint16_t>(h), cp<uint16_t>(ab),
+                    cp<uint16_t>(dy), seg_offset, row_token, tile_map, n_tiles, tiles_max, T, (long long)P, d, I, Nr,
+                    Ns, reinterpret_cast<uint16_t*>(wb + L.w8.dab), wb + L.w8.dyq, f(L.w8.dys), wb + L.w8.dabq,
+                    f(L.w8.dabs), wb + L.hr, wb + L.xr, f(L.dyrs), f(L.hrs), f(L.dabrs), f(L.xrs),
+                    reinterpret_cast<int32_t*>(wb + L.run_offset), reinterpret_cast<int*>(wb + L.w8.deal),
+                    static_cast<uint16_t*>(dx), dw13, dw2, dw_t == MOE_F32, as_stream(stream));
+  return launch_status("moe_expert_gemm_backward_f8");
+}
+
+moe_status expert_gemm_backward_w8(const void* x, const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                   const float* w2_scale, const void* h, const void* ab, const void* dy, int T, int K,
+                                   int Nr, int Ns, int d, int I, int tile_m, const int32_t* seg_offset,
+                                   const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles,
+                                   void* ws, size_t ws_bytes, void* dx, void* dw13, void* dw2, moe_dtype dw_t,
+                                   void* stream) {
+  size_t P = 0;
+  const moe_status cs = check_backward_w8(x, w13, w13_scale, w2, w2_scale, h, ab, dy, T, K, Nr, Ns, d, I, tile_m,
+                                          seg_offset, row_token, tile_map, n_tiles, ws, dx, dw13, dw2, dw_t, P);
+  if (cs != MOE_OK) return cs;
   const W8Ws L(P, d, I, Nr);
   MOE_REQUIRE(ws && ws_bytes >= L.total, MOE_EWORKSPACE, "workspace smaller than moe_gemm_backward_w8_workspace_bytes");
   // T == 0 still launches: the weight-gradient kernels write the zeros of

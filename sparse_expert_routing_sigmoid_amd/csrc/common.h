@@ -36,6 +36,8 @@ __device__ __forceinline__ float silu(float a) {
 // Data tensors (activations, weights, outputs, workspaces) are read and
 // written with 16-byte vector accesses.
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// A byte count that a 32-bit buffer offset can address.
+inline bool fits31(unsigned long long bytes) { return bytes < (1ull << 31); }
 
 // Checks the launch status after enqueueing kernels.
 moe_status launch_status(const char* where);

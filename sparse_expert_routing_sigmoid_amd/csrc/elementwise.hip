@@ -320,6 +320,125 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, 
   store8v(out + r * cols + c, v);
 }
 
+// ------------------------------------------------- runs along the rows --
+// E4M3 along the token axis of the permuted layout, the K axis of the weight
+// gradients: segment e (rows seg_offset[e] .. seg_offset[e + 1] - 1) is cut
+// into runs of 128 rows from its first row, the last run shorter, and each
+// column of a run gets its own power-of-two scale (the R10 rule).  Run r of
+// segment e has scale row run_offset[e] + r.  Segment bounds are clamped to
+// [0, P], so any seg_offset keeps every access inside the buffers.
+
+__device__ __forceinline__ void seg_bounds(const int32_t* seg_offset, int e, long long P, int& s0, int& s1) {
+  const int a = seg_offset[e], b = seg_offset[e + 1];
+  s0 = a < 0 ? 0 : (a > P ? (int)P : a);
+  s1 = b < s0 ? s0 : (b > P ? (int)P : b);
+}
+
+// run_offset[e] = sum over e' < e of ceil(len(e') / 128); run_offset[n] the
+// total.  One block: every thread sums a contiguous chunk of segments, then
+// an exclusive scan of the 1024 chunk sums in LDS.
+__global__ __launch_bounds__(1024) void k_run_offsets(const int32_t* __restrict__ seg_offset, int n, long long P,
+                                                      int32_t* __restrict__ run_offset) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x, per = (n + 1023) / 1024;
+  const int e0 = min(t * per, n), e1 = min(e0 + per, n);
+  int sum = 0;
+  for (int e = e0; e < e1; ++e) {
+    int s0, s1;
+    seg_bounds(seg_offset, e, P, s0, s1);
+    sum += (s1 - s0 + 127) / 128;
+  }
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+  for (int e = e0; e < e1; ++e) {
+    run_offset[e] = run;
+    int s0, s1;
+    seg_bounds(seg_offset, e, P, s0, s1);
+    run += (s1 - s0 + 127) / 128;
+  }
+  if (t == 1023) run_offset[n] = part[1023];
+}
+
+// One block per (run, 256-column chunk); thread (rg, cg) = (tid / 32,
+// tid % 32) holds rows 16 rg .. 16 rg + 15 of the run and columns
+// 8 cg .. 8 cg + 7 of the chunk.  The column maxima meet in LDS; codes are
+// RNE(x / scale) as in the tile quantisers.  Source row of permuted row r:
+// row_token[r] (GATHER, x [x_rows, cols]) or r itself (x [P, cols]); a row
+// whose row_token is negative (padding), or names no row of x, counts as
+// zeros, and its codes are written as 0.
+template <typename XT, bool GATHER>
+__global__ __launch_bounds__(256) void k_quant_runs(const XT* __restrict__ x, long long x_rows, int cols,
+                                                    const int32_t* __restrict__ row_token,
+                                                    const int32_t* __restrict__ seg_offset,
+                                                    const int32_t* __restrict__ run_offset, int n, long long P,
+                                                    uint8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float red[8][256];
+  __shared__ int kexp[256];
+  const int g = blockIdx.x;
+  if (g >= run_offset[n]) return;
+  int lo = 0, hi = n;  // run_offset[lo] <= g < run_offset[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (run_offset[mid] <= g) lo = mid; else hi = mid;
+  }
+  int s0, s1;
+  seg_bounds(seg_offset, lo, P, s0, s1);
+  const int row0 = s0 + 128 * (g - run_offset[lo]);
+  const int row_end = min(row0 + 128, s1);
+  const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5;
+  const int c0 = blockIdx.y * 256, col = c0 + 8 * cg;
+  const bool live_col = col < cols;
+  float v[16][8];
+  float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = row0 + 16 * rg + r;
+    long long src = -1;
+    if (live_col && row < row_end) {
+      const int tok = row_token[row];
+      if (tok >= 0) src = GATHER ? (tok < x_rows ? tok : -1) : row;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[r][c] = 0.f;
+    if (src >= 0) load8(x, src * cols + col, v[r]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) am[c] = fmaxf(am[c], fabsf(v[r][c]));
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) red[rg][8 * cg + c] = am[c];
+  __syncthreads();
+  {
+    float m = red[0][tid];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) m = fmaxf(m, red[r][tid]);
+    const int k = pow2_scale_exp(m);
+    kexp[tid] = k;
+    if (c0 + tid < cols) scale[(long long)g * cols + c0 + tid] = exp2_int(k);
+  }
+  __syncthreads();
+  if (!live_col) return;
+  float inv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) inv[c] = exp2_int(-kexp[8 * cg + c]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = row0 + 16 * rg + r;
+    if (row < row_end) {
+      uint2 w;
+      w.x = e4m3x4(v[r][0] * inv[0], v[r][1] * inv[1], v[r][2] * inv[2], v[r][3] * inv[3]);
+      w.y = e4m3x4(v[r][4] * inv[4], v[r][5] * inv[5], v[r][6] * inv[6], v[r][7] * inv[7]);
+      *reinterpret_cast<uint2*>(q + (long long)row * cols + col) = w;
+    }
+  }
+}
+
 }  // namespace
 
 moe_status combine(const void* u, moe_dtype u_t, const void* y, moe_dtype y_t, const int32_t* inv_row,
@@ -417,6 +536,48 @@ moe_status dequantize_tiles(const uint8_t* q, const float* scale, long long rows
     hipLaunchKernelGGL(k_dequant<uint16_t>, grid, dim3(256), 0, st, q, scale, rows, cols, tile_rows,
                        static_cast<uint16_t*>(out));
   return launch_status("fp8_dequantize_tiles");
+}
+
+long long quantize_runs_max(long long P, int n_seg) { return (P + 127LL * n_seg) / 128; }
+
+void launch_quantize_runs(const void* x, bool x_f32, long long x_rows, int cols, const int32_t* row_token,
+                          bool gather, const int32_t* seg_offset, int n_seg, long long P, int32_t* run_offset,
+                          bool offsets, uint8_t* q, float* scale, hipStream_t st) {
+  if (offsets) hipLaunchKernelGGL(k_run_offsets, dim3(1), dim3(1024), 0, st, seg_offset, n_seg, P, run_offset);
+  const long long runs = quantize_runs_max(P, n_seg);
+  if (runs == 0 || cols == 0) return;
+  const dim3 grid((unsigned)runs, (unsigned)((cols + 255) / 256));
+#define QR_LAUNCH(XT, G)                                                                                            \
+  hipLaunchKernelGGL((k_quant_runs<XT, G>), grid, dim3(256), 0, st, static_cast<const XT*>(x), x_rows, cols,       \
+                     row_token, seg_offset, run_offset, n_seg, P, q, scale)
+  if (x_f32) {
+    if (gather) QR_LAUNCH(float, true); else QR_LAUNCH(float, false);
+  } else {
+    if (gather) QR_LAUNCH(uint16_t, true); else QR_LAUNCH(uint16_t, false);
+  }
+#undef QR_LAUNCH
+}
+
+moe_status quantize_runs(const void* x, moe_dtype x_t, long long x_rows, int cols, const int32_t* row_token,
+                         int gather, const int32_t* seg_offset, int n_seg, long long P, int32_t* run_offset,
+                         uint8_t* q, float* scale, void* stream) {
+  MOE_REQUIRE(x_t == MOE_F32 || x_t == MOE_BF16, MOE_EINVAL, "x_t must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(n_seg >= 1 && n_seg <= (1 << 20), MOE_EINVAL, "n_seg out of range");
+  MOE_REQUIRE(P >= 0 && P < (1LL << 31) && cols >= 0 && cols % 128 == 0, MOE_EINVAL,
+              "P must be in [0, 2^31) and cols a multiple of 128");
+  MOE_REQUIRE(x_rows >= 0 && (gather || x_rows >= P), MOE_EINVAL, "x must have P rows unless gathered");
+  MOE_REQUIRE(seg_offset && run_offset && row_token, MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(P == 0 || cols == 0 || (q && scale), MOE_EINVAL, "NULL pointer");
+  // x is read only at rows that exist: none when a gathered x has no rows
+  MOE_REQUIRE(x || cols == 0 || (gather ? x_rows == 0 : P == 0), MOE_EINVAL, "NULL pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(q), MOE_EINVAL, "x and q must be 16-byte aligned");
+  MOE_REQUIRE(fits31((unsigned long long)(gather ? x_rows : P) * cols * (x_t == MOE_F32 ? 4 : 2)) &&
+                  fits31((unsigned long long)P * cols) &&
+                  fits31((unsigned long long)quantize_runs_max(P, n_seg) * cols * 4),
+              MOE_EUNSUPPORTED, "fp8_quantize_runs: operand of 2 GiB or more");
+  launch_quantize_runs(x, x_t == MOE_F32, x_rows, cols, row_token, gather != 0, seg_offset, n_seg, P, run_offset,
+                       true, q, scale, as_stream(stream));
+  return launch_status("fp8_quantize_runs");
 }
 
 void launch_fused_combine_prep(const void* u, moe_dtype u_t, const int32_t* inv_row, const float* topk_gate,

@@ -33,6 +33,10 @@ namespace moe {
 
 moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long long cols, int tile_rows, int tile_cols,
                           uint8_t* q, float* scale, void* stream);
+long long quantize_runs_max(long long P, int n_seg);
+void launch_quantize_runs(const void* x, bool x_f32, long long x_rows, int cols, const int32_t* row_token,
+                          bool gather, const int32_t* seg_offset, int n_seg, long long P, int32_t* run_offset,
+                          bool offsets, uint8_t* q, float* scale, hipStream_t st);
 
 namespace {
 
@@ -742,14 +746,18 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
 // ------------------------------------------------------------- wgrad --
 constexpr int WG_STORES = 32;  // buffer stores per wave for one bf16 result tile
 
+// Every wait for a stage's loads is a full vmcnt(0): the counter is shared
+// with the result stores, and loads and stores in flight together may
+// retire out of order, so a partial count does not tell that the older
+// loads have landed.
+
 // One pair of stages of a wgrad K loop.  On entry st0 holds stage s
 // (complete and visible) and the loads of stage s + 1 into st1 are in
-// flight, issued before the last `pending` global accesses of this wave;
-// `tok` holds the tokens of stage (s + 2) % nk.  Each buffer is refilled as
-// soon as every wave has read it: with the stage after next of this N tile,
-// or past its last stage the first stages of the next N tile of the run
-// (zeros after the last).
-template <int PENDING, bool GATHER>
+// flight; `tok` holds the tokens of stage (s + 2) % nk.  Each buffer is
+// refilled as soon as every wave has read it: with the stage after next of
+// this N tile, or past its last stage the first stages of the next N tile
+// of the run (zeros after the last).
+template <bool GATHER>
 __device__ __forceinline__ void wgrad_pair(f32x16_t (&acc)[4][4], SegRows<GATHER, 8>& S, uint8_t* __restrict__ st0,
                                            uint8_t* __restrict__ st1, const MncLane& mla, const MncLane& mlb, int wm,
                                            int wn, int lane, int w_wave, int s, int nk, uint32_t bc, bool more) {
@@ -757,7 +765,7 @@ __device__ __forceinline__ void wgrad_pair(f32x16_t (&acc)[4][4], SegRows<GATHER
   const uint32_t bn = wrap ? bc + BT * 2u : bc;
   const bool live = !wrap || more;
   mma_stage<false, false>(acc, st0, st0 + BOP, mla, mlb, wm, wn, lane);
-  vm_wait<PENDING>();
+  vm_wait<0>();
   lds_barrier();
   S.issue(st0, st0 + BOP, w_wave, lane, wrap ? 0 : s + 2, bn, live);
   S.fetch(wrap ? 1 : s + 3, w_wave, lane);
@@ -771,9 +779,8 @@ __device__ __forceinline__ void wgrad_pair(f32x16_t (&acc)[4][4], SegRows<GATHER
 // The K loops and result tiles of one wgrad item (see k_wgrad).  bf16 result
 // tiles leave through a third LDS buffer (stq, 32 KB) in four quarters of 64
 // rows, so both stage buffers keep loading meanwhile: the tile's stores are
-// issued after the loads of the next tile's first two stages and only the
-// wait for the second of those (vmcnt counts in issue order) lets them
-// drain, a whole stage of MFMAs later.
+// issued after the loads of the next tile's first two stages and drain
+// during the first stage of MFMAs of the next tile.
 template <bool GATHER, typename OT>
 __device__ __forceinline__ void wgrad_run(SegRows<GATHER, 8>& S, uint8_t* __restrict__ st0, uint8_t* __restrict__ st1,
                                           uint8_t* __restrict__ stq, const MncLane& mla, const MncLane& mlb, int wm,
@@ -802,10 +809,8 @@ __device__ __forceinline__ void wgrad_run(SegRows<GATHER, 8>& S, uint8_t* __rest
     // and a reload from scratch would wait for the stores.
     int s0 = 0;
     asm volatile("" : "+s"(s0));
-    if (nk > 0)
-      wgrad_pair<BF16 ? WG_STORES : 0>(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s0, nk, bc, more);
-    for (int s = 2; s < nk; s += 2)
-      wgrad_pair<0>(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s, nk, bc, more);
+    if (nk > 0) wgrad_pair(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s0, nk, bc, more);
+    for (int s = 2; s < nk; s += 2) wgrad_pair(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s, nk, bc, more);
     // (see mma16 for the accumulator layout)
     if constexpr (BF16) {
       // quarter qq: rows 64 qq .. 64 qq + 63 of the tile, held by the waves
@@ -883,6 +888,40 @@ __global__ __launch_bounds__(1024) void k_wgrad_deal(const int32_t* __restrict__
   }
 }
 
+// The item of this block in a weight-gradient grid: (expert e, M tile m, N
+// tiles n0 .. n1 - 1).  Block b runs on XCD b % 8.  XCD x takes every 8th
+// shared item (from x), one N tile each, then all items of its routed
+// experts (k_wgrad_deal: shares of like row counts), runs of nch N tiles, so
+// the blocks that share an expert's rows run together in one L2.  False: the
+// block has no item.
+__device__ __forceinline__ bool wgrad_item(int E, int Nr, int ntm, int ntn, int nch, const int* __restrict__ deal,
+                                           int& e, int& m, int& n0, int& n1) {
+  const int runs = (ntn + nch - 1) / nch;  // runs of a routed expert's M tile
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int shared_items = (E - Nr) * ntm * ntn;
+  const int my_shared = shared_items > x ? (shared_items - x + 7) / 8 : 0;
+  if (slot < my_shared) {
+    const int item = x + 8 * slot;
+    e = Nr + item / (ntm * ntn);
+    const int rem = item % (ntm * ntn);
+    m = rem / ntn;
+    n0 = rem % ntn;
+    n1 = n0 + 1;
+    return true;
+  }
+  const int r = slot - my_shared, i = r / (ntm * runs), S = (Nr + 7) / 8;
+  // the grid gives every XCD ceil(shared items / 8) shared slots: an XCD
+  // with one shared item fewer has one slot past its list (i == S)
+  if (i >= S) return false;
+  e = deal[x * S + i];
+  if (e < 0) return false;
+  const int rem = r % (ntm * runs);
+  m = rem / runs;
+  n0 = (rem % runs) * nch;
+  n1 = min(n0 + nch, ntn);
+  return true;
+}
+
 // dW_e [M, N] = A_e^T B_e over the K-rows of segment e.  An item is (expert,
 // M tile, run of N tiles): one block computes the N tiles of the run one
 // after the other with the same K-rows (the tokens are fetched once per
@@ -905,35 +944,8 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
   __shared__ __attribute__((aligned(1024))) uint8_t stq[BOP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int ntm = (Md + BT - 1) / BT, ntn = (Nd + BT - 1) / BT;
-  const int runs = (ntn + nch - 1) / nch;  // runs of a routed expert's M tile
-  // Block b runs on XCD b % 8.  XCD x takes every 8th shared item (from x),
-  // then all items of its routed experts (k_wgrad_deal: shares of like row
-  // counts), so the blocks that share an expert's rows run together in one
-  // L2.
-  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int shared_items = (E - Nr) * ntm * ntn;
-  const int my_shared = shared_items > x ? (shared_items - x + 7) / 8 : 0;
   int e, m, n0, n1;
-  if (slot < my_shared) {
-    const int item = x + 8 * slot;
-    e = Nr + item / (ntm * ntn);
-    const int rem = item % (ntm * ntn);
-    m = rem / ntn;
-    n0 = rem % ntn;
-    n1 = n0 + 1;
-  } else {
-    const int r = slot - my_shared, i = r / (ntm * runs), S = (Nr + 7) / 8;
-    // the grid gives every XCD ceil(shared items / 8) shared slots: an XCD
-    // with one shared item fewer has one slot past its list (i == S)
-    if (i >= S) return;
-    e = deal[x * S + i];
-    if (e < 0) return;
-    const int rem = r % (ntm * runs);
-    m = rem / runs;
-    n0 = (rem % runs) * nch;
-    n1 = min(n0 + nch, ntn);
-  }
+  if (!wgrad_item(E, Nr, (Md + BT - 1) / BT, (Nd + BT - 1) / BT, nch, deal, e, m, n0, n1)) return;
   const int w_wave = __builtin_amdgcn_readfirstlane(wave);
 
   SegRows<GATHER, 8> S;
@@ -962,6 +974,302 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
 unsigned wgrad_grid(int Nr, int Ns, int ntm, int ntn, int nch) {
   const long long per_xcd = ceil_div((long long)Ns * ntm * ntn, 8) + ceil_div(Nr, 8) * (long long)ntm * ceil_div(ntn, nch);
   return (unsigned)(8 * per_xcd);
+}
+
+// ------------------------------------------------------------ E4M3 wgrad --
+// dW_e [M, N] = sum over the rows k of segment e of A[k, :]^T B[k, :] with
+// both operands E4M3 codes in the permuted layout (A [P, M], B [P, N];
+// padding rows hold code 0) and fp32 power-of-two scales per column and run
+// of 128 rows of the segment: scale row run_offset[e] + r of [runs, M] and
+// [runs, N], as fp8_quantize_runs writes them.  A stage is one run: 128
+// K-rows x 256 columns of each operand, staged M/N-contiguous as the E4M3
+// dgrad's weight tiles (MncRows8 layout) and read on both sides with the
+// transposing 8-bit LDS read (frag_mnc8), plus the run's scales of the
+// tile's 256 + 256 columns.  A fragment lane holds one column (l % 32 of its
+// group) for all 64 K of a k-step, all in one run, so the scale of that
+// column goes to the matrix instruction per lane as its E8M0 exponent.
+constexpr int SC8 = 2 * BOP;             // offset of the A scales in a stage (B scales follow)
+constexpr int ST8 = 2 * BOP + 2 * 1024;  // bytes of a stage
+
+struct RunRows8 {
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+  int seglen, run0, kr0;
+  uint32_t Md, Nd, a_c;   // row bytes of A and B, first column of the A tile
+  uint32_t ao[8], bo[8];  // byte offsets of the lane's K-row of load j at run 0 (B: tile column 0)
+  // Scale block layout: the scales of tile columns 128 h + 32 i + r
+  // (i = 0..3) sit together at float 4 (32 h + r) + i, so a fragment lane
+  // reads its four with one 16-byte read.  Lane l of wave w loads float
+  // 64 w + l, i.e. column sc_col.
+  uint32_t sc_col;
+  // Block g = 8 w + j (1 KB) of each operand's stage buffer holds K-rows
+  // 4 g .. 4 g + 3: lane l loads K-row kr0 + 4 j (kr0 = 32 w + l / 16),
+  // physical chunk l % 16.
+  __device__ void init(int seg0, int wave, int lane) {
+    kr0 = 32 * wave + (lane >> 4);
+    sc_col = (uint32_t)((wave >> 1) * 128 + (lane & 3) * 32 + (wave & 1) * 16 + (lane >> 2));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kr = kr0 + 4 * j;
+      const uint32_t c16 = (uint32_t)((lane & 15) ^ f8_sw(kr & 7)) * 16u;
+      ao[j] = (uint32_t)(seg0 + kr) * Md + a_c + c16;
+      bo[j] = (uint32_t)(seg0 + kr) * Nd + c16;
+    }
+  }
+  // Stage s (run s of the segment) of the N tile whose first column is b_c
+  // into st, then the scales of either tile (wave w fills bytes
+  // 256 w .. 256 w + 255 of each scale block, see sc_col).  18 global
+  // accesses per wave; K-rows past the segment,
+  // and every access of a stage that is not live, get an offset with bit 31
+  // set, past the buffer, and load zeros (no branch).
+  __device__ void issue(uint8_t* st, int wave, int lane, int s, uint32_t b_c, bool live) const {
+    const int lim = live ? seglen - s * 128 : 0;  // K-rows kr < lim are live
+    const uint32_t sa = (uint32_t)s * 128u * Md, sb = (uint32_t)s * 128u * Nd + b_c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t oob = ((uint32_t)(kr0 + 4 * j - lim) & 0x80000000u) ^ 0x80000000u;
+      dma16(ra, st + (wave * 8 + j) * 1024, (ao[j] + sa) | oob, 0);
+      dma16(rb, st + BOP + (wave * 8 + j) * 1024, (bo[j] + sb) | oob, 0);
+    }
+    const uint32_t run = (uint32_t)(run0 + s);
+    const uint32_t soob = live ? 0u : OOB;
+    const uint32_t ca = a_c + sc_col, cb = b_c + sc_col;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + SC8 + wave * 256), 4, ((run * Md + ca) * 4u) | soob,
+                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + SC8 + 1024 + wave * 256), 4,
+                                             ((run * Nd + cb) * 4u) | soob, 0, 0, 0);
+  }
+};
+constexpr int RUN8_ACCESSES = 18;  // global accesses of RunRows8::issue per wave
+
+// The two k-steps (64 K-rows each) of one stage.
+__device__ __forceinline__ void mma_run8(f32x16_t (&acc)[4][4], const uint8_t* st, const MncLane8& mla,
+                                         const MncLane8& mlb, int wm, int wn, int lane) {
+  const float4 fa = *reinterpret_cast<const float4*>(st + SC8 + 16 * (wm * 32 + (lane & 31)));
+  const float4 fb = *reinterpret_cast<const float4*>(st + SC8 + 1024 + 16 * (wn * 32 + (lane & 31)));
+  const int ea[4] = {e8m0_of(fa.x), e8m0_of(fa.y), e8m0_of(fa.z), e8m0_of(fa.w)};
+  const int eb[4] = {e8m0_of(fb.x), e8m0_of(fb.y), e8m0_of(fb.z), e8m0_of(fb.w)};
+  const uint8_t* ta = st;
+  const uint8_t* tb = st + BOP;
+  i32x8_t a0[4], b0[4], a1[4], b1[4];
+  a0[0] = frag_mnc8<0, 0>(ta, mla);
+  a0[1] = frag_mnc8<1, 0>(ta, mla);
+  a0[2] = frag_mnc8<2, 0>(ta, mla);
+  a0[3] = frag_mnc8<3, 0>(ta, mla);
+  b0[0] = frag_mnc8<0, 0>(tb, mlb);
+  b0[1] = frag_mnc8<1, 0>(tb, mlb);
+  b0[2] = frag_mnc8<2, 0>(tb, mlb);
+  b0[3] = frag_mnc8<3, 0>(tb, mlb);
+  a1[0] = frag_mnc8<0, 1>(ta, mla);
+  a1[1] = frag_mnc8<1, 1>(ta, mla);
+  a1[2] = frag_mnc8<2, 1>(ta, mla);
+  a1[3] = frag_mnc8<3, 1>(ta, mla);
+  b1[0] = frag_mnc8<0, 1>(tb, mlb);
+  b1[1] = frag_mnc8<1, 1>(tb, mlb);
+  b1[2] = frag_mnc8<2, 1>(tb, mlb);
+  b1[3] = frag_mnc8<3, 1>(tb, mlb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0[j], a0[i], acc[i][j], 0, 0, 0, eb[j], 0, ea[i]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1[j], a1[i], acc[i][j], 0, 0, 0, eb[j], 0, ea[i]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// A result tile of one wave (its 128 x 128, see mma16 for the accumulator
+// layout; r0, c0: output row and column of its element 0).  bf16: through
+// the wave's own 4 KB of LDS, 16 rows at a time (16-byte chunk c of row r at
+// chunk c ^ r; written with lds_st64, which the compiler does not order
+// against the direct-to-LDS loads), read back as whole 256-byte rows and
+// stored with non-temporal buffer stores, 4 rows per instruction, 32 in
+// all; no workgroup barrier.  Columns past Nd are out of range.  fp32:
+// straight from the accumulators.
+template <typename OT>
+__device__ __forceinline__ void wgrad8_store(const f32x16_t (&acc)[4][4], uint8_t* stw,
+                                             OT* ob, int Md, int Nd, int r0, int c0, int lane) {
+  if constexpr (sizeof(OT) == 2) {
+    const __amdgpu_buffer_rsrc_t ro = rsrc(ob, (uint32_t)Md * (uint32_t)Nd * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (((lane >> 4) & 1) == half) {
+          const int rho = lane & 15;
+          uint8_t* rp = stw + rho * 256 + 8 * (lane >> 5);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int chunk = j * 4 + q;
+              const float4 v = acc_get4(acc[i][j], q);
+              lds_st64(rp + ((chunk ^ rho) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+            }
+        }
+        // the rows are read back by other lanes: the wave's LDS writes must
+        // have completed (measured: without this wait the reads can see
+        // the previous round's data)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * r + (lane >> 4), chunk = lane & 15;
+          const uint4 v = *reinterpret_cast<const uint4*>(stw + row * 256 + ((chunk ^ row) << 4));
+          const int grow = r0 + i * 32 + half * 16 + row, gcol = c0 + chunk * 8;
+          const uint32_t off = gcol < Nd ? ((uint32_t)grow * (uint32_t)Nd + (uint32_t)gcol) * 2u : OOB;
+          typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+          const u32x4_t w = {v.x, v.y, v.z, v.w};
+          __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 2);  // 2: non-temporal
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + i * 32 + (lane & 31);
+      if (r >= Md) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = c0 + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
+        }
+    }
+  }
+}
+
+// The next stage to load: N tile ln, run ls.
+struct Run8Next {
+  int ln, ls;
+};
+
+// One stage of an item's sequence (N tiles n0 .. n1 - 1, nk runs each) in
+// st: multiply it, wait for the next stage (in the other buffer) and for
+// every wave to be done with st, then load the stage after next into st.
+// The wait is a full vmcnt(0) (see the wgrad notes above): on the first
+// stage of a tile it also drains the previous tile's stores, issued after
+// the loads it waits for.
+__device__ __forceinline__ void wgrad8_step(f32x16_t (&acc)[4][4], uint8_t* st, const RunRows8& S,
+                                            const MncLane8& mla, const MncLane8& mlb, Run8Next& nx, int n1, int nk,
+                                            int wm, int wn, int lane, int w_wave) {
+  mma_run8(acc, st, mla, mlb, wm, wn, lane);
+  vm_wait<0>();
+  lds_barrier();
+  S.issue(st, w_wave, lane, nx.ls, (uint32_t)nx.ln * BT, nx.ln < n1);
+  if (++nx.ls == nk) {
+    nx.ls = 0;
+    ++nx.ln;
+  }
+}
+
+// The nk stages of one N tile (ODD: nk is odd), the first in bufa, then
+// alternating.  Every call site names a fixed buffer (no pointer chosen at
+// run time), so the compiler knows which buffer each load in flight writes
+// and lets the fragment reads of the other one go ahead.
+template <bool ODD>
+__device__ __forceinline__ void wgrad8_tile(f32x16_t (&acc)[4][4], uint8_t* bufa, uint8_t* bufb, const RunRows8& S,
+                                            const MncLane8& mla, const MncLane8& mlb, Run8Next& nx, int n1, int nk,
+                                            int wm, int wn, int lane, int w_wave) {
+  zero_acc(acc);
+  int s = 0;
+  if constexpr (ODD) {
+    wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+    for (s = 1; s < nk; s += 2) {
+      wgrad8_step(acc, bufb, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+    }
+  } else {
+    for (s = 0; s < nk; s += 2) {
+      wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_step(acc, bufb, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+    }
+  }
+}
+
+// The item (expert e, M tile m, N tiles n0 .. n1 - 1) of the E4M3 weight
+// gradient, grid and item order as k_wgrad's:
+//   down:    A = R(dy) [P, d], B = R(h) [P, I]          -> dW2 [E, d, I]
+//   gate/up: A = R([da | db]) [P, 2I], B = R(x) [P, d]  -> dW13 [E, 2I, d]
+// (R: runs of 128 rows per column, reading B5; x already gathered into the
+// permuted rows by the quantiser).
+template <typename OT>
+__global__ __launch_bounds__(BTHREADS) void k_wgrad8(const uint8_t* __restrict__ a, const float* __restrict__ as,
+                                                     const uint8_t* __restrict__ b, const float* __restrict__ bs,
+                                                     const int32_t* __restrict__ seg_offset,
+                                                     const int32_t* __restrict__ run_offset, int E, int Nr, int Md,
+                                                     int Nd, int nch, uint32_t a_bytes, uint32_t b_bytes,
+                                                     uint32_t as_bytes, uint32_t bs_bytes,
+                                                     const int* __restrict__ deal, OT* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[ST8];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[ST8];
+  __shared__ __attribute__((aligned(1024))) uint8_t stq[4 * 4096];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int e, m, n0, n1;
+  if (!wgrad_item(E, Nr, Md / BT, (Nd + BT - 1) / BT, nch, deal, e, m, n0, n1)) return;
+  const int w_wave = __builtin_amdgcn_readfirstlane(wave);
+
+  RunRows8 S;
+  S.ra = rsrc(a, a_bytes);
+  S.rb = rsrc(b, b_bytes);
+  S.rsa = rsrc(as, as_bytes);
+  S.rsb = rsrc(bs, bs_bytes);
+  const int seg0 = seg_offset[e];
+  S.seglen = seg_offset[e + 1] - seg0;
+  S.run0 = run_offset[e];
+  S.Md = (uint32_t)Md;
+  S.Nd = (uint32_t)Nd;
+  S.a_c = (uint32_t)m * BT;
+  S.init(seg0, w_wave, lane);
+
+  MncLane8 mla, mlb;
+  mla.init(wm, lane);
+  mlb.init(wn, lane);
+  uint8_t* stw = stq + w_wave * 4096;
+  OT* ob = out + (long long)e * Md * Nd;
+  const int nk = S.seglen > 0 ? (S.seglen + 127) / 128 : 0;
+  f32x16_t acc[4][4];
+  if (nk == 0) {  // no rows: zero tiles
+    zero_acc(acc);
+    for (int n = n0; n < n1; ++n) wgrad8_store(acc, stw, ob, Md, Nd, m * BT + wm * 128, n * BT + wn * 128, lane);
+    vm_wait<0>();
+    return;
+  }
+  // the first two stages (the second may be the first of the next tile)
+  S.issue(st0, w_wave, lane, 0, (uint32_t)n0 * BT, true);
+  Run8Next nx{nk > 1 ? n0 : n0 + 1, nk > 1 ? 1 : 0};
+  S.issue(st1, w_wave, lane, nx.ls, (uint32_t)nx.ln * BT, nx.ln < n1);
+  if (++nx.ls == nk) {
+    nx.ls = 0;
+    ++nx.ln;
+  }
+  vm_wait<RUN8_ACCESSES>();
+  lds_barrier();
+  const int r0 = m * BT + wm * 128, c0 = wn * 128;
+  if ((nk & 1) == 0) {
+    for (int n = n0; n < n1; ++n) {
+      wgrad8_tile<false>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + n * BT, lane);
+    }
+  } else {
+    // an odd tile ends in the buffer it began with: the next one begins in
+    // the other, so tiles go in pairs
+    int n = n0;
+    for (; n + 1 < n1; n += 2) {
+      wgrad8_tile<true>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + n * BT, lane);
+      wgrad8_tile<true>(acc, st1, st0, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + (n + 1) * BT, lane);
+    }
+    if (n < n1) {
+      wgrad8_tile<true>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + n * BT, lane);
+    }
+  }
+  vm_wait<0>();
 }
 
 }  // namespace
@@ -1029,16 +1337,14 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
 // d <= 16384 and I <= 8192: a lane holds the block scales of two K blocks.
 bool ffn_bwd_w8_ok(int d, int I) { return ffn_bwd_ok(d, I) && d / 128 <= 128 && 2 * I / 128 <= 128; }
 
-// As launch_ffn_bwd_bf16 with the two dgrad products in E4M3: dy and then
-// [da | db] are quantised in 1x128 tiles (dyq/dys, dabq/dabs scratch), the
-// weights come as E4M3 codes with 128x128 block scales.  The wgrads stay
-// bf16 (dy and [da | db] unquantised).
-void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
-                       const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
-                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
-                       int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
-                       uint8_t* dabq, float* dabs, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
-                       hipStream_t st) {
+// The two dgrad products in E4M3: dy and then [da | db] are quantised in
+// 1x128 tiles (dyq/dys, dabq/dabs scratch), the weights come as E4M3 codes
+// with 128x128 block scales; dab gets [da | db] (bf16), dx the input
+// gradient.
+static void launch_dgrads8(const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
+                           const uint16_t* ab, const uint16_t* dy, const int32_t* tile_map, const int32_t* n_tiles,
+                           int tiles_max, int T, long long P, int d, int I, uint16_t* dab, uint8_t* dyq, float* dys,
+                           uint8_t* dabq, float* dabs, uint16_t* dx, hipStream_t st) {
   // with no tokens every row is padding: nothing to quantise (and dy may be NULL)
   if (T > 0) quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
   {
@@ -1055,7 +1361,68 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        tile_map, n_tiles, 2 * I, d, (uint32_t)(P * 2 * I), (uint32_t)(P * (2 * I / 128) * 4), nullptr,
                        dx);
   }
+}
+
+// As launch_ffn_bwd_bf16 with the two dgrad products in E4M3
+// (launch_dgrads8).  The wgrads stay bf16 (dy and [da | db] unquantised).
+void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
+                       const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
+                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
+                       int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
+                       uint8_t* dabq, float* dabs, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                       hipStream_t st) {
+  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
+                 st);
   launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, deal, dw13, dw2, dw_f32, st);
+}
+
+// As launch_ffn_bwd_w8 with the weight gradients on E4M3 operands too
+// (reading B5): after the dgrads, dy, h, [da | db] and the gathered x are
+// quantised in runs of 128 rows per column (the codes of dy and [da | db]
+// overwrite dyq and dabq, which the dgrads no longer need; hr, xr, the four
+// run-scale arrays [runs, C] and run_offset [Nr + Ns + 1] are scratch), then
+// k_wgrad8 makes dW2 and dW13.
+void launch_ffn_bwd_f8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
+                       const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
+                       const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
+                       int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
+                       uint8_t* dabq, float* dabs, uint8_t* hr, uint8_t* xr, float* dyrs, float* hrs, float* dabrs,
+                       float* xrs, int32_t* run_offset, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                       hipStream_t st) {
+  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
+                 st);
+  const int E = Nr + Ns;
+  launch_quantize_runs(dy, false, P, d, row_token, false, seg_offset, E, P, run_offset, true, dyq, dyrs, st);
+  launch_quantize_runs(h, false, P, I, row_token, false, seg_offset, E, P, run_offset, false, hr, hrs, st);
+  launch_quantize_runs(dab, false, P, 2 * I, row_token, false, seg_offset, E, P, run_offset, false, dabq, dabrs, st);
+  launch_quantize_runs(x, false, T, d, row_token, true, seg_offset, E, P, run_offset, false, xr, xrs, st);
+  hipLaunchKernelGGL(k_wgrad_deal, dim3(1), dim3(1024), 0, st, seg_offset, Nr, deal);
+  const long long runs = quantize_runs_max(P, E);
+  const int nch = 4;
+  {
+    const int ntm = d / BT, ntn = (I + BT - 1) / BT;
+    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
+    const uint32_t ab_ = (uint32_t)(P * d), bb = (uint32_t)(P * I), asb = (uint32_t)(runs * d * 4),
+                   bsb = (uint32_t)(runs * I * 4);
+    if (dw_f32)
+      hipLaunchKernelGGL((k_wgrad8<float>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dyrs, hr, hrs, seg_offset,
+                         run_offset, E, Nr, d, I, nch, ab_, bb, asb, bsb, deal, static_cast<float*>(dw2));
+    else
+      hipLaunchKernelGGL((k_wgrad8<uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dyrs, hr, hrs, seg_offset,
+                         run_offset, E, Nr, d, I, nch, ab_, bb, asb, bsb, deal, static_cast<uint16_t*>(dw2));
+  }
+  {
+    const int ntm = 2 * I / BT, ntn = d / BT;
+    const unsigned grid = wgrad_grid(Nr, Ns, ntm, ntn, nch);
+    const uint32_t ab_ = (uint32_t)(P * 2 * I), bb = (uint32_t)(P * d), asb = (uint32_t)(runs * 2 * I * 4),
+                   bsb = (uint32_t)(runs * d * 4);
+    if (dw_f32)
+      hipLaunchKernelGGL((k_wgrad8<float>), dim3(grid), dim3(BTHREADS), 0, st, dabq, dabrs, xr, xrs, seg_offset,
+                         run_offset, E, Nr, 2 * I, d, nch, ab_, bb, asb, bsb, deal, static_cast<float*>(dw13));
+    else
+      hipLaunchKernelGGL((k_wgrad8<uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dabq, dabrs, xr, xrs, seg_offset,
+                         run_offset, E, Nr, 2 * I, d, nch, ab_, bb, asb, bsb, deal, static_cast<uint16_t*>(dw13));
+  }
 }
 
 }  // namespace moe

@@ -17,7 +17,8 @@ HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z0-9_]+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?(?:(?:unsigned|signed|long)\s+)*[A-Za-z_][A-Za-z0-9_]*(?:\s+|\s*\*+\s*)"
+                       r"([a-z0-9_]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
@@ -32,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = M.lib()
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     assert L.moe_status_str(0) == b"MOE_OK"
     assert L.moe_status_str(3) == b"MOE_EWORKSPACE"
 
@@ -188,6 +189,32 @@ def test_backward_entry_points_reject_bad_arguments():
     need8 = M.moe_gemm_backward_w8_workspace_bytes(T, K, Nr, Ns, d, I, tm)
     assert need8 >= P * 2 * I * 2 + P * 2 * I + P * d + P * (2 * I + d) // 128 * 4
     assert g8(wsb=need8 - 1)[0] == M.MOE_EWORKSPACE
+    f8 = lambda **kw: _status(L.moe_expert_gemm_backward_f8, *[kw.get(k, v) for k, v in dict(
+        x=F, w13=F, w13s=F, w2=F, w2s=F, h=F, ab=F, dy=F, T=T, K=K, Nr=Nr, Ns=Ns, d=d, I=I, tm=tm, so=F, rt=F,
+        tmap=F, nt=F, ws=F, wsb=big, dx=F, dw13=F, dw2=F, dwt=M.MOE_BF16, st=None).items()])
+    assert f8(I=192)[0] == M.MOE_EUNSUPPORTED
+    assert f8(d=16640)[0] == M.MOE_EUNSUPPORTED
+    assert f8(w13s=None)[0] == M.MOE_EINVAL
+    assert f8(dwt=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    assert f8(h=ctypes.c_void_p(0x1008))[0] == M.MOE_EINVAL   # misaligned
+    need_f8 = M.moe_gemm_backward_f8_workspace_bytes(T, K, Nr, Ns, d, I, tm)
+    runs = M.fp8_quantize_runs_max(P, Nr + Ns)
+    assert runs == (P + 127 * (Nr + Ns)) // 128
+    # the E4M3 dgrad workspace, the run codes of h and x, four run-scale arrays
+    assert need_f8 >= need8 + P * (I + d) + runs * (2 * d + 3 * I) * 4 + (Nr + Ns + 1) * 4
+    assert f8(wsb=need_f8 - 1)[0] == M.MOE_EWORKSPACE
+    assert M.moe_gemm_backward_f8_workspace_bytes(-1, K, Nr, Ns, d, I, tm) == 0
+    qr = lambda **kw: _status(L.fp8_quantize_runs, *[kw.get(k, v) for k, v in dict(
+        x=F, xt=M.MOE_BF16, xr=P, cols=d, rt=F, g=0, so=F, n=Nr + Ns, P=P, ro=F, q=F, sc=F, st=None).items()])
+    assert qr(cols=200)[0] == M.MOE_EINVAL               # cols % 128 != 0
+    assert qr(xt=M.MOE_E4M3)[0] == M.MOE_EINVAL
+    assert qr(n=0)[0] == M.MOE_EINVAL
+    assert qr(xr=P - 1)[0] == M.MOE_EINVAL              # x has fewer rows than the layout
+    assert qr(xr=8, g=1, so=None)[0] == M.MOE_EINVAL
+    assert qr(P=-1)[0] == M.MOE_EINVAL
+    assert qr(q=ctypes.c_void_p(0x1004))[0] == M.MOE_EINVAL
+    assert qr(cols=1 << 20, P=1 << 20, xr=1 << 20)[0] == M.MOE_EUNSUPPORTED
+    assert M.fp8_quantize_runs_max(-5, 3) == 0
     gt = lambda **kw: _status(L.moe_expert_gemm_train, *[kw.get(k, v) for k, v in dict(
         x=F, w13=F, w2=F, T=T, K=K, Nr=Nr, Ns=Ns, d=d, I=I, tm=tm, so=F, rt=F, tmap=F, nt=F, ws=F, wsb=big,
         h=F, ab=F, y=F, yt=M.MOE_BF16, st=None).items()])

@@ -106,17 +106,18 @@ TRAIN_CASES = {
 
 @pytest.mark.parametrize("name", list(TRAIN_CASES))
 def test_fp8_training_step_matches_oracle(name):
-    """MoeLayer(train=True, x_fp8=True, E4M3 weights): the E4M3 training
-    forward (keeping [a|b] and the E4M3 h in bf16) and the backward with E4M3
-    input-gradient products, against layer_backward(fp8_train=True) on the
-    oracle's own 128x128 quantisation of the same bf16 weights."""
+    """MoeLayer(train=True, x_fp8=True, E4M3 weights, wgrad_fp8=False): the
+    E4M3 training forward (keeping [a|b] and the E4M3 h in bf16) and the
+    backward with E4M3 input-gradient products and bf16 weight gradients
+    (moe_expert_gemm_backward_w8), against layer_backward(fp8_train=True) on
+    the oracle's own 128x128 quantisation of the same bf16 weights."""
     from oracle.e4m3 import dequantize_tiles, quantize_tiles
     cfg = TRAIN_CASES[name]
     print(f"fp8 training step parity {name}: {cfg}", flush=True)
     w13, w2 = W.make_expert_weights(cfg, "cuda")
     w8 = M.quantize_weights(w13, w2)
     layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True, tile_m=32,
-                       train=True)
+                       train=True, wgrad_fp8=False)
     plain = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True, tile_m=32)
     u, e, b = W.make_tokens(cfg, 0, "cuda"), W.make_centroids(cfg, "cuda"), W.make_bias(cfg, "cuda")
     out = layer.forward(u, e, b).clone()
@@ -182,7 +183,7 @@ def test_fp8_training_step_single_token():
     w13, w2 = W.make_expert_weights(cfg, "cuda")
     w8 = M.quantize_weights(w13, w2)
     layer = M.MoeLayer(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.K, torch.bfloat16, w8, x_fp8=True, tile_m=32,
-                       train=True)
+                       train=True, wgrad_fp8=False)
     u, e, b = W.make_tokens(cfg, 0, "cuda"), W.make_centroids(cfg, "cuda"), W.make_bias(cfg, "cuda")
     layer.forward(u, e, b)
     G = W.make_free((cfg.T, cfg.d), 1.0, 103, "cuda", torch.bfloat16)
