@@ -395,22 +395,41 @@ __global__ __launch_bounds__(256) void k_quant_runs(const XT* __restrict__ x, lo
   const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5;
   const int c0 = blockIdx.y * 256, col = c0 + 8 * cg;
   const bool live_col = col < cols;
-  float v[16][8];
-  float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // Every load is issued unconditionally (a row that has no source reads
+  // a row that exists and is zeroed after), so the 16 row_token loads and
+  // then the 16 data loads of a thread are in flight together; loads under
+  // a per-row branch were issued and waited for one at a time.
+  int tok[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = row0 + 16 * rg + r;
-    long long src = -1;
-    if (live_col && row < row_end) {
-      const int tok = row_token[row];
-      if (tok >= 0) src = GATHER ? (tok < x_rows ? tok : -1) : row;
-    }
+    tok[r] = row_token[row < row_end ? row : row_end - 1];
+  }
+  // a gathered x without rows is never read (it may be NULL)
+  const bool readable = !GATHER || x_rows > 0;
+  const int ccol = live_col ? col : 0;
+  float v[16][8];
+  if (readable) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[r][c] = 0.f;
-    if (src >= 0) load8(x, src * cols + col, v[r]);
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + 16 * rg + r;
+      const bool ok = live_col && row < row_end && tok[r] >= 0 && (!GATHER || tok[r] < x_rows);
+      const long long src = ok ? (GATHER ? (long long)tok[r] : (long long)row) : (GATHER ? 0LL : (long long)row0);
+      load8(x, src * cols + ccol, v[r]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[r][c] = ok ? v[r][c] : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[r][c] = 0.f;
+  }
+  float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
 #pragma unroll
     for (int c = 0; c < 8; ++c) am[c] = fmaxf(am[c], fabsf(v[r][c]));
-  }
 #pragma unroll
   for (int c = 0; c < 8; ++c) red[rg][8 * cg + c] = am[c];
   __syncthreads();

@@ -597,6 +597,37 @@ __device__ __forceinline__ void mma_stage8(f32x16_t (&acc)[4][4], const uint8_t*
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Item order of the dgrad kernels.  The items (row tile, N tile) of one
+// expert fill the same range of the item list in any order, since its row
+// tiles are contiguous in the tile map.  Inside that range they run in
+// groups of up to `grp` row tiles, N-tile major within a group.  The blocks
+// of one XCD that run at the same time (about 32, one per CU) then hold up
+// to `grp` row tiles of a few N tiles, so each weight slab is read by several
+// row tiles together and meets them in L2.  grp = 1 is the tile-major order
+// (all N tiles of one row tile, then the next), which already holds 32 / ntn
+// row tiles at once; with many N tiles (N = d) it holds about one, and each
+// row tile streams the expert's weights from memory again.  dgrad_group
+// picks grp from the N-tile count (measured at d = 7168, I = 2048: groups of
+// 8 cut the gate/up dgrad by 6-8 %, while at 8 N tiles the tile-major order
+// was as fast or faster).
+__host__ __device__ constexpr int dgrad_group(int ntn) { return ntn >= 16 ? 8 : 1; }
+static_assert(BT == MOE_TILE_ROWS, "a dgrad item covers one tile-map entry");
+
+__device__ __forceinline__ void dgrad_item(long long item, int ntn, int grp, const int32_t* __restrict__ tile_map,
+                                           const int32_t* __restrict__ seg_offset, int& tile, int& n) {
+  const int tg = (int)(item / ntn);  // some row tile of the same expert
+  const int e = tile_map[4LL * tg];
+  const int s0 = seg_offset[e];
+  const int t0 = tg - ((tile_map[4LL * tg + 1] - s0) / BT);  // the expert's first tile
+  const int nt = (seg_offset[e + 1] - s0 + BT - 1) / BT;
+  const long long local = item - (long long)t0 * ntn;
+  const int g0 = (int)(local / ((long long)grp * ntn)) * grp;
+  const int gt = nt - g0 < grp ? nt - g0 : grp;
+  const int r = (int)(local - (long long)g0 * ntn);
+  n = r / gt;
+  tile = t0 + g0 + r % gt;
+}
+
 // K loop and epilogue of one E4M3 dgrad item (see dgrad_run).  A stage
 // buffer holds the activation rows (32 KB), the weight K-rows (32 KB) and
 // the row scales (1 KB).  Lane l holds the scales of the wave's weight
@@ -645,7 +676,8 @@ template <bool SWIGLU, typename OT>
 __global__ __launch_bounds__(BTHREADS) void k_dgrad8(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                      const uint8_t* __restrict__ w, const float* __restrict__ ws,
                                                      const int32_t* __restrict__ tile_map,
-                                                     const int32_t* __restrict__ n_tiles, int Kd, int Nd,
+                                                     const int32_t* __restrict__ n_tiles,
+                                                     const int32_t* __restrict__ seg_offset, int Kd, int Nd,
                                                      uint32_t a_bytes, uint32_t as_bytes,
                                                      const uint16_t* __restrict__ ab, OT* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP + BSC];
@@ -659,7 +691,8 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad8(const uint8_t* __restrict__
   if (slot >= q) return;
   const long long item = (blockIdx.x & 7) * q + slot;
   if (item >= items) return;
-  const int tile = (int)(item / ntn), n = (int)(item % ntn);
+  int tile, n;
+  dgrad_item(item, ntn, dgrad_group(ntn), tile_map, seg_offset, tile, n);
   const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * tile);
   const int seg = tm.x, row0 = tm.y, rows = tm.w;
   const int w_wave = __builtin_amdgcn_readfirstlane(wave);
@@ -694,7 +727,7 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad8(const uint8_t* __restrict__
 
 // Items (row tile, N tile) of the tile map, dealt to the XCDs in contiguous
 // runs (block b runs on XCD b % 8): XCD x takes items [x q, x q + q) of the
-// item list ordered tile-major, so the row tiles of one expert, and the
+// item list in dgrad_item's order, so the row tiles of one expert, and the
 // weight slabs they share, stay in one L2.
 //
 // SWIGLU: A = dy [P, d] (K = d), W = W2 [E, d, I] (K-rows d, N = I); the
@@ -704,7 +737,8 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad8(const uint8_t* __restrict__
 template <bool SWIGLU, typename OT>
 __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
                                                     const int32_t* __restrict__ tile_map,
-                                                    const int32_t* __restrict__ n_tiles, int Kd, int Nd,
+                                                    const int32_t* __restrict__ n_tiles,
+                                                    const int32_t* __restrict__ seg_offset, int Kd, int Nd,
                                                     uint32_t a_bytes, const uint16_t* __restrict__ ab,
                                                     OT* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
@@ -718,7 +752,8 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
   if (slot >= q) return;
   const long long item = (blockIdx.x & 7) * q + slot;
   if (item >= items) return;
-  const int tile = (int)(item / ntn), n = (int)(item % ntn);
+  int tile, n;
+  dgrad_item(item, ntn, dgrad_group(ntn), tile_map, seg_offset, tile, n);
   const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * tile);
   const int seg = tm.x, row0 = tm.y, rows = tm.w;
   const int w_wave = __builtin_amdgcn_readfirstlane(wave);
@@ -1321,15 +1356,15 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
   {
     const long long items = (long long)tiles_max * ((I + BT - 1) / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
-    hipLaunchKernelGGL((k_dgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, w2, tile_map, n_tiles, d, I,
-                       dy_bytes, ab, dab);
+    hipLaunchKernelGGL((k_dgrad<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dy, w2, tile_map, n_tiles,
+                       seg_offset, d, I, dy_bytes, ab, dab);
   }
   // dgrad, gate/up: N = d
   {
     const long long items = (long long)tiles_max * (d / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
     hipLaunchKernelGGL((k_dgrad<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dab, w13, tile_map, n_tiles,
-                       2 * I, d, dab_bytes, nullptr, dx);
+                       seg_offset, 2 * I, d, dab_bytes, nullptr, dx);
   }
   launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, deal, dw13, dw2, dw_f32, st);
 }
@@ -1342,8 +1377,8 @@ bool ffn_bwd_w8_ok(int d, int I) { return ffn_bwd_ok(d, I) && d / 128 <= 128 && 
 // with 128x128 block scales; dab gets [da | db] (bf16), dx the input
 // gradient.
 static void launch_dgrads8(const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
-                           const uint16_t* ab, const uint16_t* dy, const int32_t* tile_map, const int32_t* n_tiles,
-                           int tiles_max, int T, long long P, int d, int I, uint16_t* dab, uint8_t* dyq, float* dys,
+                           const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
+                           const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d, int I, uint16_t* dab, uint8_t* dyq, float* dys,
                            uint8_t* dabq, float* dabs, uint16_t* dx, hipStream_t st) {
   // with no tokens every row is padding: nothing to quantise (and dy may be NULL)
   if (T > 0) quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
@@ -1351,15 +1386,15 @@ static void launch_dgrads8(const uint8_t* w13, const float* w13s, const uint8_t*
     const long long items = (long long)tiles_max * ((I + BT - 1) / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
     hipLaunchKernelGGL((k_dgrad8<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dys, w2, w2s, tile_map,
-                       n_tiles, d, I, (uint32_t)(P * d), (uint32_t)(P * (d / 128) * 4), ab, dab);
+                       n_tiles, seg_offset, d, I, (uint32_t)(P * d), (uint32_t)(P * (d / 128) * 4), ab, dab);
   }
   if (T > 0) quantize_tiles(dab, MOE_BF16, P, 2LL * I, 1, 128, dabq, dabs, st);
   {
     const long long items = (long long)tiles_max * (d / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
     hipLaunchKernelGGL((k_dgrad8<false, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dabq, dabs, w13, w13s,
-                       tile_map, n_tiles, 2 * I, d, (uint32_t)(P * 2 * I), (uint32_t)(P * (2 * I / 128) * 4), nullptr,
-                       dx);
+                       tile_map, n_tiles, seg_offset, 2 * I, d, (uint32_t)(P * 2 * I),
+                       (uint32_t)(P * (2 * I / 128) * 4), nullptr, dx);
   }
 }
 
@@ -1371,7 +1406,7 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
                        uint8_t* dabq, float* dabs, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
                        hipStream_t st) {
-  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
+  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, seg_offset, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
                  st);
   launch_wgrads(x, h, dy, dab, seg_offset, row_token, T, P, d, I, Nr, Ns, deal, dw13, dw2, dw_f32, st);
 }
@@ -1389,7 +1424,7 @@ void launch_ffn_bwd_f8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        uint8_t* dabq, float* dabs, uint8_t* hr, uint8_t* xr, float* dyrs, float* hrs, float* dabrs,
                        float* xrs, int32_t* run_offset, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
                        hipStream_t st) {
-  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
+  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, seg_offset, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
                  st);
   const int E = Nr + Ns;
   launch_quantize_runs(dy, false, P, d, row_token, false, seg_offset, E, P, run_offset, true, dyq, dyrs, st);
