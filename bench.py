@@ -71,9 +71,14 @@ def parse():
 # factor the same counters give for a plain copy of known size).  Valid only
 # for the kernel sources they were taken on: a changed source gives null.
 TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 35792293422, "write_bytes": 1359584149, "digest": "12fae6f40bd8ba57"},
-    "v3_prefill_fp8": {"fetch_bytes": 29782070269, "write_bytes": 2470444256, "digest": "12fae6f40bd8ba57"},
-    "v3_decode_fp8w": {"fetch_bytes": 11295357709, "write_bytes": 21428939, "digest": "c01919518e0da1b8"},
+    "v3_prefill_bf16": {"fetch_bytes": 35684460544, "write_bytes": 1359583846, "digest": "be4aa795438a2e48"},
+    "v3_prefill_fp8": {"fetch_bytes": 28438956032, "write_bytes": 2471575449, "digest": "be4aa795438a2e48"},
+    "v3_decode_fp8w": {"fetch_bytes": 11297040384, "write_bytes": 21428791, "digest": "26c47dd95af81869"},
+    # moe_expert_gemm_combine (--fused-combine): k_fused_prep + both phases
+    "v3_prefill_bf16:fused": {"fetch_bytes": 35609409105, "write_bytes": 2653925376, "digest": "ae3507277e8f34a5",
+                              "sources": ("gemm_mfma.hip", "elementwise.hip", "common.h")},
+    "v3_prefill_fp8:fused": {"fetch_bytes": 28219332608, "write_bytes": 5059951104, "digest": "ae3507277e8f34a5",
+                             "sources": ("gemm_mfma.hip", "elementwise.hip", "common.h")},
 }
 
 # HBM traffic of one backward expert GEMM call of the training step
@@ -81,9 +86,11 @@ TRAFFIC = {
 # taken the same way from `--train` runs; keyed by workload, and for the
 # E4M3 step with bf16 weight gradients by workload + ":bf16wgrad".
 TRAIN_TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 57156214931, "write_bytes": 24405509994, "digest": "21e05a20a7e4b31b",
+    "v3_prefill_bf16": {"fetch_bytes": 51252636842, "write_bytes": 24412897689, "digest": "b1844c194af9109b",
                         "sources": ("gemm_bwd.hip", "common.h")},
-    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 38621066352, "write_bytes": 25457392501, "digest": "ccb532542fa76c72",
+    "v3_train_fp8": {"fetch_bytes": 27499840861, "write_bytes": 26922047622, "digest": "c910a627832234d2",
+                     "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
+    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 35262141875, "write_bytes": 25541999073, "digest": "c910a627832234d2",
                                "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
 }
 
@@ -220,8 +227,8 @@ def main():
         achieved = gemm_flops / (gemm_ms * 1e-3)
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": mfma_peak / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / mfma_peak}
-    digest = gemm_source_digest(cfg.name)
     tr = TRAFFIC.get(cfg.name + (":fused" if args.fused_combine else ""))
+    digest = gemm_source_digest(cfg.name, tr.get("sources") if tr else None)
     roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) / 1e9 if tr and tr["digest"] == digest else None
     roof["traffic_unit"] = "GB per launch"
     roof["kernel_digest"] = digest
