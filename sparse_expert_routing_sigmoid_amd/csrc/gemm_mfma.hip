@@ -322,6 +322,12 @@ __device__ __forceinline__ float absmax8(float4 a, float4 b) {
                fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
 }
 
+// A barrier for LDS traffic only: this wave's LDS accesses are complete,
+// then every wave meets; global stores still in flight are not waited for
+// (the fence of __syncthreads would wait for them).  The compiler moves no
+// memory access across it.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Epilogue.  Phase B with bf16 output stores straight from the
 // accumulators.  Otherwise two passes of 128 rows (wave row 0, then 1): the
 // waves of the pass write their fp32 accumulators to LDS (64 rows per stage
@@ -390,7 +396,7 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
   }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    __syncthreads();
+    lds_sync();  // the K loop's (or the previous pass's) LDS reads are done
     if (wm == pass) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -405,7 +411,7 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
           }
         }
     }
-    __syncthreads();
+    lds_sync();
     constexpr int CH = NC / 8;                     // 8-value chunks per output row
     const int prow = it.rows - pass * 128;         // rows of this pass that exist
     const int nrow = prow < 0 ? 0 : (prow > 128 ? 128 : prow);
@@ -454,6 +460,33 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
   }
 }
 
+// The successor of the current work item (k_ffn_persistent, phase B).
+// Thread 0 claims index i of its XCD's list with an atomic add as the item
+// starts; resolve() reads the list entry once the tile's K loop has waited
+// for all its loads, before the epilogue issues its stores (read after
+// them, the entry's load would also wait for the stores).  entry < 0: the
+// list is drained.  Only wave 0's value is used.  Phase A claims as the
+// tile ends: its items are long, and a claim one item ahead left blocks
+// holding work at the end of the phase (bf16 call +2 %; phase B's claim
+// ahead: E4M3 call -0.8 %, bf16 unchanged, in A/B runs).
+struct NextItem {
+  const int* list;
+  int tot, i, entry;
+  __device__ void resolve(int tid) {
+    int e = -1;
+    if (tid == 0 && i < tot) e = list[i];
+    entry = __builtin_amdgcn_readfirstlane(e);
+  }
+};
+
+// vmcnt(0) and lgkmcnt(0) as a builtin, so the compiler knows every load has
+// completed; the empty asm statements keep memory accesses on their side.
+__device__ __forceinline__ void wait_all_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x7u << 4);
+  asm volatile("" ::: "memory");
+}
+
 // One work item for a wave with MT live 32-row MFMA tiles: accumulators,
 // K loop (two-stage pipeline, unrolled by two so each step names its
 // buffers and the loop has a single exit) and epilogue, all in one
@@ -461,7 +494,8 @@ __device__ __forceinline__ void epilogue(const f32x16_v (&acc)[MA][4], const Ite
 template <bool FP8, bool PHASE_A, int MT, typename OT, bool KEEP, bool FUSE>
 __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* st1, int wm, int wn, int tid,
                                          OT* __restrict__ out, float* __restrict__ out_scale,
-                                         uint16_t* __restrict__ ab, uint16_t* __restrict__ hb, int Nd, int n) {
+                                         uint16_t* __restrict__ ab, uint16_t* __restrict__ hb, int Nd, int n,
+                                         NextItem& nx) {
   constexpr int MA = MT > 0 ? MT : 1;
   f32x16_v acc[MA][4];
 #pragma unroll
@@ -479,7 +513,8 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
     __syncthreads();
     pipe_step<FP8, MT>(acc, it, st0, st1, s + 1, s + 2 < it.nk, (uint32_t)(s + 2) * P_ROWB);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last step's zero loads land before LDS is reused
+  wait_all_loads();  // the last step's zero loads land before LDS is reused
+  if constexpr (!PHASE_A) nx.resolve(tid);  // (see NextItem)
   epilogue<PHASE_A, FP8 && PHASE_A, MT, MA, OT, KEEP, FUSE>(acc, it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd,
                                                       n);
 }
@@ -489,7 +524,8 @@ __device__ __forceinline__ void run_tile(const Item& it, uint8_t* st0, uint8_t* 
 // bytes; the epilogue stages its rows through the first 128 KB.
 template <bool PHASE_A, int MT, typename OT, bool KEEP, bool FUSE>
 __device__ __forceinline__ void run_tile_deep(const Item& it, uint8_t* lds, int wm, int wn, int tid,
-                                              OT* __restrict__ out, uint16_t* __restrict__ ab, int Nd, int n) {
+                                              OT* __restrict__ out, uint16_t* __restrict__ ab, int Nd, int n,
+                                              NextItem& nx) {
   constexpr int MA = MT > 0 ? MT : 1;
   f32x16_v acc[MA][4];
 #pragma unroll
@@ -521,7 +557,8 @@ __device__ __forceinline__ void run_tile_deep(const Item& it, uint8_t* lds, int 
     uint8_t* t = a0; a0 = a1; a1 = t;
     t = b0; b0 = b1; b1 = b2; b2 = t;
   }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // the last zero loads land before LDS is reused
+  wait_all_loads();  // the last zero loads land before LDS is reused
+  if constexpr (!PHASE_A) nx.resolve(tid);  // (see NextItem)
   epilogue<PHASE_A, false, MT, MA, OT, KEEP, FUSE>(acc, it, lds, lds + 2 * D_AB, wm, wn, tid, out, nullptr, ab, nullptr,
                                              Nd, n);
 }
@@ -529,9 +566,10 @@ __device__ __forceinline__ void run_tile_deep(const Item& it, uint8_t* lds, int 
 // ------------------------------------------------------------------------
 // LDS of the kernel.  E4M3: two stages of A + row scales and B as separate
 // arrays (the compiler then knows they never overlap), and the item word.
-// bf16: the D_LDS bytes of the deep K loop; the item word sits in the second
-// A stage, which is first written by loads issued after the stage-0
-// barrier, when every wave has read it.
+// bf16: the D_LDS bytes of the deep K loop; the item word sits in the third
+// B stage, which neither the prologue's loads nor the epilogue touch: it is
+// first written by the loads of stage 0's body, issued after the prologue's
+// barrier, when every wave has read the word.
 template <bool FP8>
 struct KernelLds;
 template <>
@@ -550,7 +588,7 @@ struct KernelLds<false> {
   __device__ uint8_t* base() { return lds; }
   __device__ uint8_t* stage0() { return lds; }
   __device__ uint8_t* stage1() { return lds + 2 * D_AB; }
-  __device__ int* item() { return reinterpret_cast<int*>(lds + D_AB); }
+  __device__ int* item() { return reinterpret_cast<int*>(lds + 4 * D_AB); }
 };
 
 // PHASE_A: x = tokens [T, Kd] gathered by row_token, w = W13 [E, 2*Nd, Kd],
@@ -593,23 +631,33 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
   const long long w_expert = (long long)wrows * Kd * EB;  // bytes per expert
   const int kblocks = Kd * EB / P_ROWB;        // K blocks (stages) of a row
 
-  for (;;) {
-    __syncthreads();  // previous item done with LDS and the item word
-    if (tid == 0) {
-      // this XCD's list first; when it is drained, help the other XCDs
-      int got = -1;
-      for (int k = 0; k < 8 && got < 0; ++k) {
-        const int y = (xcd + k) & 7;
-        const int tot = totals[y];
-        if (__atomic_load_n(&counters[y], __ATOMIC_RELAXED) >= tot) continue;
-        const int i = atomicAdd(&counters[y], 1);
-        if (i < tot) got = items[offsets[y] + i];
-      }
-      *s_item_p = got;
+  // Items are claimed by thread 0 and passed on through the LDS item word.
+  // In phase B the claim of an item's successor on this XCD's list (an
+  // atomic add) is issued when the item starts and its result read after
+  // the K loop (NextItem); phase A claims as the tile ends.  When the list
+  // is drained, the other XCDs' lists are searched as the tile ends.  The
+  // barriers between items wait for LDS traffic only: the epilogue's global
+  // stores drain under the next item's set-up (a __syncthreads fence would
+  // wait for them).
+  const int tot_x = totals[xcd], off_x = offsets[xcd];
+  auto steal = [&](int k0) {
+    int got = -1;
+    for (int k = k0; k < 8 && got < 0; ++k) {
+      const int y = (xcd + k) & 7;
+      const int tot = totals[y];
+      if (__atomic_load_n(&counters[y], __ATOMIC_RELAXED) >= tot) continue;
+      const int i = atomicAdd(&counters[y], 1);
+      if (i < tot) got = items[offsets[y] + i];
     }
-    __syncthreads();
-    const int entry = *s_item_p;
-    if (entry < 0) break;
+    return got;
+  };
+  if (tid == 0) *s_item_p = steal(0);
+  lds_sync();
+  int entry = *s_item_p;
+  constexpr bool EARLY = !PHASE_A;  // see NextItem
+  while (entry >= 0) {
+    NextItem nx{items + off_x, tot_x, 0, -1};
+    if (EARLY && tid == 0) nx.i = atomicAdd(&counters[xcd], 1);
     const int tile = entry >> 8;
     const int n = entry & 255;
     const int4 tm = *reinterpret_cast<const int4*>(tile_map + 4LL * tile);
@@ -669,21 +717,25 @@ __global__ __launch_bounds__(P_THREADS) void k_ffn_persistent(const uint8_t* __r
     mt_live = __builtin_amdgcn_readfirstlane(mt_live < 0 ? 0 : (mt_live > 4 ? 4 : mt_live));
     if constexpr (FP8) {
       switch (mt_live) {
-        case 4: run_tile<FP8, PHASE_A, 4, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        case 3: run_tile<FP8, PHASE_A, 3, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        case 2: run_tile<FP8, PHASE_A, 2, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        case 1: run_tile<FP8, PHASE_A, 1, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
-        default: run_tile<FP8, PHASE_A, 0, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n); break;
+        case 4: run_tile<FP8, PHASE_A, 4, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n, nx); break;
+        case 3: run_tile<FP8, PHASE_A, 3, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n, nx); break;
+        case 2: run_tile<FP8, PHASE_A, 2, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n, nx); break;
+        case 1: run_tile<FP8, PHASE_A, 1, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n, nx); break;
+        default: run_tile<FP8, PHASE_A, 0, OT, KEEP, FUSE>(it, st0, st1, wm, wn, tid, out, out_scale, ab, hb, Nd, n, nx); break;
       }
     } else {
       switch (mt_live) {
-        case 4: run_tile_deep<PHASE_A, 4, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        case 3: run_tile_deep<PHASE_A, 3, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        case 2: run_tile_deep<PHASE_A, 2, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        case 1: run_tile_deep<PHASE_A, 1, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
-        default: run_tile_deep<PHASE_A, 0, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n); break;
+        case 4: run_tile_deep<PHASE_A, 4, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n, nx); break;
+        case 3: run_tile_deep<PHASE_A, 3, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n, nx); break;
+        case 2: run_tile_deep<PHASE_A, 2, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n, nx); break;
+        case 1: run_tile_deep<PHASE_A, 1, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n, nx); break;
+        default: run_tile_deep<PHASE_A, 0, OT, KEEP, FUSE>(it, lds, wm, wn, tid, out, ab, Nd, n, nx); break;
       }
     }
+    lds_sync();  // every wave done with LDS and the item word
+    if (tid == 0) *s_item_p = EARLY && nx.entry >= 0 ? nx.entry : steal(EARLY ? 1 : 0);
+    lds_sync();
+    entry = *s_item_p;
   }
 }
 
