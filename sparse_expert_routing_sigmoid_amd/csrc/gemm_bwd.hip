@@ -781,10 +781,11 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
 // ------------------------------------------------------------- wgrad --
 constexpr int WG_STORES = 32;  // buffer stores per wave for one bf16 result tile
 
-// Every wait for a stage's loads is a full vmcnt(0): the counter is shared
-// with the result stores, and loads and stores in flight together may
-// retire out of order, so a partial count does not tell that the older
-// loads have landed.
+// A wave's loads and stores share vmcnt and complete in issue order, so the
+// first wait of a tile whose predecessor's bf16 result stores (exactly
+// WG_STORES per wave) were issued after the loads it waits for lets those
+// stores stay in flight; every other wait is for everything (fp32 results
+// leave as a number of stores that depends on the columns).
 
 // One pair of stages of a wgrad K loop.  On entry st0 holds stage s
 // (complete and visible) and the loads of stage s + 1 into st1 are in
@@ -795,12 +796,16 @@ constexpr int WG_STORES = 32;  // buffer stores per wave for one bf16 result til
 template <bool GATHER>
 __device__ __forceinline__ void wgrad_pair(f32x16_t (&acc)[4][4], SegRows<GATHER, 8>& S, uint8_t* __restrict__ st0,
                                            uint8_t* __restrict__ st1, const MncLane& mla, const MncLane& mlb, int wm,
-                                           int wn, int lane, int w_wave, int s, int nk, uint32_t bc, bool more) {
+                                           int wn, int lane, int w_wave, int s, int nk, uint32_t bc, bool more,
+                                           bool after_store = false) {
   const bool wrap = s + 2 == nk;
   const uint32_t bn = wrap ? bc + BT * 2u : bc;
   const bool live = !wrap || more;
   mma_stage<false, false>(acc, st0, st0 + BOP, mla, mlb, wm, wn, lane);
-  vm_wait<0>();
+  if (after_store)
+    vm_wait<WG_STORES>();
+  else
+    vm_wait<0>();
   lds_barrier();
   S.issue(st0, st0 + BOP, w_wave, lane, wrap ? 0 : s + 2, bn, live);
   S.fetch(wrap ? 1 : s + 3, w_wave, lane);
@@ -844,7 +849,7 @@ __device__ __forceinline__ void wgrad_run(SegRows<GATHER, 8>& S, uint8_t* __rest
     // and a reload from scratch would wait for the stores.
     int s0 = 0;
     asm volatile("" : "+s"(s0));
-    if (nk > 0) wgrad_pair(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s0, nk, bc, more);
+    if (nk > 0) wgrad_pair(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s0, nk, bc, more, BF16 && n > n0);
     for (int s = 2; s < nk; s += 2) wgrad_pair(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s, nk, bc, more);
     // (see mma16 for the accumulator layout)
     if constexpr (BF16) {
@@ -1184,14 +1189,18 @@ struct Run8Next {
 // One stage of an item's sequence (N tiles n0 .. n1 - 1, nk runs each) in
 // st: multiply it, wait for the next stage (in the other buffer) and for
 // every wave to be done with st, then load the stage after next into st.
-// The wait is a full vmcnt(0) (see the wgrad notes above): on the first
-// stage of a tile it also drains the previous tile's stores, issued after
-// the loads it waits for.
+// after_store: the first stage of a tile whose predecessor's WG_STORES bf16
+// result stores were issued after the loads this wait is for, so it lets
+// them stay in flight (the wave's memory operations complete in issue
+// order); otherwise the wait is for everything.
 __device__ __forceinline__ void wgrad8_step(f32x16_t (&acc)[4][4], uint8_t* st, const RunRows8& S,
                                             const MncLane8& mla, const MncLane8& mlb, Run8Next& nx, int n1, int nk,
-                                            int wm, int wn, int lane, int w_wave) {
+                                            int wm, int wn, int lane, int w_wave, bool after_store = false) {
   mma_run8(acc, st, mla, mlb, wm, wn, lane);
-  vm_wait<0>();
+  if (after_store)
+    vm_wait<WG_STORES>();
+  else
+    vm_wait<0>();
   lds_barrier();
   S.issue(st, w_wave, lane, nx.ls, (uint32_t)nx.ln * BT, nx.ln < n1);
   if (++nx.ls == nk) {
@@ -1207,17 +1216,19 @@ __device__ __forceinline__ void wgrad8_step(f32x16_t (&acc)[4][4], uint8_t* st, 
 template <bool ODD>
 __device__ __forceinline__ void wgrad8_tile(f32x16_t (&acc)[4][4], uint8_t* bufa, uint8_t* bufb, const RunRows8& S,
                                             const MncLane8& mla, const MncLane8& mlb, Run8Next& nx, int n1, int nk,
-                                            int wm, int wn, int lane, int w_wave) {
+                                            int wm, int wn, int lane, int w_wave, bool after_store) {
   zero_acc(acc);
   int s = 0;
   if constexpr (ODD) {
-    wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+    wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave, after_store);
     for (s = 1; s < nk; s += 2) {
       wgrad8_step(acc, bufb, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
       wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
     }
   } else {
-    for (s = 0; s < nk; s += 2) {
+    wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave, after_store);
+    wgrad8_step(acc, bufb, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+    for (s = 2; s < nk; s += 2) {
       wgrad8_step(acc, bufa, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
       wgrad8_step(acc, bufb, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
     }
@@ -1284,9 +1295,13 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad8(const uint8_t* __restrict__
   vm_wait<RUN8_ACCESSES>();
   lds_barrier();
   const int r0 = m * BT + wm * 128, c0 = wn * 128;
+  // bf16 results leave as exactly WG_STORES stores per wave, which the
+  // next tile's first wait lets stay in flight; fp32 ones (a number of
+  // stores that depends on the columns) are waited for
+  constexpr bool PARTIAL = sizeof(OT) == 2;
   if ((nk & 1) == 0) {
     for (int n = n0; n < n1; ++n) {
-      wgrad8_tile<false>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_tile<false>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave, PARTIAL && n > n0);
       wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + n * BT, lane);
     }
   } else {
@@ -1294,13 +1309,13 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad8(const uint8_t* __restrict__
     // the other, so tiles go in pairs
     int n = n0;
     for (; n + 1 < n1; n += 2) {
-      wgrad8_tile<true>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_tile<true>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave, PARTIAL && n > n0);
       wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + n * BT, lane);
-      wgrad8_tile<true>(acc, st1, st0, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_tile<true>(acc, st1, st0, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave, PARTIAL);
       wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + (n + 1) * BT, lane);
     }
     if (n < n1) {
-      wgrad8_tile<true>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave);
+      wgrad8_tile<true>(acc, st0, st1, S, mla, mlb, nx, n1, nk, wm, wn, lane, w_wave, PARTIAL && n > n0);
       wgrad8_store(acc, stw, ob, Md, Nd, r0, c0 + n * BT, lane);
     }
   }
