@@ -25,6 +25,11 @@ CASES = {
     "ragged": BASE.with_(T=300, d=768, Nr=12, Ns=2, I=384, K=3),
     # several row tiles per expert and a longer K loop
     "mid_reduced": BASE.with_(T=1024, d=1024, Nr=32, Ns=2, I=640, K=6),
+    # 16 N tiles of d, where the gate/up dgrad runs an expert's items in
+    # groups of 8 row tiles, N-tile major; the shared expert has 9 row tiles
+    # (a group of 8 and one of 1).  I / d near the V3 layer's, so that the
+    # FFN part of du is not small next to the router part
+    "wide": BASE.with_(T=2304, d=4096, Nr=8, Ns=1, I=1024, K=2),
 }
 
 

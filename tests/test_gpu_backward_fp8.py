@@ -29,6 +29,8 @@ CASES = {
     # I % 256 == 128: the last N tile of the down dgrad is half a tile
     "ragged": BASE.with_(T=300, d=768, Nr=12, Ns=2, I=384, K=3),
     "mid_reduced": BASE.with_(T=1024, d=1024, Nr=32, Ns=2, I=640, K=6),
+    # 16 N tiles of d: the gate/up dgrad's items in groups of row tiles
+    "wide": BASE.with_(T=2304, d=4096, Nr=8, Ns=1, I=1024, K=2),
 }
 
 
