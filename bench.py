@@ -71,13 +71,13 @@ def parse():
 # factor the same counters give for a plain copy of known size).  Valid only
 # for the kernel sources they were taken on: a changed source gives null.
 TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 35684460544, "write_bytes": 1359583846, "digest": "be4aa795438a2e48"},
-    "v3_prefill_fp8": {"fetch_bytes": 28438956032, "write_bytes": 2471575449, "digest": "be4aa795438a2e48"},
+    "v3_prefill_bf16": {"fetch_bytes": 36386514944, "write_bytes": 1359597158, "digest": "fa2660644de4db0d"},
+    "v3_prefill_fp8": {"fetch_bytes": 28487229440, "write_bytes": 2472013209, "digest": "fa2660644de4db0d"},
     "v3_decode_fp8w": {"fetch_bytes": 11297040384, "write_bytes": 21428791, "digest": "26c47dd95af81869"},
     # moe_expert_gemm_combine (--fused-combine): k_fused_prep + both phases
-    "v3_prefill_bf16:fused": {"fetch_bytes": 35609409105, "write_bytes": 2653925376, "digest": "ae3507277e8f34a5",
+    "v3_prefill_bf16:fused": {"fetch_bytes": 37123061514, "write_bytes": 2653917798, "digest": "cde06645bb9ca92d",
                               "sources": ("gemm_mfma.hip", "elementwise.hip", "common.h")},
-    "v3_prefill_fp8:fused": {"fetch_bytes": 28219332608, "write_bytes": 5059951104, "digest": "ae3507277e8f34a5",
+    "v3_prefill_fp8:fused": {"fetch_bytes": 28890714112, "write_bytes": 5059960217, "digest": "cde06645bb9ca92d",
                              "sources": ("gemm_mfma.hip", "elementwise.hip", "common.h")},
 }
 
@@ -86,11 +86,11 @@ TRAFFIC = {
 # taken the same way from `--train` runs; keyed by workload, and for the
 # E4M3 step with bf16 weight gradients by workload + ":bf16wgrad".
 TRAIN_TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 51252636842, "write_bytes": 24412897689, "digest": "b1844c194af9109b",
+    "v3_prefill_bf16": {"fetch_bytes": 51114372224, "write_bytes": 24303993241, "digest": "d775e1abb9759084",
                         "sources": ("gemm_bwd.hip", "common.h")},
-    "v3_train_fp8": {"fetch_bytes": 27499840861, "write_bytes": 26922047622, "digest": "c910a627832234d2",
+    "v3_train_fp8": {"fetch_bytes": 27641560413, "write_bytes": 27079476051, "digest": "8e1dc7bf20529fb8",
                      "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
-    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 35262141875, "write_bytes": 25541999073, "digest": "c910a627832234d2",
+    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 35254774912, "write_bytes": 25330469785, "digest": "8e1dc7bf20529fb8",
                                "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
 }
 
