@@ -126,9 +126,11 @@ struct KcRows {
       off[j] = tr < rows ? (uint32_t)(row0 + tr) * row_bytes + c16 : OOB;
     }
   }
-  __device__ void issue(uint8_t* st, int wave, int s, uint32_t oob) const {
+  __device__ void issue(uint8_t* st, int wave, int s, uint32_t oob) const { issue_j<0, 8>(st, wave, s, oob); }
+  template <int J0, int J1>
+  __device__ void issue_j(uint8_t* st, int wave, int s, uint32_t oob) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(r, st + (wave * 8 + j) * 1024, off[j] | oob, (uint32_t)s * 128u);
+    for (int j = J0; j < J1; ++j) dma16(r, st + (wave * 8 + j) * 1024, off[j] | oob, (uint32_t)s * 128u);
   }
 };
 
@@ -149,9 +151,11 @@ struct MncRows {
       off[j] = (uint32_t)kr * row_bytes + (uint32_t)col0 * 2u + c * 16u;
     }
   }
-  __device__ void issue(uint8_t* st, int wave, int s, uint32_t oob) const {
+  __device__ void issue(uint8_t* st, int wave, int s, uint32_t oob) const { issue_j<0, 8>(st, wave, s, oob); }
+  template <int J0, int J1>
+  __device__ void issue_j(uint8_t* st, int wave, int s, uint32_t oob) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(r, st + (wave * 8 + j) * 1024, off[j] | oob, (uint32_t)s * kstride);
+    for (int j = J0; j < J1; ++j) dma16(r, st + (wave * 8 + j) * 1024, off[j] | oob, (uint32_t)s * kstride);
   }
 };
 
@@ -451,6 +455,105 @@ __device__ __forceinline__ void dgrad_run(const KcRows& A, const MncRows& B, uin
   dgrad_epilogue<SWIGLU, OT>(acc, st1, wm, wn, tid, lane, Nd, n, row0, rows, ab, out);
 }
 
+// bf16 dgrad K loop with three weight stages (the forward's layout): LDS
+// holds two 32 KB stages of the activation-gradient rows (A) and three of
+// the weight K-rows (B), 160 KB; B is loaded two stages ahead and A one, so
+// 64 KB of the weight stream is in flight per CU.  The wait before a
+// stage's barrier leaves the 8 loads of the B stage two ahead outstanding
+// (a wave's loads complete in issue order).  Per stage s:
+//   k-step 0: B(s + 2) blocks 0-3 -> b_dst, fragments of k 1, MFMAs of k 0
+//   k-step 1: B(s + 2) blocks 4-7, fragments of k 2, MFMAs of k 1
+//   k-step 2: fragments of k 3, MFMAs of k 2
+//   wait for this wave's LDS reads and everything but B(s + 2), barrier
+//   k-step 3: A(s + 2) -> a_cur (the A(s) buffer), fragments of k 0 of
+//   stage s + 1 (a_nxt, b_nxt), MFMAs of k 3
+// Within a k-step the MFMAs, the LDS reads and the global loads are
+// interleaved one by one, so the LDS serves the reads and the
+// direct-to-LDS writes while the matrix pipe is busy.
+template <int NMFMA, int NDS, int NVM>
+__device__ __forceinline__ void dg_order_kstep() {
+  constexpr int N = NMFMA > NDS ? (NMFMA > NVM ? NMFMA : NVM) : (NDS > NVM ? NDS : NVM);
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    if (q < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (q < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (q < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
+// vmcnt(8) / vmcnt(16) and lgkmcnt(0) (expcnt left at its maximum).
+constexpr unsigned DG_WAIT_VM8_LGKM0 = (8u & 0xFu) | (0x7u << 4) | ((8u >> 4) << 14);
+constexpr unsigned DG_WAIT_VM16_LGKM0 = (16u & 0xFu) | (0x7u << 4) | ((16u >> 4) << 14);
+
+template <int MT>
+__device__ __forceinline__ void dg_deep_body(f32x16_t (&acc)[4][4], bf16x8_t (&af)[2][4], bf16x8_t (&bf)[2][4],
+                                             const KcRows& A, const MncRows& B, const MncLane& mlb, int wm, int wn,
+                                             int lane, int w_wave, int s, uint8_t* __restrict__ a_cur,
+                                             const uint8_t* __restrict__ b_cur, const uint8_t* __restrict__ a_nxt,
+                                             const uint8_t* __restrict__ b_nxt, uint8_t* __restrict__ b_dst,
+                                             uint32_t oob2) {
+  constexpr int NM = 4 * MT, ND = MT + 8;
+  B.issue_j<0, 4>(b_dst, w_wave, s + 2, oob2);
+  load_frags<true, false, 1, MT>(af[1], bf[1], a_cur, b_cur, mlb, mlb, wm, wn, lane);
+  mma16<0, MT>(acc, af[0], bf[0]);
+  dg_order_kstep<NM, ND, 4>();
+  __builtin_amdgcn_sched_barrier(0);
+  B.issue_j<4, 8>(b_dst, w_wave, s + 2, oob2);
+  load_frags<true, false, 2, MT>(af[0], bf[0], a_cur, b_cur, mlb, mlb, wm, wn, lane);
+  mma16<1, MT>(acc, af[1], bf[1]);
+  dg_order_kstep<NM, ND, 4>();
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<true, false, 3, MT>(af[1], bf[1], a_cur, b_cur, mlb, mlb, wm, wn, lane);
+  mma16<2, MT>(acc, af[0], bf[0]);
+  dg_order_kstep<NM, ND, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(DG_WAIT_VM8_LGKM0);  // own LDS reads done; A(s + 1), B(s + 1) landed
+  __builtin_amdgcn_s_barrier();                  // ... for every wave
+  __builtin_amdgcn_sched_barrier(0);
+  A.issue(a_cur, w_wave, s + 2, oob2);
+  load_frags<true, false, 0, MT>(af[0], bf[0], a_nxt, b_nxt, mlb, mlb, wm, wn, lane);
+  mma16<3, MT>(acc, af[1], bf[1]);
+  dg_order_kstep<NM, ND, 8>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K loop and epilogue of one bf16 dgrad item on the three-stage loop; lds:
+// DG_LDS bytes, the epilogue's staging in its first 64 KB.
+constexpr int DG_AB = BT * 128;    // 32 KB: one stage of A or of B
+constexpr int DG_LDS = 5 * DG_AB;  // A0 A1 B0 B1 B2
+template <bool SWIGLU, typename OT, int MT>
+__device__ __forceinline__ void dgrad_run_deep(const KcRows& A, const MncRows& B, uint8_t* __restrict__ lds,
+                                               const MncLane& mlb, int wm, int wn, int tid, int lane, int w_wave,
+                                               int Kd, int Nd, int n, int row0, int rows,
+                                               const uint16_t* __restrict__ ab, OT* __restrict__ out) {
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+  const int nk = Kd / BKS;
+  uint8_t* a0 = lds;
+  uint8_t* a1 = lds + DG_AB;
+  uint8_t* b0 = lds + 2 * DG_AB;
+  uint8_t* b1 = lds + 3 * DG_AB;
+  uint8_t* b2 = lds + 4 * DG_AB;
+  // prologue: A(0), B(0), then B(1), A(1); wait for the first two
+  const uint32_t oob1 = nk > 1 ? 0u : OOB;
+  A.issue(a0, w_wave, 0, 0u);
+  B.issue(b0, w_wave, 0, 0u);
+  B.issue(b1, w_wave, 1, oob1);
+  A.issue(a1, w_wave, 1, oob1);
+  __builtin_amdgcn_s_waitcnt(DG_WAIT_VM16_LGKM0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8_t af[2][4], bf[2][4];
+  load_frags<true, false, 0, MT>(af[0], bf[0], a0, b0, mlb, mlb, wm, wn, lane);
+  for (int s = 0; s < nk; ++s) {
+    dg_deep_body<MT>(acc, af, bf, A, B, mlb, wm, wn, lane, w_wave, s, a0, b0, a1, b1, b2, s + 2 < nk ? 0u : OOB);
+    uint8_t* t = a0; a0 = a1; a1 = t;
+    t = b0; b0 = b1; b1 = b2; b2 = t;
+  }
+  vm_wait<0>();  // the last (zero) loads land before LDS is reused
+  dgrad_epilogue<SWIGLU, OT>(acc, lds, wm, wn, tid, lane, Nd, n, row0, rows, ab, out);
+}
+
 // ------------------------------------------------------------ E4M3 dgrad --
 // The dgrad products with E4M3 operands: the activation gradient in 1x128
 // tiles along K (a power-of-two scale per row and 128 K), the weights in
@@ -741,8 +844,7 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
                                                     const int32_t* __restrict__ seg_offset, int Kd, int Nd,
                                                     uint32_t a_bytes, const uint16_t* __restrict__ ab,
                                                     OT* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[DG_LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ntn = (Nd + BT - 1) / BT;
@@ -770,11 +872,11 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
   int mt = (rows - wm * 128 + 31) >> 5;
   mt = __builtin_amdgcn_readfirstlane(mt < 0 ? 0 : (mt > 4 ? 4 : mt));
   switch (mt) {
-    case 4: dgrad_run<SWIGLU, OT, 4>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
-    case 3: dgrad_run<SWIGLU, OT, 3>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
-    case 2: dgrad_run<SWIGLU, OT, 2>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
-    case 1: dgrad_run<SWIGLU, OT, 1>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
-    default: dgrad_run<SWIGLU, OT, 0>(A, B, st0, st1, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 4: dgrad_run_deep<SWIGLU, OT, 4>(A, B, lds, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 3: dgrad_run_deep<SWIGLU, OT, 3>(A, B, lds, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 2: dgrad_run_deep<SWIGLU, OT, 2>(A, B, lds, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    case 1: dgrad_run_deep<SWIGLU, OT, 1>(A, B, lds, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
+    default: dgrad_run_deep<SWIGLU, OT, 0>(A, B, lds, mlb, wm, wn, tid, lane, w_wave, Kd, Nd, n, row0, rows, ab, out); break;
   }
 }
 
