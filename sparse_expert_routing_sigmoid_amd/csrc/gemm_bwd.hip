@@ -23,7 +23,8 @@
 //
 // Block tile 256 x 256 x 64 (K per stage), 4 waves in 2 x 2, each wave
 // 128 x 128 as 4 x 4 MFMA tiles of 32x32, fp32 accumulators; operands go
-// global -> LDS by the direct 16-byte buffer-to-LDS load, two stages.  LDS
+// global -> LDS by the direct 16-byte buffer-to-LDS load (two stages; the
+// bf16 dgrad keeps three weight stages, dgrad_run_deep).  LDS
 // tiles are XOR-swizzled at 16-byte granularity so that fragment reads hit
 // distinct banks: K-contiguous tiles as in the forward, M/N-contiguous tiles
 // by a XOR of the chunk index that depends on K-row % 4 (mnc_sw).
@@ -421,40 +422,6 @@ __device__ __forceinline__ void dgrad_epilogue(const f32x16_t (&acc)[4][4], uint
 }
 
 
-// K loop and epilogue of one dgrad item for a wave with MT live 32-row
-// groups (all instantiations run the same barriers).
-template <bool SWIGLU, typename OT, int MT>
-__device__ __forceinline__ void dgrad_run(const KcRows& A, const MncRows& B, uint8_t* __restrict__ st0,
-                                          uint8_t* __restrict__ st1, const MncLane& mlb, int wm, int wn, int tid,
-                                          int lane, int w_wave, int Kd, int Nd, int n, int row0, int rows,
-                                          const uint16_t* __restrict__ ab, OT* __restrict__ out) {
-  f32x16_t acc[4][4];
-  zero_acc(acc);
-  // Kd % 128 == 0, so the stage count is even and the loop body, two stages
-  // that name their buffers, has no branch: a branch lets the compiler sink
-  // MFMAs past the next barrier and costs registers.  The final issue loads
-  // zeros (out of range) into a buffer nobody reads.
-  const int nk = Kd / BKS;
-  A.issue(st0, w_wave, 0, 0u);
-  B.issue(st0 + BOP, w_wave, 0, 0u);
-  for (int s = 0; s < nk; s += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    A.issue(st1, w_wave, s + 1, 0u);
-    B.issue(st1 + BOP, w_wave, s + 1, 0u);
-    mma_stage<true, false, MT>(acc, st0, st0 + BOP, mlb, mlb, wm, wn, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint32_t oob = s + 2 < nk ? 0u : OOB;
-    A.issue(st0, w_wave, s + 2, oob);
-    B.issue(st0 + BOP, w_wave, s + 2, oob);
-    mma_stage<true, false, MT>(acc, st1, st1 + BOP, mlb, mlb, wm, wn, lane);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  dgrad_epilogue<SWIGLU, OT>(acc, st1, wm, wn, tid, lane, Nd, n, row0, rows, ab, out);
-}
-
 // bf16 dgrad K loop with three weight stages (the forward's layout): LDS
 // holds two 32 KB stages of the activation-gradient rows (A) and three of
 // the weight K-rows (B), 160 KB; B is loaded two stages ahead and A one, so
@@ -517,8 +484,9 @@ __device__ __forceinline__ void dg_deep_body(f32x16_t (&acc)[4][4], bf16x8_t (&a
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// K loop and epilogue of one bf16 dgrad item on the three-stage loop; lds:
-// DG_LDS bytes, the epilogue's staging in its first 64 KB.
+// K loop and epilogue of one bf16 dgrad item for a wave with MT live 32-row
+// groups (all instantiations run the same barriers); lds: DG_LDS bytes, the
+// epilogue's staging in its first 64 KB.
 constexpr int DG_AB = BT * 128;    // 32 KB: one stage of A or of B
 constexpr int DG_LDS = 5 * DG_AB;  // A0 A1 B0 B1 B2
 template <bool SWIGLU, typename OT, int MT>
@@ -731,7 +699,7 @@ __device__ __forceinline__ void dgrad_item(long long item, int ntn, int grp, con
   tile = t0 + g0 + r % gt;
 }
 
-// K loop and epilogue of one E4M3 dgrad item (see dgrad_run).  A stage
+// K loop and epilogue of one E4M3 dgrad item (see dgrad_run_deep).  A stage
 // buffer holds the activation rows (32 KB), the weight K-rows (32 KB) and
 // the row scales (1 KB).  Lane l holds the scales of the wave's weight
 // blocks for K blocks l and l + 64 (bsc0, bsc1).
