@@ -86,11 +86,11 @@ TRAFFIC = {
 # taken the same way from `--train` runs; keyed by workload, and for the
 # E4M3 step with bf16 weight gradients by workload + ":bf16wgrad".
 TRAIN_TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 51114372224, "write_bytes": 24303993241, "digest": "d775e1abb9759084",
+    "v3_prefill_bf16": {"fetch_bytes": 53626741930, "write_bytes": 24459432345, "digest": "9dbe4587a6172bf4",
                         "sources": ("gemm_bwd.hip", "common.h")},
-    "v3_train_fp8": {"fetch_bytes": 27641560413, "write_bytes": 27079476051, "digest": "8e1dc7bf20529fb8",
+    "v3_train_fp8": {"fetch_bytes": 27620137924, "write_bytes": 27167020063, "digest": "fd07b413cae5ea33",
                      "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
-    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 35254774912, "write_bytes": 25330469785, "digest": "8e1dc7bf20529fb8",
+    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 35409371468, "write_bytes": 25265441894, "digest": "fd07b413cae5ea33",
                                "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
 }
 
