@@ -24,7 +24,8 @@
 // Block tile 256 x 256 x 64 (K per stage), 4 waves in 2 x 2, each wave
 // 128 x 128 as 4 x 4 MFMA tiles of 32x32, fp32 accumulators; operands go
 // global -> LDS by the direct 16-byte buffer-to-LDS load (two stages; the
-// bf16 dgrad keeps three weight stages, dgrad_run_deep).  LDS
+// bf16 dgrad keeps three weight stages, dgrad_run_deep; the bf16 wgrad four
+// stages of 32 K-rows, wgrad_run).  LDS
 // tiles are XOR-swizzled at 16-byte granularity so that fragment reads hit
 // distinct banks: K-contiguous tiles as in the forward, M/N-contiguous tiles
 // by a XOR of the chunk index that depends on K-row % 4 (mnc_sw).
@@ -161,39 +162,67 @@ struct MncRows {
 };
 
 // The K-rows of one segment of the permuted layout (rows seg0 .. seg0 +
-// seglen - 1), for both operands of a weight gradient.  A K-row is live if it
-// lies in the segment and holds a token (row_token >= 0); dead K-rows load
-// zeros on both sides.  Operand A reads permuted row seg0 + k; operand B the
-// same row, or (GATHER) the token's row of x.  The loading waves (lw = 0 ..
-// 32 / NB - 1) issue NB 1 KB blocks of each operand apiece per stage; the
-// tokens of the next stage are fetched one stage ahead.
-template <bool GATHER, int NB>
-struct SegRows {
+// seglen - 1), for both operands of a weight gradient, in stages of WK
+// K-rows.  A K-row is live if it lies in the segment and holds a token
+// (row_token >= 0); dead K-rows load zeros on both sides.  Operand A reads
+// permuted row seg0 + k; operand B the same row, or (GATHER) the token's row
+// of x.  Wave w issues the 1 KB blocks g = WNB w .. WNB w + WNB - 1 of each
+// operand (block g: K-rows 2 g and 2 g + 1, one per half-wave).  The tokens
+// of a stage are loaded into one of four register slots, slot Q for the
+// stages k with k % 4 == Q, well before the stage's loads are issued.
+constexpr int WK = 32;         // K-rows per wgrad stage
+constexpr int WNB = 4;         // 1 KB blocks of each operand per wave and stage
+constexpr int WOP = WK * 512;  // bytes of one operand of a stage (16 KB)
+constexpr int WST = 2 * WOP;   // bytes of a stage: A, then B
+constexpr int WG_VM = 3 * WNB; // global accesses of a wave per stage: tokens + loads of both operands
+
+template <bool GATHER>
+struct SegRing {
   __amdgpu_buffer_rsrc_t ra, rb, rt;  // A, B, row_token
-  int seg0, seglen;
-  uint32_t a_rb, b_rb, a_c;  // row bytes, A tile column byte offset
-  int tok[NB];
-  __device__ void fetch(int s, int lw, int lane) {
+  int seglen;
+  uint32_t a_rs, b_rs;  // bytes of WK rows of A and of B (the scalar step per stage)
+  int kr0;              // K-row of this lane in block j = 0 (block j: kr0 + 2 j)
+  uint32_t a_off[WNB];  // byte offset of the lane's chunk of A in stage 0 (row seg0 + kr)
+  uint32_t b_off[WNB];  // the same for B (GATHER: column part only; the row comes from the token)
+  uint32_t t_off;       // byte offset of the lane's token of block 0 in stage 0
+  int tok[4][WNB];
+  __device__ void init(int seg0, int seg_len, uint32_t a_rb, uint32_t b_rb, uint32_t a_c, int w, int lane) {
+    seglen = seg_len;
+    a_rs = a_rb * WK;
+    b_rs = b_rb * WK;
+    kr0 = 2 * w * WNB + (lane >> 5);
+    t_off = (uint32_t)(seg0 + kr0) * 4u;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int k = s * BKS + 2 * (lw * NB + j) + (lane >> 5);
-      // K-rows past the segment load 0 (out of range); issue() masks them,
-      // so nothing here waits for the load
-      tok[j] = __builtin_amdgcn_raw_buffer_load_b32(rt, k < seglen ? (uint32_t)(seg0 + k) * 4u : OOB, 0, 0);
+    for (int j = 0; j < WNB; ++j) {
+      const int kr = kr0 + 2 * j;
+      const uint32_t c16 = (uint32_t)((lane & 31) ^ mnc_sw(kr & 3)) * 16u;
+      a_off[j] = (uint32_t)(seg0 + kr) * a_rb + a_c + c16;
+      b_off[j] = GATHER ? c16 : (uint32_t)(seg0 + kr) * b_rb + c16;
     }
   }
-  __device__ void issue(uint8_t* sa, uint8_t* sb, int lw, int lane, int s, uint32_t b_c, bool live) const {
+  // tokens of stage k into slot Q (K-rows past the segment read 0; issue()
+  // masks them, so nothing waits for these loads before the stage's issue)
+  template <int Q>
+  __device__ void fetch(int k) {
+    const int lim = seglen - k * WK;  // K-rows of stage k in the segment: kr < lim
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int g = lw * NB + j;
-      const int kr = 2 * g + (lane >> 5);
-      const uint32_t c16 = (uint32_t)((lane & 31) ^ mnc_sw(kr & 3)) * 16u;
-      const int row = seg0 + s * BKS + kr;
-      const bool ok = live && s * BKS + kr < seglen && tok[j] >= 0;
-      const uint32_t oa = ok ? (uint32_t)row * a_rb + a_c + c16 : OOB;
-      const uint32_t ob = ok ? (uint32_t)(GATHER ? tok[j] : row) * b_rb + b_c + c16 : OOB;
-      dma16(ra, sa + g * 1024, oa, 0);
-      dma16(rb, sb + g * 1024, ob, 0);
+    for (int j = 0; j < WNB; ++j)
+      tok[Q][j] = __builtin_amdgcn_raw_buffer_load_b32(rt, kr0 + 2 * j < lim ? t_off + 8u * j : OOB,
+                                                       (uint32_t)(k * WK * 4), 0);
+  }
+  // stage k of the tile whose B columns start at byte b_c, into stage buffer
+  // st (A at st, B at st + WOP); zeros unless live
+  template <int Q>
+  __device__ void issue(uint8_t* st, int w, int k, uint32_t b_c, bool live) const {
+    const int lim = live ? seglen - k * WK : 0;
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) {
+      const int g = w * WNB + j;
+      const bool ok = kr0 + 2 * j < lim && tok[Q][j] >= 0;
+      const uint32_t oa = ok ? a_off[j] : OOB;
+      const uint32_t ob = ok ? (GATHER ? __umul24((uint32_t)tok[Q][j], b_rs / WK) + b_c + b_off[j] : b_off[j] + b_c) : OOB;
+      dma16(ra, st + g * 1024, oa, (uint32_t)k * a_rs);
+      dma16(rb, st + WOP + g * 1024, ob, GATHER ? 0u : (uint32_t)k * b_rs);
     }
   }
 };
@@ -239,28 +268,6 @@ __device__ __forceinline__ void mma16(f32x16_t (&acc)[4][4], const bf16x8_t (&af
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-}
-
-// The four k-steps of one stage, fragments double-buffered.  MT: the 32-row
-// groups of the wave's A rows that hold rows (the others are neither read
-// nor multiplied; their accumulators stay zero).
-template <bool A_KC, bool B_KC, int MT = 4>
-__device__ __forceinline__ void mma_stage(f32x16_t (&acc)[4][4], const uint8_t* __restrict__ sa,
-                                          const uint8_t* __restrict__ sb, const MncLane& mla, const MncLane& mlb,
-                                          int wm, int wn, int lane) {
-  bf16x8_t f0[4], g0[4], f1[4], g1[4];
-  load_frags<A_KC, B_KC, 0, MT>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
-  load_frags<A_KC, B_KC, 1, MT>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
-  mma16<0, MT>(acc, f0, g0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_frags<A_KC, B_KC, 2, MT>(f0, g0, sa, sb, mla, mlb, wm, wn, lane);
-  mma16<1, MT>(acc, f1, g1);
-  __builtin_amdgcn_sched_barrier(0);
-  load_frags<A_KC, B_KC, 3, MT>(f1, g1, sa, sb, mla, mlb, wm, wn, lane);
-  mma16<2, MT>(acc, f0, g0);
-  __builtin_amdgcn_sched_barrier(0);
-  mma16<3, MT>(acc, f1, g1);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
@@ -851,130 +858,218 @@ __global__ __launch_bounds__(BTHREADS) void k_dgrad(const uint16_t* __restrict__
 // ------------------------------------------------------------- wgrad --
 constexpr int WG_STORES = 32;  // buffer stores per wave for one bf16 result tile
 
-// A wave's loads and stores share vmcnt and complete in issue order, so the
-// first wait of a tile whose predecessor's bf16 result stores (exactly
-// WG_STORES per wave) were issued after the loads it waits for lets those
-// stores stay in flight; every other wait is for everything (fp32 results
-// leave as a number of stores that depends on the columns).
-
-// One pair of stages of a wgrad K loop.  On entry st0 holds stage s
-// (complete and visible) and the loads of stage s + 1 into st1 are in
-// flight; `tok` holds the tokens of stage (s + 2) % nk.  Each buffer is
-// refilled as soon as every wave has read it: with the stage after next of
-// this N tile, or past its last stage the first stages of the next N tile
-// of the run (zeros after the last).
-template <bool GATHER>
-__device__ __forceinline__ void wgrad_pair(f32x16_t (&acc)[4][4], SegRows<GATHER, 8>& S, uint8_t* __restrict__ st0,
-                                           uint8_t* __restrict__ st1, const MncLane& mla, const MncLane& mlb, int wm,
-                                           int wn, int lane, int w_wave, int s, int nk, uint32_t bc, bool more,
-                                           bool after_store = false) {
-  const bool wrap = s + 2 == nk;
-  const uint32_t bn = wrap ? bc + BT * 2u : bc;
-  const bool live = !wrap || more;
-  mma_stage<false, false>(acc, st0, st0 + BOP, mla, mlb, wm, wn, lane);
-  if (after_store)
-    vm_wait<WG_STORES>();
-  else
-    vm_wait<0>();
-  lds_barrier();
-  S.issue(st0, st0 + BOP, w_wave, lane, wrap ? 0 : s + 2, bn, live);
-  S.fetch(wrap ? 1 : s + 3, w_wave, lane);
-  mma_stage<false, false>(acc, st1, st1 + BOP, mla, mlb, wm, wn, lane);
-  vm_wait<0>();
-  lds_barrier();
-  S.issue(st1, st1 + BOP, w_wave, lane, wrap ? 1 : s + 3, bn, live);
-  S.fetch(wrap ? (2 < nk ? 2 : 0) : (s + 4 < nk ? s + 4 : 0), w_wave, lane);
+// s_waitcnt for at most N global accesses of this wave in flight and none
+// of its LDS accesses (expcnt left at its maximum).
+template <int N>
+__device__ __forceinline__ void vm_lgkm0_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// The K loops and result tiles of one wgrad item (see k_wgrad).  bf16 result
-// tiles leave through a third LDS buffer (stq, 32 KB) in four quarters of 64
-// rows, so both stage buffers keep loading meanwhile: the tile's stores are
-// issued after the loads of the next tile's first two stages and drain
-// during the first stage of MFMAs of the next tile.
-template <bool GATHER, typename OT>
-__device__ __forceinline__ void wgrad_run(SegRows<GATHER, 8>& S, uint8_t* __restrict__ st0, uint8_t* __restrict__ st1,
-                                          uint8_t* __restrict__ stq, const MncLane& mla, const MncLane& mlb, int wm,
-                                          int wn, int tid, int lane, int w_wave, int m, int n0, int n1, int nk, int Md,
-                                          int Nd, OT* __restrict__ ob) {
-  constexpr bool BF16 = sizeof(OT) == 2;
-  S.fetch(0, w_wave, lane);
-  S.issue(st0, st0 + BOP, w_wave, lane, 0, (uint32_t)n0 * BT * 2u, nk > 0);
-  S.fetch(1, w_wave, lane);
-  S.issue(st1, st1 + BOP, w_wave, lane, 1, (uint32_t)n0 * BT * 2u, nk > 0);
-  S.fetch(2 < nk ? 2 : 0, w_wave, lane);
-  // The token loads may be moved freely (row_token is read-only); pin them
-  // here, so the first pair does not see them as still in flight.
+// The fragments of k-step KK of a wgrad stage (both operands M/N-contiguous).
+// The stage pointer is a restrict parameter so that these reads carry an
+// alias scope of their own, which the direct-to-LDS loads (plain pointers)
+// do not share: the compiler then adds no wait of its own on those loads
+// before the reads (the explicit waits of wg_stage order them).
+template <int KK>
+__device__ __forceinline__ void wg_frags(bf16x8_t (&af)[4], bf16x8_t (&bf)[4], const uint8_t* __restrict__ stg,
+                                         const MncLane& mla, const MncLane& mlb) {
+  af[0] = frag_mnc<0, KK>(stg, mla);
+  af[1] = frag_mnc<1, KK>(stg, mla);
+  af[2] = frag_mnc<2, KK>(stg, mla);
+  af[3] = frag_mnc<3, KK>(stg, mla);
+  bf[0] = frag_mnc<0, KK>(stg + WOP, mlb);
+  bf[1] = frag_mnc<1, KK>(stg + WOP, mlb);
+  bf[2] = frag_mnc<2, KK>(stg + WOP, mlb);
+  bf[3] = frag_mnc<3, KK>(stg + WOP, mlb);
+}
+
+// One stage k of the wgrad K loop (J = k % 4: stage buffer J, token slot J).
+// On entry the fragments of k-step 0 of stage k are in fa[0] / fb[0] and the
+// loads of stages k + 1 .. k + 3 are in flight.  The k-step-1 fragments are
+// read under the k-step-0 MFMAs; then the wave waits until stage k + 1 has
+// landed and its own reads of stage k are done (VMW: the global accesses it
+// issued after stage k + 1's loads, which may stay in flight), and the
+// barrier makes both hold for every wave.  Buffer J is then free: it takes
+// stage k_ld of the tile at column offset b_c (zeros unless live), behind
+// the tokens of stage k_tk into slot J + 3; the k-step-0 fragments of stage
+// k + 1 are read under the k-step-1 MFMAs.  A stage's loads thus have three
+// stages of MFMAs to land, and its tokens (issued three stages before the
+// loads that the wait before their use covers) never hold a wait back.
+template <bool GATHER, int J, int VMW>
+__device__ __forceinline__ void wg_stage(f32x16_t (&acc)[4][4], bf16x8_t (&fa)[2][4], bf16x8_t (&fb)[2][4],
+                                         SegRing<GATHER>& S, uint8_t* cur, const uint8_t* nxt, const MncLane& mla,
+                                         const MncLane& mlb, int lane, int w_wave, int k_ld, uint32_t b_c, bool live,
+                                         int k_tk) {
+  wg_frags<1>(fa[1], fb[1], cur, mla, mlb);
+  mma16<0, 4>(acc, fa[0], fb[0]);
+  dg_order_kstep<16, 16, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  vm_lgkm0_wait<VMW>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  S.template fetch<(J + 3) & 3>(k_tk);
+  S.template issue<J>(cur, w_wave, k_ld, b_c, live);
+  wg_frags<0>(fa[0], fb[0], nxt, mla, mlb);
+  mma16<1, 4>(acc, fa[1], fb[1]);
+  dg_order_kstep<16, 16, WG_VM>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stages kb .. kb + 3 of a tile with nk stages (nk % 4 == 0).  The loads
+// issued go to stages kb + 4 .. kb + 7 of this tile, or past its end to
+// stages 0 .. 3 of the next tile of the run (bn; zeros after the last);
+// tokens are fetched for stages kb + 7 .. kb + 10, taken modulo nk (every
+// tile of a run has the same K-rows).  FIRST: the first four stages of a
+// tile, whose first three waits may leave the previous tile's WG_STORES
+// result stores in flight (issued after the loads they wait for).
+template <bool GATHER, bool FIRST>
+__device__ __forceinline__ void wg_body(f32x16_t (&acc)[4][4], bf16x8_t (&fa)[2][4], bf16x8_t (&fb)[2][4],
+                                        SegRing<GATHER>& S, uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3,
+                                        const MncLane& mla,
+                                        const MncLane& mlb, int lane, int w_wave, int kb, int nk, uint32_t bc,
+                                        uint32_t bn, bool more) {
+  constexpr int W0 = 2 * WG_VM + (FIRST ? WG_STORES : 0);
+  constexpr int W3 = 2 * WG_VM;
+  const bool wrap = kb + 4 == nk;
+  const int k0 = wrap ? 0 : kb + 4;
+  const uint32_t b_c = wrap ? bn : bc;
+  const bool live = !wrap || more;
+  int kt[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(S.tok[j]));
-  vm_wait<0>();
-  lds_barrier();
-  for (int n = n0; n < n1; ++n) {
-    f32x16_t acc[4][4];
-    zero_acc(acc);
-    const uint32_t bc = (uint32_t)n * BT * 2u;
-    const bool more = n + 1 < n1;
-    // The first pair runs with the previous tile's stores still in flight.
-    // Its stage index is hidden from the compiler: as a constant it would
-    // hoist that pair's load addresses out of the N loop and spill them,
-    // and a reload from scratch would wait for the stores.
-    int s0 = 0;
-    asm volatile("" : "+s"(s0));
-    if (nk > 0) wgrad_pair(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s0, nk, bc, more, BF16 && n > n0);
-    for (int s = 2; s < nk; s += 2) wgrad_pair(acc, S, st0, st1, mla, mlb, wm, wn, lane, w_wave, s, nk, bc, more);
-    // (see mma16 for the accumulator layout)
-    if constexpr (BF16) {
-      // quarter qq: rows 64 qq .. 64 qq + 63 of the tile, held by the waves
-      // with wm = qq / 2 as their 32-row groups i = 2 (qq % 2), + 1; 16-byte
-      // chunk c of row r at chunk c ^ (r % 32); every thread then copies 8
-      // chunks out of full 512-byte rows with non-temporal buffer stores
-      // (columns past Nd are out of range and dropped).
-      const __amdgpu_buffer_rsrc_t ro = rsrc(ob, (uint32_t)Md * (uint32_t)Nd * 2u);
+  for (int j = 0; j < 4; ++j) {
+    int t = kb + 7 + j;
+    t -= t >= nk ? nk : 0;
+    t -= t >= nk ? nk : 0;
+    kt[j] = t;
+  }
+  wg_stage<GATHER, 0, W0>(acc, fa, fb, S, s0, s1, mla, mlb, lane, w_wave, k0, b_c, live, kt[0]);
+  wg_stage<GATHER, 1, W0>(acc, fa, fb, S, s1, s2, mla, mlb, lane, w_wave, k0 + 1, b_c, live, kt[1]);
+  wg_stage<GATHER, 2, W0>(acc, fa, fb, S, s2, s3, mla, mlb, lane, w_wave, k0 + 2, b_c, live, kt[2]);
+  wg_stage<GATHER, 3, W3>(acc, fa, fb, S, s3, s0, mla, mlb, lane, w_wave, k0 + 3, b_c, live, kt[3]);
+}
+
+// One 256 x 256 result tile of a weight gradient (see mma16 for the
+// accumulator layout).  bf16: through stq (32 KB) in four quarters of 64
+// rows; quarter qq holds rows 64 qq .. 64 qq + 63 of the tile, written by
+// the waves with wm = qq / 2 from their 32-row groups i = 2 (qq % 2), + 1;
+// 16-byte chunk c of row r sits at chunk c ^ (r % 32), and every thread
+// then copies 8 chunks out of full 512-byte rows with non-temporal buffer
+// stores, exactly WG_STORES per wave (columns past Nd are out of range and
+// dropped).  fp32: straight from the accumulators.
+template <typename OT>
+__device__ __forceinline__ void wgrad_store_tile(f32x16_t (&acc)[4][4], uint8_t* __restrict__ stq, int wm, int wn,
+                                                 int tid, int lane, int m, int n, int Md, int Nd,
+                                                 OT* __restrict__ ob) {
+  if constexpr (sizeof(OT) == 2) {
+    // Everything but the loads of the last stage issued (2 WNB) lands
+    // before the stores: the tokens the next tile's first stages use are
+    // then known to be in registers, and the compiler adds no wait of its
+    // own for them behind these stores.
+    vm_wait<2 * WNB>();
+    const __amdgpu_buffer_rsrc_t ro = rsrc(ob, (uint32_t)Md * (uint32_t)Nd * 2u);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        lds_barrier();
-        if (wm == qq / 2) {
+    for (int qq = 0; qq < 4; ++qq) {
+      lds_barrier();
+      if (wm == qq / 2) {
 #pragma unroll
-          for (int ii = 0; ii < 2; ++ii) {
-            const int i = 2 * (qq % 2) + ii;
-            const int row = ii * 32 + (lane & 31);
-            uint8_t* rp = stq + row * 512 + 8 * (lane >> 5);
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * (qq % 2) + ii;
+          const int row = ii * 32 + (lane & 31);
+          uint8_t* rp = stq + row * 512 + 8 * (lane >> 5);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int chunk = wn * 16 + j * 4 + q;
-                const float4 v = acc_get4(acc[i][j], q);
-                lds_st64(rp + ((chunk ^ (row & 31)) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-              }
-          }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int rr = 0; rr < WG_STORES / 4; ++rr) {
-          const int idx = rr * BTHREADS + tid, row = idx >> 5, chunk = idx & 31;
-          const uint4 v = *reinterpret_cast<const uint4*>(stq + row * 512 + ((chunk ^ (row & 31)) << 4));
-          const int grow = m * BT + qq * 64 + row, gcol = n * BT + chunk * 8;
-          const uint32_t off = grow < Md && gcol < Nd ? ((uint32_t)grow * (uint32_t)Nd + (uint32_t)gcol) * 2u : OOB;
-          typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-          const u32x4_t q = {v.x, v.y, v.z, v.w};
-          __builtin_amdgcn_raw_buffer_store_b128(q, ro, off, 0, 2);  // 2: non-temporal
+            for (int q = 0; q < 4; ++q) {
+              const int chunk = wn * 16 + j * 4 + q;
+              const float4 v = acc_get4(acc[i][j], q);
+              lds_st64(rp + ((chunk ^ (row & 31)) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+            }
         }
       }
-    } else {
+      lds_barrier();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m * BT + wm * 128 + i * 32 + (lane & 31);
-        if (r >= Md) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
-            if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
-          }
+      for (int rr = 0; rr < WG_STORES / 4; ++rr) {
+        const int idx = rr * BTHREADS + tid, row = idx >> 5, chunk = idx & 31;
+        const uint4 v = *reinterpret_cast<const uint4*>(stq + row * 512 + ((chunk ^ (row & 31)) << 4));
+        const int grow = m * BT + qq * 64 + row, gcol = n * BT + chunk * 8;
+        const uint32_t off = grow < Md && gcol < Nd ? ((uint32_t)grow * (uint32_t)Nd + (uint32_t)gcol) * 2u : OOB;
+        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t q = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(q, ro, off, 0, 2);  // 2: non-temporal
       }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = m * BT + wm * 128 + i * 32 + (lane & 31);
+      if (r >= Md) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n * BT + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (col < Nd) put4(ob + (long long)r * Nd + col, acc_get4(acc[i][j], q));
+        }
+    }
   }
+}
+
+// The K loops and result tiles of one wgrad item (see k_wgrad): the N
+// tiles n0 .. n1 - 1 of M tile m, nk stages each (nk % 4 == 0), as one
+// stream of stages through four stage buffers, the loads three stages
+// ahead across tile boundaries.  A tile's bf16 result stores are issued
+// after the loads of the next tile's first four stages and drain under its
+// first three stages; fp32 results are waited for at once.
+template <bool GATHER, typename OT>
+__device__ __forceinline__ void wgrad_run(SegRing<GATHER>& S, uint8_t* st, uint8_t* __restrict__ stq,
+                                          const MncLane& mla, const MncLane& mlb, int wm, int wn, int tid, int lane,
+                                          int w_wave, int m, int n0, int n1, int nk, int Md, int Nd,
+                                          OT* __restrict__ ob) {
+  f32x16_t acc[4][4];
+  if (nk == 0) {  // no rows: zero tiles
+    zero_acc(acc);
+    for (int n = n0; n < n1; ++n) wgrad_store_tile(acc, stq, wm, wn, tid, lane, m, n, Md, Nd, ob);
+    vm_wait<0>();
+    return;
+  }
+  // prologue: tokens and loads of stages 0 .. 3 (nk >= 4), tokens of stages
+  // 4 .. 6 (mod nk), everything landed before the first stage
+  const uint32_t bc0 = (uint32_t)n0 * BT * 2u;
+  S.template fetch<0>(0);
+  S.template fetch<1>(1);
+  S.template fetch<2>(2);
+  S.template fetch<3>(3);
+  S.template issue<0>(st, w_wave, 0, bc0, true);
+  S.template issue<1>(st + WST, w_wave, 1, bc0, true);
+  S.template issue<2>(st + 2 * WST, w_wave, 2, bc0, true);
+  S.template issue<3>(st + 3 * WST, w_wave, 3, bc0, true);
+  S.template fetch<0>(4 < nk ? 4 : 0);
+  S.template fetch<1>(5 < nk ? 5 : 1);
+  S.template fetch<2>(6 < nk ? 6 : 2);
+  // The token loads may be moved freely (row_token is read-only); pin them
+  // here, so the first stages do not see them as still in flight.
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) asm volatile("" ::"v"(S.tok[q][j]));
+  vm_wait<0>();
+  lds_barrier();
+  bf16x8_t fa[2][4], fb[2][4];
+  wg_frags<0>(fa[0], fb[0], st, mla, mlb);
+  for (int n = n0; n < n1; ++n) {
+    zero_acc(acc);
+    const uint32_t bc = (uint32_t)n * BT * 2u, bn = bc + BT * 2u;
+    const bool more = n + 1 < n1;
+    wg_body<GATHER, true>(acc, fa, fb, S, st, st + WST, st + 2 * WST, st + 3 * WST, mla, mlb, lane, w_wave, 0, nk,
+                          bc, bn, more);
+    for (int kb = 4; kb < nk; kb += 4)
+      wg_body<GATHER, false>(acc, fa, fb, S, st, st + WST, st + 2 * WST, st + 3 * WST, mla, mlb, lane, w_wave, kb,
+                             nk, bc, bn, more);
+    wgrad_store_tile(acc, stq, wm, wn, tid, lane, m, n, Md, Nd, ob);
+    if constexpr (sizeof(OT) != 2) vm_wait<0>();
+  }
+  vm_wait<0>();  // the last (zero) loads land before the block's LDS is released
 }
 
 // The routed experts of the wgrad dealt to the 8 XCDs by their (padded)
@@ -1049,34 +1144,34 @@ __global__ __launch_bounds__(BTHREADS) void k_wgrad(const uint16_t* __restrict__
                                                     const int32_t* __restrict__ row_token, int P_rows, int E, int Nr,
                                                     int Md, int Nd, int nch, uint32_t a_bytes, uint32_t b_bytes,
                                                     const int* __restrict__ deal, OT* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * BOP];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * BOP];
-  __shared__ __attribute__((aligned(1024))) uint8_t stq[BOP];
+  // One LDS array for the four stages and the result staging: with two
+  // arrays the compiler tags their accesses with alias scopes and then waits
+  // for every direct-to-LDS load in flight before each fragment read.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * WST + BOP];
+  uint8_t* st = lds;
+  uint8_t* stq = lds + 4 * WST;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int e, m, n0, n1;
   if (!wgrad_item(E, Nr, (Md + BT - 1) / BT, (Nd + BT - 1) / BT, nch, deal, e, m, n0, n1)) return;
   const int w_wave = __builtin_amdgcn_readfirstlane(wave);
 
-  SegRows<GATHER, 8> S;
+  SegRing<GATHER> S;
   S.ra = rsrc(a, a_bytes);
   S.rb = rsrc(b, b_bytes);
   S.rt = rsrc(row_token, (uint32_t)P_rows * 4u);
-  S.seg0 = seg_offset[e];
-  S.seglen = seg_offset[e + 1] - S.seg0;
-  S.a_rb = (uint32_t)Md * 2u;
-  S.b_rb = (uint32_t)Nd * 2u;
-  S.a_c = (uint32_t)m * BT * 2u;
+  const int seg0 = seg_offset[e];
+  S.init(seg0, seg_offset[e + 1] - seg0, (uint32_t)Md * 2u, (uint32_t)Nd * 2u, (uint32_t)m * BT * 2u, w_wave, lane);
 
   MncLane mla, mlb;
   mla.init(wm, lane);
   mlb.init(wn, lane);
   OT* ob = out + (long long)e * Md * Nd;
-  // Stages rounded up to an even count (the extra stage loads zeros), so the
-  // two-stage loop body has no branch on the stage.  No rows: nk = 0 and
-  // zeros are stored.
-  const int nk = (S.seglen + 2 * BKS - 1) / (2 * BKS) * 2;
-  wgrad_run(S, st0, st1, stq, mla, mlb, wm, wn, tid, lane, w_wave, m, n0, n1, nk, Md, Nd, ob);
+  // Stages rounded up to a multiple of four (the extra stages load zeros),
+  // so the loop body (four stages) has no branch on the stage.  No rows:
+  // nk = 0 and zeros are stored.
+  const int nk = (S.seglen + 4 * WK - 1) / (4 * WK) * 4;
+  wgrad_run(S, st, stq, mla, mlb, wm, wn, tid, lane, w_wave, m, n0, n1, nk, Md, Nd, ob);
 }
 
 // Blocks of k_wgrad: 8 XCDs x (a share of the shared items + the items of
@@ -1203,6 +1298,11 @@ template <typename OT>
 __device__ __forceinline__ void wgrad8_store(const f32x16_t (&acc)[4][4], uint8_t* stw,
                                              OT* ob, int Md, int Nd, int r0, int c0, int lane) {
   if constexpr (sizeof(OT) == 2) {
+    // Everything but the loads of the last stage issued (2 WNB) lands
+    // before the stores: the tokens the next tile's first stages use are
+    // then known to be in registers, and the compiler adds no wait of its
+    // own for them behind these stores.
+    vm_wait<2 * WNB>();
     const __amdgpu_buffer_rsrc_t ro = rsrc(ob, (uint32_t)Md * (uint32_t)Nd * 2u);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
