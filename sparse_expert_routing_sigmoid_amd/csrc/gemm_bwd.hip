@@ -951,12 +951,13 @@ __device__ __forceinline__ void wg_body(f32x16_t (&acc)[4][4], bf16x8_t (&fa)[2]
 
 // One 256 x 256 result tile of a weight gradient (see mma16 for the
 // accumulator layout).  bf16: through stq (32 KB) in four quarters of 64
-// rows; quarter qq holds rows 64 qq .. 64 qq + 63 of the tile, written by
-// the waves with wm = qq / 2 from their 32-row groups i = 2 (qq % 2), + 1;
-// 16-byte chunk c of row r sits at chunk c ^ (r % 32), and every thread
-// then copies 8 chunks out of full 512-byte rows with non-temporal buffer
-// stores, exactly WG_STORES per wave (columns past Nd are out of range and
-// dropped).  fp32: straight from the accumulators.
+// rows; quarter qq holds the 32-row group i = qq of every wave: stq row
+// 32 wm + r is tile row 128 wm + 32 qq + r, so all four waves convert and
+// write their share in every quarter (the conversion is the quarter's
+// critical path).  16-byte chunk c of stq row r sits at chunk c ^ (r % 32),
+// and every thread then copies 8 chunks out of full 512-byte rows with
+// non-temporal buffer stores, exactly WG_STORES per wave (columns past Nd
+// are out of range and dropped).  fp32: straight from the accumulators.
 template <typename OT>
 __device__ __forceinline__ void wgrad_store_tile(f32x16_t (&acc)[4][4], uint8_t* __restrict__ stq, int wm, int wn,
                                                  int tid, int lane, int m, int n, int Md, int Nd,
@@ -971,28 +972,24 @@ __device__ __forceinline__ void wgrad_store_tile(f32x16_t (&acc)[4][4], uint8_t*
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       lds_barrier();
-      if (wm == qq / 2) {
+      {
+        const int row = wm * 32 + (lane & 31);
+        uint8_t* rp = stq + row * 512 + 8 * (lane >> 5);
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * (qq % 2) + ii;
-          const int row = ii * 32 + (lane & 31);
-          uint8_t* rp = stq + row * 512 + 8 * (lane >> 5);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int chunk = wn * 16 + j * 4 + q;
-              const float4 v = acc_get4(acc[i][j], q);
-              lds_st64(rp + ((chunk ^ (row & 31)) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-            }
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int chunk = wn * 16 + j * 4 + q;
+            const float4 v = acc_get4(acc[qq][j], q);
+            lds_st64(rp + ((chunk ^ (row & 31)) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+          }
       }
       lds_barrier();
 #pragma unroll
       for (int rr = 0; rr < WG_STORES / 4; ++rr) {
         const int idx = rr * BTHREADS + tid, row = idx >> 5, chunk = idx & 31;
         const uint4 v = *reinterpret_cast<const uint4*>(stq + row * 512 + ((chunk ^ (row & 31)) << 4));
-        const int grow = m * BT + qq * 64 + row, gcol = n * BT + chunk * 8;
+        const int grow = m * BT + (row >> 5) * 128 + qq * 32 + (row & 31), gcol = n * BT + chunk * 8;
         const uint32_t off = grow < Md && gcol < Nd ? ((uint32_t)grow * (uint32_t)Nd + (uint32_t)gcol) * 2u : OOB;
         typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
         const u32x4_t q = {v.x, v.y, v.z, v.w};
