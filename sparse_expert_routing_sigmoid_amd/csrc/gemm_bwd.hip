@@ -1285,12 +1285,12 @@ __device__ __forceinline__ void mma_run8(f32x16_t (&acc)[4][4], const uint8_t* s
 
 // A result tile of one wave (its 128 x 128, see mma16 for the accumulator
 // layout; r0, c0: output row and column of its element 0).  bf16: through
-// the wave's own 4 KB of LDS, 16 rows at a time (16-byte chunk c of row r at
-// chunk c ^ r; written with lds_st64, which the compiler does not order
-// against the direct-to-LDS loads), read back as whole 256-byte rows and
-// stored with non-temporal buffer stores, 4 rows per instruction, 32 in
-// all; no workgroup barrier.  Columns past Nd are out of range.  fp32:
-// straight from the accumulators.
+// the wave's own 4 KB of LDS, 32 rows x 64 columns at a time, so every lane
+// converts its own values in every round (written with lds_st64, which the
+// compiler does not order against the direct-to-LDS loads), read back as
+// whole 128-byte row pieces and stored with non-temporal buffer stores, 8
+// rows per instruction, 32 in all; no workgroup barrier.  Columns past Nd
+// are out of range.  fp32: straight from the accumulators.
 template <typename OT>
 __device__ __forceinline__ void wgrad8_store(const f32x16_t (&acc)[4][4], uint8_t* stw,
                                              OT* ob, int Md, int Nd, int r0, int c0, int lane) {
@@ -1304,17 +1304,20 @@ __device__ __forceinline__ void wgrad8_store(const f32x16_t (&acc)[4][4], uint8_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (((lane >> 4) & 1) == half) {
-          const int rho = lane & 15;
-          uint8_t* rp = stw + rho * 256 + 8 * (lane >> 5);
+      for (int jh = 0; jh < 2; ++jh) {
+        // round (i, jh): the wave's 32 rows of group i, columns of the MFMA
+        // tiles j = 2 jh, 2 jh + 1 (64 columns, 128 bytes a row), every lane
+        // converting its own values; chunk c of row r at chunk c ^ (r % 8)
+        {
+          const int row = lane & 31;
+          uint8_t* rp = stw + row * 128 + 8 * (lane >> 5);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int chunk = j * 4 + q;
-              const float4 v = acc_get4(acc[i][j], q);
-              lds_st64(rp + ((chunk ^ rho) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+              const int chunk = jj * 4 + q;
+              const float4 v = acc_get4(acc[i][2 * jh + jj], q);
+              lds_st64(rp + ((chunk ^ (row & 7)) << 4), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
             }
         }
         // the rows are read back by other lanes: the wave's LDS writes must
@@ -1323,9 +1326,9 @@ __device__ __forceinline__ void wgrad8_store(const f32x16_t (&acc)[4][4], uint8_
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 4 * r + (lane >> 4), chunk = lane & 15;
-          const uint4 v = *reinterpret_cast<const uint4*>(stw + row * 256 + ((chunk ^ row) << 4));
-          const int grow = r0 + i * 32 + half * 16 + row, gcol = c0 + chunk * 8;
+          const int row = 8 * r + (lane >> 3), chunk = lane & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(stw + row * 128 + ((chunk ^ (row & 7)) << 4));
+          const int grow = r0 + i * 32 + row, gcol = c0 + jh * 64 + chunk * 8;
           const uint32_t off = gcol < Nd ? ((uint32_t)grow * (uint32_t)Nd + (uint32_t)gcol) * 2u : OOB;
           typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
           const u32x4_t w = {v.x, v.y, v.z, v.w};
