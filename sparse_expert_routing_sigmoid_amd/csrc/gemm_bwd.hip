@@ -345,9 +345,11 @@ __device__ __forceinline__ void vm_wait() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // A 256 x 256 bf16 result tile leaves through a free 64 KB stage buffer in
-// two halves of 128 rows: the waves of the half write their accumulators as
-// bf16 (16-byte chunk c of row r at chunk c ^ (r % 32), so the 32 rows one
-// write instruction touches fall on different banks), then every thread
+// two halves of 128 rows: half h holds the 32-row groups 2 h and 2 h + 1 of
+// every wave (buffer row 64 wm + 32 (i - 2 h) + r is tile row
+// 128 wm + 32 i + r), so all four waves convert in both halves; 16-byte
+// chunk c of buffer row r sits at chunk c ^ (r % 32), so the 32 rows one
+// write instruction touches fall on different banks; then every thread
 // copies 16-byte chunks out, two full 512-byte rows per wave instruction
 // (non-temporal stores).
 // Rows >= rows_valid and columns >= cols_valid are not written.
@@ -357,28 +359,27 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16_t (&acc)[4][4], uin
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
-    if (wm == half) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = i * 32 + (lane & 31);
-        uint8_t* rp = stg + row * 512 + 8 * (lane >> 5);
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * half + ii;
+      const int row = wm * 64 + ii * 32 + (lane & 31);
+      uint8_t* rp = stg + row * 512 + 8 * (lane >> 5);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int chunk = wn * 16 + j * 4 + q;
-            const float4 v = acc_get4(acc[i][j], q);
-            *reinterpret_cast<uint2*>(rp + ((chunk ^ (row & 31)) << 4)) =
-                make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-          }
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int chunk = wn * 16 + j * 4 + q;
+          const float4 v = acc_get4(acc[i][j], q);
+          *reinterpret_cast<uint2*>(rp + ((chunk ^ (row & 31)) << 4)) =
+              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        }
     }
     __syncthreads();
 #pragma unroll 4
     for (int rr = 0; rr < 16; ++rr) {
       const int idx = rr * BTHREADS + tid, row = idx >> 5, chunk = idx & 31;
       const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 512 + ((chunk ^ (row & 31)) << 4));
-      const int grow = half * 128 + row;
+      const int grow = (row >> 6) * 128 + half * 64 + (row & 63);
       if (grow < rows_valid && chunk * 8 < cols_valid)
         nt_store16(out + grow * ld + chunk * 8, v);
     }
