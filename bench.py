@@ -71,13 +71,13 @@ def parse():
 # factor the same counters give for a plain copy of known size).  Valid only
 # for the kernel sources they were taken on: a changed source gives null.
 TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 36386514944, "write_bytes": 1359597158, "digest": "fa2660644de4db0d"},
-    "v3_prefill_fp8": {"fetch_bytes": 28487229440, "write_bytes": 2472013209, "digest": "fa2660644de4db0d"},
-    "v3_decode_fp8w": {"fetch_bytes": 11297040384, "write_bytes": 21428791, "digest": "26c47dd95af81869"},
+    "v3_prefill_bf16": {"fetch_bytes": 36420200448, "write_bytes": 1359596134, "digest": "0cad120530f2390f"},
+    "v3_prefill_fp8": {"fetch_bytes": 28308518912, "write_bytes": 2472101068, "digest": "0cad120530f2390f"},
+    "v3_decode_fp8w": {"fetch_bytes": 11296614400, "write_bytes": 21416633, "digest": "07612974f52de25f"},
     # moe_expert_gemm_combine (--fused-combine): k_fused_prep + both phases
-    "v3_prefill_bf16:fused": {"fetch_bytes": 37123061514, "write_bytes": 2653917798, "digest": "cde06645bb9ca92d",
+    "v3_prefill_bf16:fused": {"fetch_bytes": 37136534056, "write_bytes": 2653921382, "digest": "a14063dd68e34507",
                               "sources": ("gemm_mfma.hip", "elementwise.hip", "common.h")},
-    "v3_prefill_fp8:fused": {"fetch_bytes": 28890714112, "write_bytes": 5059960217, "digest": "cde06645bb9ca92d",
+    "v3_prefill_fp8:fused": {"fetch_bytes": 28748369100, "write_bytes": 5060349440, "digest": "a14063dd68e34507",
                              "sources": ("gemm_mfma.hip", "elementwise.hip", "common.h")},
 }
 
@@ -86,11 +86,11 @@ TRAFFIC = {
 # taken the same way from `--train` runs; keyed by workload, and for the
 # E4M3 step with bf16 weight gradients by workload + ":bf16wgrad".
 TRAIN_TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 53626741930, "write_bytes": 24459432345, "digest": "9dbe4587a6172bf4",
+    "v3_prefill_bf16": {"fetch_bytes": 50849053824, "write_bytes": 24476222976, "digest": "4b441e056e44c76a",
                         "sources": ("gemm_bwd.hip", "common.h")},
-    "v3_train_fp8": {"fetch_bytes": 27620137924, "write_bytes": 27167020063, "digest": "fd07b413cae5ea33",
+    "v3_train_fp8": {"fetch_bytes": 27867554961, "write_bytes": 26992763423, "digest": "1cc3ea766cb60c69",
                      "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
-    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 35409371468, "write_bytes": 25265441894, "digest": "fd07b413cae5ea33",
+    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 32586135065, "write_bytes": 25486114304, "digest": "1cc3ea766cb60c69",
                                "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
 }
 
