@@ -901,19 +901,25 @@ template <bool GATHER, int J, int VMW>
 __device__ __forceinline__ void wg_stage(f32x16_t (&acc)[4][4], bf16x8_t (&fa)[2][4], bf16x8_t (&fb)[2][4],
                                          SegRing<GATHER>& S, uint8_t* cur, const uint8_t* nxt, const MncLane& mla,
                                          const MncLane& mlb, int lane, int w_wave, int k_ld, uint32_t b_c, bool live,
-                                         int k_tk) {
-  wg_frags<1>(fa[1], fb[1], cur, mla, mlb);
-  mma16<0, 4>(acc, fa[0], fb[0]);
-  dg_order_kstep<16, 16, 0>();
+                                         int k_tk, bool real) {
+  if (real) {
+    wg_frags<1>(fa[1], fb[1], cur, mla, mlb);
+    mma16<0, 4>(acc, fa[0], fb[0]);
+    dg_order_kstep<16, 16, 0>();
+  }
   __builtin_amdgcn_sched_barrier(0);
   vm_lgkm0_wait<VMW>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   S.template fetch<(J + 3) & 3>(k_tk);
   S.template issue<J>(cur, w_wave, k_ld, b_c, live);
-  wg_frags<0>(fa[0], fb[0], nxt, mla, mlb);
-  mma16<1, 4>(acc, fa[1], fb[1]);
-  dg_order_kstep<16, 16, WG_VM>();
+  if (real) {
+    wg_frags<0>(fa[0], fb[0], nxt, mla, mlb);
+    mma16<1, 4>(acc, fa[1], fb[1]);
+    dg_order_kstep<16, 16, 0>();
+  } else {  // a stage of zero K-rows: nothing to multiply
+    wg_frags<0>(fa[0], fb[0], nxt, mla, mlb);
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -944,10 +950,11 @@ __device__ __forceinline__ void wg_body(f32x16_t (&acc)[4][4], bf16x8_t (&fa)[2]
     t -= t >= nk ? nk : 0;
     kt[j] = t;
   }
-  wg_stage<GATHER, 0, W0>(acc, fa, fb, S, s0, s1, mla, mlb, lane, w_wave, k0, b_c, live, kt[0]);
-  wg_stage<GATHER, 1, W0>(acc, fa, fb, S, s1, s2, mla, mlb, lane, w_wave, k0 + 1, b_c, live, kt[1]);
-  wg_stage<GATHER, 2, W0>(acc, fa, fb, S, s2, s3, mla, mlb, lane, w_wave, k0 + 2, b_c, live, kt[2]);
-  wg_stage<GATHER, 3, W3>(acc, fa, fb, S, s3, s0, mla, mlb, lane, w_wave, k0 + 3, b_c, live, kt[3]);
+  const int nreal = (S.seglen + WK - 1) / WK;  // stages that hold K-rows
+  wg_stage<GATHER, 0, W0>(acc, fa, fb, S, s0, s1, mla, mlb, lane, w_wave, k0, b_c, live, kt[0], kb < nreal);
+  wg_stage<GATHER, 1, W0>(acc, fa, fb, S, s1, s2, mla, mlb, lane, w_wave, k0 + 1, b_c, live, kt[1], kb + 1 < nreal);
+  wg_stage<GATHER, 2, W0>(acc, fa, fb, S, s2, s3, mla, mlb, lane, w_wave, k0 + 2, b_c, live, kt[2], kb + 2 < nreal);
+  wg_stage<GATHER, 3, W3>(acc, fa, fb, S, s3, s0, mla, mlb, lane, w_wave, k0 + 3, b_c, live, kt[3], kb + 3 < nreal);
 }
 
 // One 256 x 256 result tile of a weight gradient (see mma16 for the
