@@ -86,11 +86,11 @@ TRAFFIC = {
 # taken the same way from `--train` runs; keyed by workload, and for the
 # E4M3 step with bf16 weight gradients by workload + ":bf16wgrad".
 TRAIN_TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 50849053824, "write_bytes": 24476222976, "digest": "4b441e056e44c76a",
+    "v3_prefill_bf16": {"fetch_bytes": 50881294250, "write_bytes": 24487474912, "digest": "1703d8e9b52a6041",
                         "sources": ("gemm_bwd.hip", "common.h")},
-    "v3_train_fp8": {"fetch_bytes": 27867554961, "write_bytes": 26992763423, "digest": "1cc3ea766cb60c69",
+    "v3_train_fp8": {"fetch_bytes": 27657010645, "write_bytes": 26985784117, "digest": "54571ef9a8c642ec",
                      "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
-    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 32586135065, "write_bytes": 25486114304, "digest": "1cc3ea766cb60c69",
+    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 32783964672, "write_bytes": 25267414912, "digest": "54571ef9a8c642ec",
                                "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
 }
 
