@@ -471,9 +471,10 @@ def train_main(args, cfg, dev, stream):
                    "k_wgrad (down), k_wgrad (gate/up)")
     elif wgrad8:
         peak = PEAK["fp8"]
-        kernels = ("moe_expert_gemm_backward_f8 call: k_quant_1x128 (dy), k_dgrad8 (down + SwiGLU backward), "
-                   "k_quant_1x128 ([da|db]), k_dgrad8 (gate/up), k_run_offsets, 4 x k_quant_runs (dy, h, [da|db], "
-                   "gathered x), k_wgrad_deal, k_wgrad8 (down), k_wgrad8 (gate/up); every product E4M3")
+        kernels = ("moe_expert_gemm_backward_f8 call: k_run_offsets, k_quant_runs (dy: runs and 1x128 tiles), "
+                   "k_dgrad8 (down + SwiGLU backward), k_quant_runs ([da|db]: runs and 1x128 tiles), k_dgrad8 "
+                   "(gate/up), k_quant_runs (h), k_quant_runs (gathered x), k_wgrad_deal, k_wgrad8 (down), "
+                   "k_wgrad8 (gate/up); every product E4M3")
     else:
         # half the flops (the input-gradient products) at the E4M3 peak, half
         # (the weight gradients) at the bf16 peak: the call's time at peak

@@ -505,7 +505,9 @@ moe_status moe_expert_gemm_backward_w8(const void* x, const uint8_t* w13, const 
  * (fp32 accumulation).  dy and [da | db] are quantised from their bf16
  * values; h and x are the bf16 operands of the forward (after the E4M3
  * forward: the decoded E4M3 h and Q(u), exact in bf16), quantised again
- * along the tokens.  dx as in moe_expert_gemm_backward_w8.
+ * along the tokens.  dx as in moe_expert_gemm_backward_w8.  dy and
+ * [da | db] are each read once for both of their E4M3 layouts (the 1x128
+ * tiles of the input-gradient products and the token runs).
  *   ws  device, moe_gemm_backward_f8_workspace_bytes(...) bytes
  *   every other argument as moe_expert_gemm_backward_w8
  *   Errors: as moe_expert_gemm_backward_w8.

@@ -48,8 +48,9 @@ void launch_ffn_bwd_f8(const uint16_t* x, const uint8_t* w13, const float* w13s,
                        const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
                        const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
                        int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
-                       uint8_t* dabq, float* dabs, uint8_t* hr, uint8_t* xr, float* dyrs, float* hrs, float* dabrs,
-                       float* xrs, int32_t* run_offset, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
+                       uint8_t* dabq, float* dabs, uint8_t* hr, uint8_t* xr, uint8_t* dyr, uint8_t* dabr,
+                       float* dyrs, float* hrs, float* dabrs, float* xrs, int32_t* run_offset, int* deal, uint16_t* dx,
+                       void* dw13, void* dw2, bool dw_f32,
                        hipStream_t st);
 long long quantize_runs_max(long long P, int n_seg);
 void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, const uint16_t* h,
@@ -468,18 +469,20 @@ size_t gemm_backward_w8_workspace_bytes(int T, int K, int Nr, int Ns, int d, int
   return W8Ws(permute_rows(T, K, Nr, Ns, tile_m), d, I, Nr).total;
 }
 
-// Workspace of the all-E4M3 backward: W8Ws, then the run codes of h and of
-// the gathered x, the four run-scale arrays [runs, C] (dy, h, [da | db], x)
-// and run_offset [Nr + Ns + 1].
+// Workspace of the all-E4M3 backward: W8Ws, then the run codes of h, of the
+// gathered x, of dy and of [da | db], the four run-scale arrays [runs, C]
+// (dy, h, [da | db], x) and run_offset [Nr + Ns + 1].
 struct F8Ws {
   W8Ws w8;
-  size_t hr, xr, dyrs, hrs, dabrs, xrs, run_offset, total;
+  size_t hr, xr, dyr, dabr, dyrs, hrs, dabrs, xrs, run_offset, total;
   F8Ws(size_t P, int d, int I, int Nr, int Ns) : w8(P, d, I, Nr) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t runs = (size_t)quantize_runs_max((long long)P, Nr + Ns);
     hr = up(w8.total);
     xr = hr + up(P * I);
-    dyrs = xr + up(P * d);
+    dyr = xr + up(P * d);
+    dabr = dyr + up(P * d);
+    dyrs = dabr + up(P * 2 * I);
     hrs = dyrs + up(runs * d * 4);
     dabrs = hrs + up(runs * I * 4);
     xrs = dabrs + up(runs * 2 * I * 4);
@@ -538,7 +541,8 @@ moe_status expert_gemm_backward_f8(const void* x, const uint8_t* w13, const floa
   launch_ffn_bwd_f8(cp<uint16_t>(x), w13, w13_scale, w2, w2_scale, cp<uint16_t>(h), cp<uint16_t>(ab),
                     cp<uint16_t>(dy), seg_offset, row_token, tile_map, n_tiles, tiles_max, T, (long long)P, d, I, Nr,
                     Ns, reinterpret_cast<uint16_t*>(wb + L.w8.dab), wb + L.w8.dyq, f(L.w8.dys), wb + L.w8.dabq,
-                    f(L.w8.dabs), wb + L.hr, wb + L.xr, f(L.dyrs), f(L.hrs), f(L.dabrs), f(L.xrs),
+                    f(L.w8.dabs), wb + L.hr, wb + L.xr, wb + L.dyr, wb + L.dabr, f(L.dyrs), f(L.hrs), f(L.dabrs),
+                    f(L.xrs),
                     reinterpret_cast<int32_t*>(wb + L.run_offset), reinterpret_cast<int*>(wb + L.w8.deal),
                     static_cast<uint16_t*>(dx), dw13, dw2, dw_t == MOE_F32, as_stream(stream));
   return launch_status("moe_expert_gemm_backward_f8");

@@ -372,13 +372,17 @@ __global__ __launch_bounds__(1024) void k_run_offsets(const int32_t* __restrict_
 // RNE(x / scale) as in the tile quantisers.  Source row of permuted row r:
 // row_token[r] (GATHER, x [x_rows, cols]) or r itself (x [P, cols]); a row
 // whose row_token is negative (padding), or names no row of x, counts as
-// zeros, and its codes are written as 0.
-template <typename XT, bool GATHER>
+// zeros, and its codes are written as 0.  ROW1 (x [P, cols]): the same
+// values are also quantised in 1x128 row tiles into q_tile [P, cols] and
+// s_tile [P, cols / 128], as k_quant_1x128 does, so a tensor that needs both
+// layouts is read once; rows outside every segment are not written.
+template <typename XT, bool GATHER, bool ROW1>
 __global__ __launch_bounds__(256) void k_quant_runs(const XT* __restrict__ x, long long x_rows, int cols,
                                                     const int32_t* __restrict__ row_token,
                                                     const int32_t* __restrict__ seg_offset,
                                                     const int32_t* __restrict__ run_offset, int n, long long P,
-                                                    uint8_t* __restrict__ q, float* __restrict__ scale) {
+                                                    uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                    uint8_t* __restrict__ q_tile, float* __restrict__ s_tile) {
   __shared__ float red[8][256];
   __shared__ int kexp[256];
   const int g = blockIdx.x;
@@ -424,6 +428,28 @@ __global__ __launch_bounds__(256) void k_quant_runs(const XT* __restrict__ x, lo
     for (int r = 0; r < 16; ++r)
 #pragma unroll
       for (int c = 0; c < 8; ++c) v[r][c] = 0.f;
+  }
+  if constexpr (ROW1) {
+    // a row's 1x128 tile is held by the 16 lanes of a wave with this rg and
+    // this half of the 256-column chunk (lane bits 0-3 = cg & 15)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float m = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(v[r][c]));
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      const int k = pow2_scale_exp(m);
+      const float iv = exp2_int(-k);
+      const int row = row0 + 16 * rg + r;
+      if (live_col && row < row_end) {
+        uint2 w;
+        w.x = e4m3x4(v[r][0] * iv, v[r][1] * iv, v[r][2] * iv, v[r][3] * iv);
+        w.y = e4m3x4(v[r][4] * iv, v[r][5] * iv, v[r][6] * iv, v[r][7] * iv);
+        *reinterpret_cast<uint2*>(q_tile + (long long)row * cols + col) = w;
+        if ((cg & 15) == 0) s_tile[(long long)row * (cols / 128) + col / 128] = exp2_int(k);
+      }
+    }
   }
   float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -561,18 +587,19 @@ long long quantize_runs_max(long long P, int n_seg) { return (P + 127LL * n_seg)
 
 void launch_quantize_runs(const void* x, bool x_f32, long long x_rows, int cols, const int32_t* row_token,
                           bool gather, const int32_t* seg_offset, int n_seg, long long P, int32_t* run_offset,
-                          bool offsets, uint8_t* q, float* scale, hipStream_t st) {
+                          bool offsets, uint8_t* q, float* scale, hipStream_t st, uint8_t* q1, float* s1) {
   if (offsets) hipLaunchKernelGGL(k_run_offsets, dim3(1), dim3(1024), 0, st, seg_offset, n_seg, P, run_offset);
   const long long runs = quantize_runs_max(P, n_seg);
   if (runs == 0 || cols == 0) return;
   const dim3 grid((unsigned)runs, (unsigned)((cols + 255) / 256));
-#define QR_LAUNCH(XT, G)                                                                                            \
-  hipLaunchKernelGGL((k_quant_runs<XT, G>), grid, dim3(256), 0, st, static_cast<const XT*>(x), x_rows, cols,       \
-                     row_token, seg_offset, run_offset, n_seg, P, q, scale)
+#define QR_LAUNCH(XT, G, R1)                                                                                        \
+  hipLaunchKernelGGL((k_quant_runs<XT, G, R1>), grid, dim3(256), 0, st, static_cast<const XT*>(x), x_rows, cols,   \
+                     row_token, seg_offset, run_offset, n_seg, P, q, scale, q1, s1)
+  const bool row1 = q1 != nullptr && !gather;  // 1x128 tiles as well (x [P, cols])
   if (x_f32) {
-    if (gather) QR_LAUNCH(float, true); else QR_LAUNCH(float, false);
+    if (gather) QR_LAUNCH(float, true, false); else if (row1) QR_LAUNCH(float, false, true); else QR_LAUNCH(float, false, false);
   } else {
-    if (gather) QR_LAUNCH(uint16_t, true); else QR_LAUNCH(uint16_t, false);
+    if (gather) QR_LAUNCH(uint16_t, true, false); else if (row1) QR_LAUNCH(uint16_t, false, true); else QR_LAUNCH(uint16_t, false, false);
   }
 #undef QR_LAUNCH
 }
@@ -595,7 +622,7 @@ moe_status quantize_runs(const void* x, moe_dtype x_t, long long x_rows, int col
                   fits31((unsigned long long)quantize_runs_max(P, n_seg) * cols * 4),
               MOE_EUNSUPPORTED, "fp8_quantize_runs: operand of 2 GiB or more");
   launch_quantize_runs(x, x_t == MOE_F32, x_rows, cols, row_token, gather != 0, seg_offset, n_seg, P, run_offset,
-                       true, q, scale, as_stream(stream));
+                       true, q, scale, as_stream(stream), nullptr, nullptr);
   return launch_status("fp8_quantize_runs");
 }
 

@@ -38,7 +38,7 @@ moe_status quantize_tiles(const void* x, moe_dtype x_t, long long rows, long lon
 long long quantize_runs_max(long long P, int n_seg);
 void launch_quantize_runs(const void* x, bool x_f32, long long x_rows, int cols, const int32_t* row_token,
                           bool gather, const int32_t* seg_offset, int n_seg, long long P, int32_t* run_offset,
-                          bool offsets, uint8_t* q, float* scale, hipStream_t st);
+                          bool offsets, uint8_t* q, float* scale, hipStream_t st, uint8_t* q1, float* s1);
 
 namespace {
 
@@ -1565,23 +1565,46 @@ void launch_ffn_bwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t*
 // d <= 16384 and I <= 8192: a lane holds the block scales of two K blocks.
 bool ffn_bwd_w8_ok(int d, int I) { return ffn_bwd_ok(d, I) && d / 128 <= 128 && 2 * I / 128 <= 128; }
 
+// Token runs of the weight-gradient products, made while the input-gradient
+// products' 1x128 tiles are: run codes and scales of dy and of [da | db],
+// the run offsets and what the run quantiser reads besides.
+struct RunsOut {
+  uint8_t* dyr;
+  float* dyrs;
+  uint8_t* dabr;
+  float* dabrs;
+  const int32_t* row_token;
+  int32_t* run_offset;
+  int n_seg;
+};
+
 // The two dgrad products in E4M3: dy and then [da | db] are quantised in
 // 1x128 tiles (dyq/dys, dabq/dabs scratch), the weights come as E4M3 codes
 // with 128x128 block scales; dab gets [da | db] (bf16), dx the input
-// gradient.
+// gradient.  With `runs` (and tokens), each of dy and [da | db] is read once
+// by the run quantiser, which writes its 128-token runs and its 1x128 tiles
+// together.
 static void launch_dgrads8(const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
                            const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
                            const int32_t* tile_map, const int32_t* n_tiles, int tiles_max, int T, long long P, int d, int I, uint16_t* dab, uint8_t* dyq, float* dys,
-                           uint8_t* dabq, float* dabs, uint16_t* dx, hipStream_t st) {
+                           uint8_t* dabq, float* dabs, uint16_t* dx, hipStream_t st, const RunsOut* runs = nullptr) {
   // with no tokens every row is padding: nothing to quantise (and dy may be NULL)
-  if (T > 0) quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
+  if (T > 0 && runs)
+    launch_quantize_runs(dy, false, P, d, runs->row_token, false, seg_offset, runs->n_seg, P, runs->run_offset, true,
+                         runs->dyr, runs->dyrs, st, dyq, dys);
+  else if (T > 0)
+    quantize_tiles(dy, MOE_BF16, P, d, 1, 128, dyq, dys, st);
   {
     const long long items = (long long)tiles_max * ((I + BT - 1) / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
     hipLaunchKernelGGL((k_dgrad8<true, uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dys, w2, w2s, tile_map,
                        n_tiles, seg_offset, d, I, (uint32_t)(P * d), (uint32_t)(P * (d / 128) * 4), ab, dab);
   }
-  if (T > 0) quantize_tiles(dab, MOE_BF16, P, 2LL * I, 1, 128, dabq, dabs, st);
+  if (T > 0 && runs)
+    launch_quantize_runs(dab, false, P, 2 * I, runs->row_token, false, seg_offset, runs->n_seg, P, runs->run_offset,
+                         false, runs->dabr, runs->dabrs, st, dabq, dabs);
+  else if (T > 0)
+    quantize_tiles(dab, MOE_BF16, P, 2LL * I, 1, 128, dabq, dabs, st);
   {
     const long long items = (long long)tiles_max * (d / BT);
     const unsigned grid = (unsigned)(8 * ((items + 7) / 8));
@@ -1605,25 +1628,32 @@ void launch_ffn_bwd_w8(const uint16_t* x, const uint8_t* w13, const float* w13s,
 }
 
 // As launch_ffn_bwd_w8 with the weight gradients on E4M3 operands too
-// (reading B5): after the dgrads, dy, h, [da | db] and the gathered x are
-// quantised in runs of 128 rows per column (the codes of dy and [da | db]
-// overwrite dyq and dabq, which the dgrads no longer need; hr, xr, the four
-// run-scale arrays [runs, C] and run_offset [Nr + Ns + 1] are scratch), then
-// k_wgrad8 makes dW2 and dW13.
+// (reading B5): dy, h, [da | db] and the gathered x are quantised in runs of
+// 128 rows per column (dy and [da | db] together with their 1x128 tiles for
+// the dgrads, so each is read once; dyr, dabr, hr, xr, the four run-scale
+// arrays [runs, C] and run_offset [Nr + Ns + 1] are scratch), then k_wgrad8
+// makes dW2 and dW13.
 void launch_ffn_bwd_f8(const uint16_t* x, const uint8_t* w13, const float* w13s, const uint8_t* w2, const float* w2s,
                        const uint16_t* h, const uint16_t* ab, const uint16_t* dy, const int32_t* seg_offset,
                        const int32_t* row_token, const int32_t* tile_map, const int32_t* n_tiles, int tiles_max,
                        int T, long long P, int d, int I, int Nr, int Ns, uint16_t* dab, uint8_t* dyq, float* dys,
-                       uint8_t* dabq, float* dabs, uint8_t* hr, uint8_t* xr, float* dyrs, float* hrs, float* dabrs,
-                       float* xrs, int32_t* run_offset, int* deal, uint16_t* dx, void* dw13, void* dw2, bool dw_f32,
-                       hipStream_t st) {
-  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, seg_offset, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
-                 st);
+                       uint8_t* dabq, float* dabs, uint8_t* hr, uint8_t* xr, uint8_t* dyr, uint8_t* dabr,
+                       float* dyrs, float* hrs, float* dabrs, float* xrs, int32_t* run_offset, int* deal, uint16_t* dx,
+                       void* dw13, void* dw2, bool dw_f32, hipStream_t st) {
   const int E = Nr + Ns;
-  launch_quantize_runs(dy, false, P, d, row_token, false, seg_offset, E, P, run_offset, true, dyq, dyrs, st);
-  launch_quantize_runs(h, false, P, I, row_token, false, seg_offset, E, P, run_offset, false, hr, hrs, st);
-  launch_quantize_runs(dab, false, P, 2 * I, row_token, false, seg_offset, E, P, run_offset, false, dabq, dabrs, st);
-  launch_quantize_runs(x, false, T, d, row_token, true, seg_offset, E, P, run_offset, false, xr, xrs, st);
+  const RunsOut ro{dyr, dyrs, dabr, dabrs, row_token, run_offset, E};
+  launch_dgrads8(w13, w13s, w2, w2s, ab, dy, seg_offset, tile_map, n_tiles, tiles_max, T, P, d, I, dab, dyq, dys, dabq, dabs, dx,
+                 st, &ro);
+  if (T <= 0) {  // no 1x128 tiles were made: the runs on their own
+    launch_quantize_runs(dy, false, P, d, row_token, false, seg_offset, E, P, run_offset, true, dyr, dyrs, st, nullptr,
+                         nullptr);
+    launch_quantize_runs(dab, false, P, 2 * I, row_token, false, seg_offset, E, P, run_offset, false, dabr, dabrs, st,
+                         nullptr, nullptr);
+  }
+  launch_quantize_runs(h, false, P, I, row_token, false, seg_offset, E, P, run_offset, false, hr, hrs, st, nullptr,
+                       nullptr);
+  launch_quantize_runs(x, false, T, d, row_token, true, seg_offset, E, P, run_offset, false, xr, xrs, st, nullptr,
+                       nullptr);
   hipLaunchKernelGGL(k_wgrad_deal, dim3(1), dim3(1024), 0, st, seg_offset, Nr, deal);
   const long long runs = quantize_runs_max(P, E);
   const int nch = 4;
@@ -1633,10 +1663,10 @@ void launch_ffn_bwd_f8(const uint16_t* x, const uint8_t* w13, const float* w13s,
     const uint32_t ab_ = (uint32_t)(P * d), bb = (uint32_t)(P * I), asb = (uint32_t)(runs * d * 4),
                    bsb = (uint32_t)(runs * I * 4);
     if (dw_f32)
-      hipLaunchKernelGGL((k_wgrad8<float>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dyrs, hr, hrs, seg_offset,
+      hipLaunchKernelGGL((k_wgrad8<float>), dim3(grid), dim3(BTHREADS), 0, st, dyr, dyrs, hr, hrs, seg_offset,
                          run_offset, E, Nr, d, I, nch, ab_, bb, asb, bsb, deal, static_cast<float*>(dw2));
     else
-      hipLaunchKernelGGL((k_wgrad8<uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dyq, dyrs, hr, hrs, seg_offset,
+      hipLaunchKernelGGL((k_wgrad8<uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dyr, dyrs, hr, hrs, seg_offset,
                          run_offset, E, Nr, d, I, nch, ab_, bb, asb, bsb, deal, static_cast<uint16_t*>(dw2));
   }
   {
@@ -1645,10 +1675,10 @@ void launch_ffn_bwd_f8(const uint16_t* x, const uint8_t* w13, const float* w13s,
     const uint32_t ab_ = (uint32_t)(P * 2 * I), bb = (uint32_t)(P * d), asb = (uint32_t)(runs * 2 * I * 4),
                    bsb = (uint32_t)(runs * d * 4);
     if (dw_f32)
-      hipLaunchKernelGGL((k_wgrad8<float>), dim3(grid), dim3(BTHREADS), 0, st, dabq, dabrs, xr, xrs, seg_offset,
+      hipLaunchKernelGGL((k_wgrad8<float>), dim3(grid), dim3(BTHREADS), 0, st, dabr, dabrs, xr, xrs, seg_offset,
                          run_offset, E, Nr, 2 * I, d, nch, ab_, bb, asb, bsb, deal, static_cast<float*>(dw13));
     else
-      hipLaunchKernelGGL((k_wgrad8<uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dabq, dabrs, xr, xrs, seg_offset,
+      hipLaunchKernelGGL((k_wgrad8<uint16_t>), dim3(grid), dim3(BTHREADS), 0, st, dabr, dabrs, xr, xrs, seg_offset,
                          run_offset, E, Nr, 2 * I, d, nch, ab_, bb, asb, bsb, deal, static_cast<uint16_t*>(dw13));
   }
 }

@@ -200,8 +200,8 @@ def test_backward_entry_points_reject_bad_arguments():
     need_f8 = M.moe_gemm_backward_f8_workspace_bytes(T, K, Nr, Ns, d, I, tm)
     runs = M.fp8_quantize_runs_max(P, Nr + Ns)
     assert runs == (P + 127 * (Nr + Ns)) // 128
-    # the E4M3 dgrad workspace, the run codes of h and x, four run-scale arrays
-    assert need_f8 >= need8 + P * (I + d) + runs * (2 * d + 3 * I) * 4 + (Nr + Ns + 1) * 4
+    # the E4M3 dgrad workspace, the run codes of h, x, dy and [da|db], four run-scale arrays
+    assert need_f8 >= need8 + P * (I + d) + P * (d + 2 * I) + runs * (2 * d + 3 * I) * 4 + (Nr + Ns + 1) * 4
     assert f8(wsb=need_f8 - 1)[0] == M.MOE_EWORKSPACE
     assert M.moe_gemm_backward_f8_workspace_bytes(-1, K, Nr, Ns, d, I, tm) == 0
     qr = lambda **kw: _status(L.fp8_quantize_runs, *[kw.get(k, v) for k, v in dict(
