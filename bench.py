@@ -86,11 +86,11 @@ TRAFFIC = {
 # taken the same way from `--train` runs; keyed by workload, and for the
 # E4M3 step with bf16 weight gradients by workload + ":bf16wgrad".
 TRAIN_TRAFFIC = {
-    "v3_prefill_bf16": {"fetch_bytes": 50881294250, "write_bytes": 24487474912, "digest": "1703d8e9b52a6041",
+    "v3_prefill_bf16": {"fetch_bytes": 50803504256, "write_bytes": 24468564554, "digest": "eeb0641dc97e5494",
                         "sources": ("gemm_bwd.hip", "common.h")},
-    "v3_train_fp8": {"fetch_bytes": 27657010645, "write_bytes": 26985784117, "digest": "54571ef9a8c642ec",
+    "v3_train_fp8": {"fetch_bytes": 25938263722, "write_bytes": 27113556970, "digest": "76e3eec81c97cbbb",
                      "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
-    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 32783964672, "write_bytes": 25267414912, "digest": "54571ef9a8c642ec",
+    "v3_train_fp8:bf16wgrad": {"fetch_bytes": 32813522133, "write_bytes": 25460402218, "digest": "76e3eec81c97cbbb",
                                "sources": ("gemm_bwd.hip", "elementwise.hip", "common.h")},
 }
 
